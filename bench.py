@@ -1,0 +1,275 @@
+"""Decode-step benchmark of Windowed-MTP draft/verify attention on one MI355X.
+
+One benchmark step is one pass of the whole hot path over the 1M-context
+workload (batch 1, 32 query / 2 kv heads, head_dim 256, 64-token pages in a
+seeded permutation, draft depth 7, window 4 + 4092, verify of 8 causal queries):
+
+  windowed arm   7 x (ring append + windowed draft attention)
+  native arm     7 x (paged append + full draft attention split pass + combine)
+  verify         paged append of the 8 proposed positions + verify attention
+
+Each step appends to both arms, so the context grows by 7 draft positions (and
+the target by 8) per step, as in a decode loop that accepts every draft.  All
+inputs are generated and uploaded before the timed region.  HIP events on the
+launch stream time every phase; the per-step cost of each arm is assembled as
+in the per-step cost identity: t_step = t_verify + sum of the arm's draft steps
+(append + attention).
+
+Prints one JSON line.  ``value`` is the windowed arm's decode-step time (us).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "draft-attn µs/step + decode-step µs at 1M ctx (full vs window); HBM GB/s"
+HBM_PEAK_GBS = 8000.0
+WORKLOAD = "ctx1m_g32x2_d256"
+
+
+def log(msg: str) -> None:
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def cpu_baseline(K, V, q, L, G, g=1):
+    """The float64 oracle on a bounded sample: one kv head's G query rows of one
+    native draft step over L keys; scaled to the whole step (all kv heads)."""
+    from oracle import attention as OA
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        threads = len(os.sched_getaffinity(0))
+    qg = q[g * G:(g + 1) * G]
+    Kg = K[:, g:g + 1, :]
+    Vg = V[:, g:g + 1, :]
+    t0 = time.perf_counter()
+    OA.draft_full(qg, Kg, Vg, L, 1.0)
+    dt = time.perf_counter() - t0
+    return dt, threads
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--seed", type=int, default=2026)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--num-splits", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this path is built and measured for a single "
+              "MI355X (multi-GPU sharding is designed, not built); run with --gpus 1",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import long_context_decode_attention_amd as lib
+    import workloads as W
+    from long_context_decode_attention_amd import scenario as sc
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    lib.load()
+    dev = "cuda"
+    cfg = W.CONFIGS[WORKLOAD]
+    B, Hq, Hkv, D = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["D"]
+    S, gamma, n_q = cfg["S"], cfg["gamma"], cfg["n_q"]
+    C, n_sink, n_recent = cfg["C"], cfg["n_sink"], cfg["n_recent"]
+    G = Hq // Hkv
+    nsteps = args.warmup + args.steps
+    seed = args.seed
+
+    # ---------------------------------------------------------------- setup (untimed)
+    log("generating inputs")
+    d_extra = gamma * nsteps
+    t_extra = n_q * nsteps
+    Kd = W.kv_positions(seed, "draft_k", 0, 0, S + d_extra, Hkv, D)
+    Vd = W.kv_positions(seed, "draft_v", 0, 0, S + d_extra, Hkv, D)
+    Kt = W.kv_positions(seed, "target_k", 0, 0, S + t_extra, Hkv, D)
+    Vt = W.kv_positions(seed, "target_v", 0, 0, S + t_extra, Hkv, D)
+    log("filling caches and ring")
+    npd = (S + d_extra + 63) // 64
+    npt = (S + t_extra + 63) // 64
+    dkv = sc.alloc_paged_kv([S + d_extra], Hkv, D, W.page_permutation(seed, "draft_k", npd), dev)
+    tkv = sc.alloc_paged_kv([S + t_extra], Hkv, D, W.page_permutation(seed, "target_k", npt), dev)
+    ring = lib.new_ring(B, C, Hkv, D, n_sink, n_recent, dev)
+    sc.fill_paged(dkv, 0, 0, Kd[:S], Vd[:S])
+    sc.fill_paged(tkv, 0, 0, Kt[:S], Vt[:S])
+    sc.fill_ring(ring, 0, Kd[:S], Vd[:S])
+    # per-step inputs, resident on the device
+    kd_new = sc.to_device_bf16(Kd[S:S + d_extra]).view(nsteps, gamma, 1, 1, Hkv, D)
+    vd_new = sc.to_device_bf16(Vd[S:S + d_extra]).view(nsteps, gamma, 1, 1, Hkv, D)
+    kt_new = sc.to_device_bf16(Kt[S:S + t_extra]).view(nsteps, 1, n_q, Hkv, D)
+    vt_new = sc.to_device_bf16(Vt[S:S + t_extra]).view(nsteps, 1, n_q, Hkv, D)
+    qd_host = np.stack([W.queries(seed, "q_draft", (B, Hq), D, step=k * gamma + j)
+                        for k in range(nsteps) for j in range(gamma)])
+    qd = sc.to_device_bf16(qd_host).view(nsteps, gamma, B, Hq, D)
+    qv = sc.to_device_bf16(np.stack([W.queries(seed, "q_verify", (B, n_q, Hq), D, step=k)
+                                     for k in range(nsteps)])).view(nsteps, B, n_q, Hq, D)
+    # draft step j of bench step k appends position S + k*gamma + j - 1 and reads S + k*gamma + j keys
+    d_pos = torch.tensor([[S + k * gamma + j for j in range(gamma)] for k in range(nsteps)],
+                         dtype=torch.int32, device=dev).view(nsteps, gamma, 1)
+    d_len = d_pos + 1
+    t_pos = torch.tensor([S + k * n_q for k in range(nsteps)], dtype=torch.int32,
+                         device=dev).view(nsteps, 1)
+    t_len = t_pos + n_q
+    max_d = S + d_extra
+    max_t = S + t_extra
+    # outputs and workspaces
+    o_w = torch.empty(B, Hq, D, device=dev)
+    l_w = torch.empty(B, Hq, device=dev)
+    o_f = torch.empty(B, Hq, D, device=dev)
+    l_f = torch.empty(B, Hq, device=dev)
+    o_v = torch.empty(B, n_q, Hq, D, device=dev)
+    l_v = torch.empty(B, n_q, Hq, device=dev)
+    ws_w = lib.new_workspace(lib.workspace_bytes(B, Hq, Hkv, D, 1, C), dev)
+    ws_f = lib.new_workspace(lib.workspace_bytes(B, Hq, Hkv, D, 1, max_d, args.num_splits,
+                                                 partials_only=True), dev)
+    ws_v = lib.new_workspace(lib.workspace_bytes(B, Hq, Hkv, D, n_q, max_t), dev)
+    po, pl = lib.partials_view(ws_f, B, Hq, Hkv, D, 1, max_d, args.num_splits)
+    splits_f = lib.plan_splits(B, Hq, Hkv, D, 1, max_d, args.num_splits)
+    stream = torch.cuda.current_stream()
+
+    marks = []   # per step: dict of events
+
+    # Marshal every launch of every step before the timed region.
+    plan = []
+    for k in range(nsteps):
+        win = []
+        for j in range(gamma):
+            win.append(lib.ring_append(ring, kd_new[k, j], vd_new[k, j], prepare=True))
+            win.append(lib.draft_attn_window(qd[k, j], ring, 1.0, o_w, l_w, ws_w, prepare=True))
+        full = []
+        for j in range(gamma):
+            full.append((
+                lib.paged_append(dkv.k, dkv.v, dkv.block_table, d_pos[k, j], kd_new[k, j],
+                                 vd_new[k, j], prepare=True),
+                lib.draft_attn_full(qd[k, j], dkv.k, dkv.v, dkv.block_table, d_len[k, j], max_d,
+                                    1.0, workspace=ws_f, num_splits=args.num_splits,
+                                    partials_only=True, prepare=True),
+                lib.split_combine(po, pl, B, Hkv, G, 1, splits_per_group=splits_f,
+                                  o=o_f.view(B, 1, Hq, D), lse=l_f.view(B, 1, Hq), prepare=True)))
+        ver = (lib.paged_append(tkv.k, tkv.v, tkv.block_table, t_pos[k], kt_new[k], vt_new[k],
+                                prepare=True),
+               lib.verify_attn(qv[k], tkv.k, tkv.v, tkv.block_table, t_len[k], max_t, 1.0, o_v,
+                               l_v, ws_v, prepare=True))
+        plan.append((win, full, ver))
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5 + 2 * gamma)]
+           for _ in range(nsteps)]
+
+    def step(k):
+        win, full, ver = plan[k]
+        e = evs[k]
+        e[0].record(stream)
+        for c in win:                       # windowed arm: gamma x (ring append + attention)
+            c()
+        e[1].record(stream)
+        for j, (app, attn, comb) in enumerate(full):   # native arm
+            app()
+            e[5 + 2 * j].record(stream)
+            attn()
+            e[6 + 2 * j].record(stream)
+            comb()
+        e[2].record(stream)
+        ver[0]()                            # target append of the proposed positions
+        e[3].record(stream)
+        ver[1]()                            # verify attention
+        e[4].record(stream)
+        return {"t0": e[0], "t1": e[1], "t2": e[2], "v0": e[3], "t3": e[4],
+                "attn": [(e[5 + 2 * j], e[6 + 2 * j]) for j in range(gamma)]}
+
+    log("warmup")
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    log("timed steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.warmup, nsteps):
+        marks.append(step(k))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    def us(a, b):
+        return a.elapsed_time(b) * 1000.0
+
+    win_chain = np.median([us(m["t0"], m["t1"]) for m in marks])
+    full_chain = np.median([us(m["t1"], m["t2"]) for m in marks])
+    verify_us = np.median([us(m["t2"], m["t3"]) for m in marks])
+    verify_kernel_us = np.median([us(m["v0"], m["t3"]) for m in marks])
+    attn_us = np.array([us(a, b) for m in marks for (a, b) in m["attn"]])
+    attn_mean = float(attn_us.mean())
+    step_window = verify_us + win_chain
+    step_full = verify_us + full_chain
+    L_avg = S + gamma * (args.warmup + nsteps) / 2.0     # mean keys over the timed draft steps
+    kv_bytes = 2 * Hkv * D * 2                             # K + V bytes per position
+    attn_bytes = kv_bytes * L_avg + B * Hq * D * 2         # keys' K/V + q (algorithmic)
+    verify_bytes = kv_bytes * (S + n_q * (args.warmup + nsteps) / 2.0) + B * n_q * Hq * (D * 2 + D * 4 + 4)
+    win_bytes = kv_bytes * (n_sink + n_recent) + B * Hq * D * 2
+    achieved = attn_bytes / (attn_mean * 1e-6) / 1e9
+    verify_gbs = verify_bytes / (verify_kernel_us * 1e-6) / 1e9
+    win_step_us = win_chain / gamma
+    up, down = step_full / step_window - 1.0, 1.0 - step_window / step_full
+
+    out = {
+        "metric": METRIC,
+        "value": round(float(step_window), 2),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1000.0, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 K/V, q ~ N(0,1)/sqrt(D))",
+        "config": {"workload": WORKLOAD, "batch": B, "context": S, "q_heads": Hq, "kv_heads": Hkv,
+                   "head_dim": D, "page_tokens": 64, "pages": "seeded permutation",
+                   "draft_depth": gamma, "window": f"{n_sink}+{n_recent}", "ring_slots": C,
+                   "verify_queries": n_q},
+        "draft_attn_us_per_step": {"full": round(float(full_chain / gamma), 2),
+                                   "window": round(float(win_step_us), 2),
+                                   "full_attention_kernel": round(attn_mean, 2)},
+        "decode_step_us": {"full": round(float(step_full), 2), "window": round(float(step_window), 2),
+                           "verify": round(float(verify_us), 2)},
+        "cost_reduction": {"native_over_window_minus_1": round(float(up), 4),
+                           "one_minus_window_over_native": round(float(down), 4)},
+        "hbm_gbs": {"full_draft_attention": round(achieved, 1), "verify": round(verify_gbs, 1),
+                    "window_draft_step": round(win_bytes / (win_step_us * 1e-6) / 1e9, 1)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "attn_split_kernel<256,1,false> (native draft, split pass)",
+                     "bytes_per_launch": int(attn_bytes)},
+        "roofline_verify": {"bound": "hbm", "achieved": round(verify_gbs, 1), "peak": HBM_PEAK_GBS,
+                            "unit": "GB/s", "frac": round(verify_gbs / HBM_PEAK_GBS, 4)},
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle, one kv head of one native draft step)")
+        q0 = qd_host[0][0]
+        dt, threads = cpu_baseline(Kd, Vd, q0, S + 1, G)
+        out["cpu_baseline"] = {
+            "value": round(dt * Hkv * 1e6, 1), "unit": "us/step", "cores": threads, "kind": "oracle",
+            "sample": f"float64 oracle, native draft attention of kv head 1 ({G} query rows) over "
+                      f"{S + 1} keys, timed once and scaled x{Hkv} to one draft step",
+        }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

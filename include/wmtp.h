@@ -1,0 +1,243 @@
+/*
+ * wmtp.h - C ABI of the Windowed-MTP draft/verify attention library for
+ * MI355X (gfx950).  Library file: libwmtp.so.
+ *
+ * What the calls compute (sources are the three pages on arXiv 2607.21535,
+ * cited by title and part):
+ *   - native draft: the draft head's single query per head attends over the
+ *     whole draft KV at every draft step ("Windowed-MTP: Removing the
+ *     Full-Context Draft-KV Tax at Million-Token Context", English abstract);
+ *   - windowed draft: the same attention over the first n_sink positions plus
+ *     the most recent n_recent positions only, held in a compact per-request
+ *     ring (pith.science verdict page: key machinery; referee minor comment on
+ *     the App. A pseudocode, slot = ring_base(r) + logical_pos);
+ *   - verify: the target's full-context causal attention of the gamma+1
+ *     proposed positions, the same in both arms (English abstract; verdict
+ *     page, key machinery: the verify term is untouched);
+ *   - split combine: log-sum-exp merge of attention over disjoint key subsets
+ *     (not on the pages; how split-KV decoding is put back together).
+ *
+ * Conventions for every call
+ *   - Pointers are device pointers unless marked (host).  The caller allocates
+ *     and owns every buffer, including the workspace; the library never
+ *     allocates or frees device memory and keeps no state between calls.
+ *   - bf16 tensors are passed as uint16_t bit patterns.  Every bf16/float
+ *     pointer must be 16-byte aligned.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *     stream) and return after the launches are queued.
+ *   - Arguments are checked on the host before anything is launched; a
+ *     failed check returns an error code and launches nothing.  A fault
+ *     inside a kernel shows up at the caller's next synchronisation.  The
+ *     library never exits or aborts.
+ *   - Values the host cannot check (lengths, page ids, ring state) are
+ *     clamped on the device so that no access leaves the buffers described
+ *     by the size arguments: a length above max_seq_len or above
+ *     max_pages*64 is cut to the smaller bound; a key on a page id outside
+ *     [0, num_pages) is treated as absent.
+ *
+ * KV layout ("tiled pages").  KV is stored in pages of WMTP_PAGE_TOKENS = 64
+ * positions.  Page p, kv head g holds two tiles of 32 positions; tile
+ * t = (p * Hkv + g) * 2 + (pos % 64) / 32 occupies 32 * D bf16 elements at
+ * element offset t * 32 * D of its cache, laid out as
+ *     K tile: [D/32][32 positions][32 dims]: (pos, d) at
+ *             (d / 32) * 1024 + (pos % 32) * 32 + d % 32
+ *     V tile: [D][32 positions]:             (pos, d) at d * 32 + pos % 32
+ * so a cache of num_pages pages holds num_pages * Hkv * 64 * D elements.
+ * A draft ring of capacity C (a multiple of 64) for request r is the same
+ * layout: C / 64 pages, ring page i of request r is page r * (C / 64) + i,
+ * and ring slot s is position s of that request's pages.
+ *
+ * Query rows.  With G = Hq / Hkv, query head h reads kv head h / G.
+ */
+#ifndef WMTP_H
+#define WMTP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define WMTP_PAGE_TOKENS 64
+
+typedef enum wmtp_status {
+  WMTP_OK = 0,
+  WMTP_ERR_INVALID_ARG = 1,  /* null or misaligned pointer, bad size, inconsistent sizes */
+  WMTP_ERR_UNSUPPORTED = 2,  /* valid but not built: D not in {64,128,256}, too many query rows */
+  WMTP_ERR_WORKSPACE = 3,    /* workspace missing or smaller than wmtp_workspace_bytes() */
+  WMTP_ERR_HIP = 4           /* the HIP runtime refused a launch */
+} wmtp_status;
+
+/* flags for the attention calls */
+#define WMTP_FLAG_PARTIALS_ONLY 1u /* stop after the split pass: leave per-split (o, lse)
+                                      in the workspace (layout below) and do not write
+                                      o/lse; merge them later with wmtp_split_combine(),
+                                      e.g. after gathering partials of a sequence that is
+                                      split across devices */
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* wmtp_status_string(wmtp_status s);
+
+/*
+ * Split plan shared by the three attention calls.  n_q = 1 for the draft
+ * calls; max_keys = max_seq_len for the paged calls and C for the ring call;
+ * num_splits = 0 lets the library choose.  Returns the number of key splits
+ * per (sequence, kv head) that a call with these arguments will use, or -1
+ * if the sizes are invalid.
+ */
+int wmtp_plan_splits(int B, int Hq, int Hkv, int D, int n_q, int max_keys, int num_splits);
+
+/*
+ * Workspace bytes the same call needs (0 when one split suffices and the
+ * result is written directly, unless partials_only is non-zero).  Layout:
+ * with P = B * Hkv * splits partials of R = n_q * Hq / Hkv rows each,
+ *   part_o   fp32 [P][R][D] at byte 0 (partial p = (b * Hkv + g) * splits + s;
+ *            row r = i * G + (h - g * G) for query i, head h),
+ *   part_lse fp32 [P][R]    at byte ((P * R * D * 4 + 255) / 256) * 256;
+ * each partial is a normalised output and its natural-log log-sum-exp
+ * (-inf and zeros for a split with no key).
+ */
+size_t wmtp_workspace_bytes(int B, int Hq, int Hkv, int D, int n_q, int max_keys,
+                            int num_splits, int partials_only);
+
+/*
+ * Native (full-context) draft attention, one decode query per head.
+ * (Field-notes entry, English abstract: the native MTP draft attends over the whole KV cache at
+ * every draft step.)
+ *   q            bf16 [B][Hq][D]
+ *   k_cache      bf16 tiled pages, num_pages pages (layout above)
+ *   v_cache      bf16 tiled pages, num_pages pages
+ *   block_table  int32 [B][max_pages]: logical page i of sequence b is
+ *                physical page block_table[b * max_pages + i]
+ *   seq_lens     int32 [B]: keys of sequence b, this step's appended
+ *                position included; sequence b reads positions [0, L_b)
+ *   B, Hq, Hkv, D, num_pages, max_pages, max_seq_len   (host) sizes;
+ *                max_seq_len bounds every seq_lens entry
+ *   softmax_scale (host) logits are softmax_scale * (q . k)
+ *   o            fp32 [B][Hq][D] out
+ *   lse          fp32 [B][Hq] out, natural log; may be NULL
+ *   workspace, workspace_bytes   scratch of wmtp_workspace_bytes() bytes
+ *   num_splits   (host) 0 = automatic, else a requested split count
+ *   flags        WMTP_FLAG_PARTIALS_ONLY or 0
+ * A sequence with no key gets o = 0 and lse = -inf.
+ */
+wmtp_status wmtp_draft_attn_full(const uint16_t* q, const uint16_t* k_cache,
+                                 const uint16_t* v_cache, const int32_t* block_table,
+                                 const int32_t* seq_lens, int B, int Hq, int Hkv, int D,
+                                 int num_pages, int max_pages, int max_seq_len,
+                                 float softmax_scale, float* o, float* lse, void* workspace,
+                                 size_t workspace_bytes, int num_splits, unsigned flags,
+                                 void* stream);
+
+/*
+ * Windowed draft attention over a per-request ring of C slots.
+ * (Verdict page, key machinery: the draft reads the first n_sink positions
+ * plus the most recent ones; referee minor comment on App. A: the draft KV
+ * lives in a ring addressed as ring_base(r) + logical_pos.)
+ *   q          bf16 [B][Hq][D]
+ *   ring_k     bf16 tiled pages, B * C / 64 pages
+ *   ring_v     bf16 tiled pages, B * C / 64 pages
+ *   ring_pos   int32 [B][C]: position held by each slot, -1 if empty
+ *   ring_T     int64 [B]: positions appended so far (the context length L)
+ *   B, Hq, Hkv, D, C, n_sink, n_recent   (host); C % 64 == 0,
+ *              0 <= n_sink < C, 1 <= n_recent <= C - n_sink
+ *   softmax_scale, o, lse, workspace, workspace_bytes, num_splits, flags,
+ *   stream     as in wmtp_draft_attn_full
+ * Slot s of request b is read iff its position p = ring_pos[b][s] satisfies
+ * 0 <= p < L and (p < n_sink or p >= L - n_recent); slot order does not
+ * matter because cached keys carry their positions already.
+ */
+wmtp_status wmtp_draft_attn_window(const uint16_t* q, const uint16_t* ring_k,
+                                   const uint16_t* ring_v, const int32_t* ring_pos,
+                                   const int64_t* ring_T, int B, int Hq, int Hkv, int D, int C,
+                                   int n_sink, int n_recent, float softmax_scale, float* o,
+                                   float* lse, void* workspace, size_t workspace_bytes,
+                                   int num_splits, unsigned flags, void* stream);
+
+/*
+ * Append n_new consecutive positions to each request's draft ring.
+ * (Referee minor comment on App. A: slot = ring_base(r) + logical_pos, with
+ * slack beyond the window.)  Position p of request b goes to slot
+ *     p                                    if p < n_sink
+ *     n_sink + (p - n_sink) % (C - n_sink) otherwise
+ * of ring b; the appended positions are ring_T[b] .. ring_T[b] + n_new - 1,
+ * and ring_T[b] grows by n_new on the device.  Positions that a later
+ * position of the same call overwrites are skipped, so n_new may exceed C
+ * (bulk fill after prefill, or a rebuild on resume).  Capacity beyond
+ * n_sink + n_recent is slack: the window call reads only the last n_recent,
+ * so up to (C - n_sink - n_recent) rolled-back positions never evict a
+ * position still in the window.  Rolling back is writing a smaller ring_T.
+ *   ring_k, ring_v   bf16 tiled pages (in/out), B * C / 64 pages
+ *   ring_pos         int32 [B][C] (in/out)
+ *   ring_T           int64 [B] (in/out); negative values count as 0
+ *   k_new, v_new     bf16 [B][n_new][Hkv][D], row-major
+ *   B, n_new, Hkv, D, C, n_sink   (host)
+ */
+wmtp_status wmtp_ring_append(uint16_t* ring_k, uint16_t* ring_v, int32_t* ring_pos,
+                             int64_t* ring_T, const uint16_t* k_new, const uint16_t* v_new,
+                             int B, int n_new, int Hkv, int D, int C, int n_sink, void* stream);
+
+/*
+ * Write n_new consecutive positions into paged caches: position
+ * start_pos[b] + t of sequence b takes k_new/v_new[b][t].  Lengths are the
+ * caller's: this call does not change seq_lens.  Positions on a logical page
+ * >= max_pages or on a page id outside [0, num_pages) are skipped.
+ *   k_cache, v_cache bf16 tiled pages (in/out), num_pages pages
+ *   block_table      int32 [B][max_pages]
+ *   start_pos        int32 [B]
+ *   k_new, v_new     bf16 [B][n_new][Hkv][D], row-major
+ *   B, n_new, Hkv, D, num_pages, max_pages  (host)
+ */
+wmtp_status wmtp_paged_append(uint16_t* k_cache, uint16_t* v_cache, const int32_t* block_table,
+                              const int32_t* start_pos, const uint16_t* k_new,
+                              const uint16_t* v_new, int B, int n_new, int Hkv, int D,
+                              int num_pages, int max_pages, void* stream);
+
+/*
+ * Full-context causal verify of n_q proposed positions per sequence.
+ * (English abstract: verification keeps full attention; verdict page, key
+ * machinery: the verify term is the same in both arms.)
+ *   q          bf16 [B][n_q][Hq][D]
+ *   k_cache, v_cache, block_table, seq_lens, num_pages, max_pages,
+ *   max_seq_len  as in wmtp_draft_attn_full; seq_lens counts the n_q
+ *              appended positions, and query i sees the first
+ *              seq_lens[b] - n_q + i + 1 positions
+ *   o          fp32 [B][n_q][Hq][D] out
+ *   lse        fp32 [B][n_q][Hq] out, may be NULL
+ *   n_q * Hq / Hkv must not exceed 256.
+ */
+wmtp_status wmtp_verify_attn(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                             const int32_t* block_table, const int32_t* seq_lens, int B, int n_q,
+                             int Hq, int Hkv, int D, int num_pages, int max_pages,
+                             int max_seq_len, float softmax_scale, float* o, float* lse,
+                             void* workspace, size_t workspace_bytes, int num_splits,
+                             unsigned flags, void* stream);
+
+/*
+ * Merge per-split attention results (log-sum-exp combine):
+ *     lse = ln sum_s exp(lse_s),  o = sum_s exp(lse_s - lse) * o_s
+ * over the splits of each (sequence b, kv head g) group.
+ *   part_o        fp32 [n_parts][R][D], R = n_q * G, layout as in the workspace
+ *   part_lse      fp32 [n_parts][R]; -inf marks an empty split
+ *   n_parts       (host) partials in part_o / part_lse; split_indptr entries
+ *                 are clamped to [0, n_parts] on the device
+ *   split_indptr  int32 [B * Hkv + 1]: group (b * Hkv + g) owns partials
+ *                 split_indptr[grp] .. split_indptr[grp + 1] - 1; or NULL,
+ *                 then group grp owns grp * splits_per_group ..
+ *                 (grp + 1) * splits_per_group - 1
+ *   splits_per_group (host) used when split_indptr is NULL
+ *   B, Hkv, G, n_q, D (host)
+ *   o             fp32 [B][n_q][Hkv * G][D] out
+ *   lse           fp32 [B][n_q][Hkv * G] out, may be NULL
+ * A group with no key gets o = 0 and lse = -inf.
+ */
+wmtp_status wmtp_split_combine(const float* part_o, const float* part_lse, int n_parts,
+                               const int32_t* split_indptr, int splits_per_group, int B, int Hkv,
+                               int G, int n_q, int D, float* o, float* lse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WMTP_H */

@@ -1,0 +1,298 @@
+// C ABI of libwmtp (declared in include/wmtp.h): host-side argument checks,
+// split planning and kernel launches.  Nothing here allocates device memory.
+#include "wmtp.h"
+
+#include "internal.h"
+
+#include <climits>
+#include <cmath>
+
+using namespace wmtp;
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
+bool head_dim_ok(int D) { return D == 64 || D == 128 || D == 256; }
+
+wmtp_status from_hip(hipError_t e) { return e == hipSuccess ? WMTP_OK : WMTP_ERR_HIP; }
+
+// Common tail of the three attention calls: plan, check the workspace, launch the
+// split pass and, when there is more than one split, the combine.
+wmtp_status run_attention(AttnArgs a, bool ring, int max_keys, float* o, float* lse,
+                          void* workspace, size_t workspace_bytes, int num_splits,
+                          unsigned flags, hipStream_t stream) {
+  const int partials_only = (flags & WMTP_FLAG_PARTIALS_ONLY) ? 1 : 0;
+  AttnPlan p;
+  if (!plan_attention(a.B, a.Hq, a.Hkv, a.D, a.n_q, max_keys, num_splits, partials_only, &p))
+    return (a.n_q * (a.Hq / a.Hkv) > 256) ? WMTP_ERR_UNSUPPORTED : WMTP_ERR_INVALID_ARG;
+  if (p.ws_bytes > 0) {
+    if (!workspace || !aligned16(workspace)) return WMTP_ERR_WORKSPACE;
+    if (workspace_bytes < p.ws_bytes) return WMTP_ERR_WORKSPACE;
+  }
+  a.G = p.G;
+  a.R = p.R;
+  a.nsplit = p.nsplit;
+  a.kb_per_split = p.kb_per_split;
+  a.items = p.items;
+  a.nrg = p.nrg;
+  a.direct = p.direct;
+  a.max_keys = max_keys;
+  float* part_o = static_cast<float*>(workspace);
+  float* part_lse = p.ws_bytes ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                                          p.lse_offset)
+                               : nullptr;
+  if (p.direct) {
+    a.out_o = o;
+    a.out_lse = lse;
+  } else {
+    a.out_o = part_o;
+    a.out_lse = part_lse;
+  }
+  hipError_t e = launch_attention(a, p, ring, stream);
+  if (e != hipSuccess) return WMTP_ERR_HIP;
+  if (p.direct || partials_only) return WMTP_OK;
+  CombineArgs c;
+  c.part_o = part_o;
+  c.part_lse = part_lse;
+  c.indptr = nullptr;
+  c.n_parts = p.items;
+  c.splits_per_group = p.nsplit;
+  c.B = a.B;
+  c.Hkv = a.Hkv;
+  c.G = p.G;
+  c.n_q = a.n_q;
+  c.D = a.D;
+  c.R = p.R;
+  c.o = o;
+  c.lse = lse;
+  return from_hip(launch_combine(c, stream));
+}
+
+bool attn_dims_ok(int B, int Hq, int Hkv, int D) {
+  return B >= 1 && Hq >= 1 && Hkv >= 1 && Hq % Hkv == 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* wmtp_status_string(wmtp_status s) {
+  switch (s) {
+    case WMTP_OK: return "ok";
+    case WMTP_ERR_INVALID_ARG: return "invalid argument";
+    case WMTP_ERR_UNSUPPORTED: return "unsupported configuration";
+    case WMTP_ERR_WORKSPACE: return "workspace missing or too small";
+    case WMTP_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+int wmtp_plan_splits(int B, int Hq, int Hkv, int D, int n_q, int max_keys, int num_splits) {
+  AttnPlan p;
+  if (!plan_attention(B, Hq, Hkv, D, n_q, max_keys, num_splits, 0, &p)) return -1;
+  return p.nsplit;
+}
+
+size_t wmtp_workspace_bytes(int B, int Hq, int Hkv, int D, int n_q, int max_keys, int num_splits,
+                            int partials_only) {
+  AttnPlan p;
+  if (!plan_attention(B, Hq, Hkv, D, n_q, max_keys, num_splits, partials_only, &p)) return 0;
+  return p.ws_bytes;
+}
+
+static wmtp_status paged_attention(const uint16_t* q, const uint16_t* k_cache,
+                                   const uint16_t* v_cache, const int32_t* block_table,
+                                   const int32_t* seq_lens, int B, int n_q, int Hq, int Hkv,
+                                   int D, int num_pages, int max_pages, int max_seq_len,
+                                   float softmax_scale, float* o, float* lse, void* workspace,
+                                   size_t workspace_bytes, int num_splits, unsigned flags,
+                                   void* stream) {
+  if (!attn_dims_ok(B, Hq, Hkv, D) || n_q < 1) return WMTP_ERR_INVALID_ARG;
+  if (!head_dim_ok(D)) return WMTP_ERR_UNSUPPORTED;
+  if (n_q * (Hq / Hkv) > 256) return WMTP_ERR_UNSUPPORTED;
+  if (num_pages < 1 || max_pages < 1 || max_seq_len < 0 || num_splits < 0)
+    return WMTP_ERR_INVALID_ARG;
+  if ((flags & ~WMTP_FLAG_PARTIALS_ONLY) != 0) return WMTP_ERR_INVALID_ARG;
+  if (!std::isfinite(softmax_scale)) return WMTP_ERR_INVALID_ARG;
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens) return WMTP_ERR_INVALID_ARG;
+  if (!(flags & WMTP_FLAG_PARTIALS_ONLY) && !o) return WMTP_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || (o && !aligned16(o)) ||
+      !aligned4(block_table) || !aligned4(seq_lens) || (lse && !aligned4(lse)))
+    return WMTP_ERR_INVALID_ARG;
+  if ((long)max_pages * 64 > (long)INT_MAX) return WMTP_ERR_INVALID_ARG;
+  const int max_keys = max_seq_len < max_pages * 64 ? max_seq_len : max_pages * 64;
+  AttnArgs a = {};
+  a.q = q;
+  a.kc = k_cache;
+  a.vc = v_cache;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.n_q = n_q;
+  a.D = D;
+  a.num_pages = num_pages;
+  a.max_pages = max_pages;
+  a.scale_log2 = softmax_scale * kLog2e;
+  return run_attention(a, false, max_keys, o, lse, workspace, workspace_bytes, num_splits, flags,
+                       static_cast<hipStream_t>(stream));
+}
+
+wmtp_status wmtp_draft_attn_full(const uint16_t* q, const uint16_t* k_cache,
+                                 const uint16_t* v_cache, const int32_t* block_table,
+                                 const int32_t* seq_lens, int B, int Hq, int Hkv, int D,
+                                 int num_pages, int max_pages, int max_seq_len,
+                                 float softmax_scale, float* o, float* lse, void* workspace,
+                                 size_t workspace_bytes, int num_splits, unsigned flags,
+                                 void* stream) {
+  return paged_attention(q, k_cache, v_cache, block_table, seq_lens, B, 1, Hq, Hkv, D, num_pages,
+                         max_pages, max_seq_len, softmax_scale, o, lse, workspace,
+                         workspace_bytes, num_splits, flags, stream);
+}
+
+wmtp_status wmtp_verify_attn(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                             const int32_t* block_table, const int32_t* seq_lens, int B, int n_q,
+                             int Hq, int Hkv, int D, int num_pages, int max_pages,
+                             int max_seq_len, float softmax_scale, float* o, float* lse,
+                             void* workspace, size_t workspace_bytes, int num_splits,
+                             unsigned flags, void* stream) {
+  return paged_attention(q, k_cache, v_cache, block_table, seq_lens, B, n_q, Hq, Hkv, D,
+                         num_pages, max_pages, max_seq_len, softmax_scale, o, lse, workspace,
+                         workspace_bytes, num_splits, flags, stream);
+}
+
+wmtp_status wmtp_draft_attn_window(const uint16_t* q, const uint16_t* ring_k,
+                                   const uint16_t* ring_v, const int32_t* ring_pos,
+                                   const int64_t* ring_T, int B, int Hq, int Hkv, int D, int C,
+                                   int n_sink, int n_recent, float softmax_scale, float* o,
+                                   float* lse, void* workspace, size_t workspace_bytes,
+                                   int num_splits, unsigned flags, void* stream) {
+  if (!attn_dims_ok(B, Hq, Hkv, D)) return WMTP_ERR_INVALID_ARG;
+  if (!head_dim_ok(D)) return WMTP_ERR_UNSUPPORTED;
+  if (Hq / Hkv > 256) return WMTP_ERR_UNSUPPORTED;
+  if (C < 64 || C % 64 != 0 || n_sink < 0 || n_sink >= C || n_recent < 1 ||
+      n_recent > C - n_sink || num_splits < 0)
+    return WMTP_ERR_INVALID_ARG;
+  if ((long)B * C > (long)INT_MAX) return WMTP_ERR_INVALID_ARG;
+  if ((flags & ~WMTP_FLAG_PARTIALS_ONLY) != 0) return WMTP_ERR_INVALID_ARG;
+  if (!std::isfinite(softmax_scale)) return WMTP_ERR_INVALID_ARG;
+  if (!q || !ring_k || !ring_v || !ring_pos || !ring_T) return WMTP_ERR_INVALID_ARG;
+  if (!(flags & WMTP_FLAG_PARTIALS_ONLY) && !o) return WMTP_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(ring_k) || !aligned16(ring_v) || !aligned16(ring_pos) ||
+      !aligned8(ring_T) || (o && !aligned16(o)) || (lse && !aligned4(lse)))
+    return WMTP_ERR_INVALID_ARG;
+  AttnArgs a = {};
+  a.q = q;
+  a.kc = ring_k;
+  a.vc = ring_v;
+  a.ring_pos = ring_pos;
+  a.ring_T = ring_T;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.n_q = 1;
+  a.D = D;
+  a.num_pages = B * (C / 64);
+  a.max_pages = C / 64;
+  a.C = C;
+  a.n_sink = n_sink;
+  a.n_recent = n_recent;
+  a.scale_log2 = softmax_scale * kLog2e;
+  return run_attention(a, true, C, o, lse, workspace, workspace_bytes, num_splits, flags,
+                       static_cast<hipStream_t>(stream));
+}
+
+wmtp_status wmtp_ring_append(uint16_t* ring_k, uint16_t* ring_v, int32_t* ring_pos,
+                             int64_t* ring_T, const uint16_t* k_new, const uint16_t* v_new,
+                             int B, int n_new, int Hkv, int D, int C, int n_sink, void* stream) {
+  if (B < 1 || Hkv < 1 || n_new < 0) return WMTP_ERR_INVALID_ARG;
+  if (!head_dim_ok(D)) return WMTP_ERR_UNSUPPORTED;
+  if (C < 64 || C % 64 != 0 || n_sink < 0 || n_sink >= C) return WMTP_ERR_INVALID_ARG;
+  if ((long)B * C > (long)INT_MAX) return WMTP_ERR_INVALID_ARG;
+  if (!ring_k || !ring_v || !ring_pos || !ring_T) return WMTP_ERR_INVALID_ARG;
+  if (n_new > 0 && (!k_new || !v_new)) return WMTP_ERR_INVALID_ARG;
+  if (!aligned16(ring_k) || !aligned16(ring_v) || !aligned4(ring_pos) || !aligned8(ring_T) ||
+      (k_new && !aligned16(k_new)) || (v_new && !aligned16(v_new)))
+    return WMTP_ERR_INVALID_ARG;
+  if (n_new == 0) return WMTP_OK;
+  RingAppendArgs a;
+  a.kc = ring_k;
+  a.vc = ring_v;
+  a.ring_pos = ring_pos;
+  a.ring_T = ring_T;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.B = B;
+  a.n_new = n_new;
+  a.Hkv = Hkv;
+  a.D = D;
+  a.C = C;
+  a.n_sink = n_sink;
+  return from_hip(launch_ring_append(a, static_cast<hipStream_t>(stream)));
+}
+
+wmtp_status wmtp_paged_append(uint16_t* k_cache, uint16_t* v_cache, const int32_t* block_table,
+                              const int32_t* start_pos, const uint16_t* k_new,
+                              const uint16_t* v_new, int B, int n_new, int Hkv, int D,
+                              int num_pages, int max_pages, void* stream) {
+  if (B < 1 || B > 65535 || Hkv < 1 || n_new < 0 || num_pages < 1 || max_pages < 1)
+    return WMTP_ERR_INVALID_ARG;
+  if (!head_dim_ok(D)) return WMTP_ERR_UNSUPPORTED;
+  if (!k_cache || !v_cache || !block_table || !start_pos) return WMTP_ERR_INVALID_ARG;
+  if (n_new > 0 && (!k_new || !v_new)) return WMTP_ERR_INVALID_ARG;
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned4(block_table) ||
+      !aligned4(start_pos) || (k_new && !aligned16(k_new)) || (v_new && !aligned16(v_new)))
+    return WMTP_ERR_INVALID_ARG;
+  if ((long)n_new * Hkv * (D / 8) / 256 + 1 > (long)INT_MAX) return WMTP_ERR_INVALID_ARG;
+  if (n_new == 0) return WMTP_OK;
+  PagedAppendArgs a;
+  a.kc = k_cache;
+  a.vc = v_cache;
+  a.block_table = block_table;
+  a.start_pos = start_pos;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.B = B;
+  a.n_new = n_new;
+  a.Hkv = Hkv;
+  a.D = D;
+  a.num_pages = num_pages;
+  a.max_pages = max_pages;
+  return from_hip(launch_paged_append(a, static_cast<hipStream_t>(stream)));
+}
+
+wmtp_status wmtp_split_combine(const float* part_o, const float* part_lse, int n_parts,
+                               const int32_t* split_indptr, int splits_per_group, int B, int Hkv,
+                               int G, int n_q, int D, float* o, float* lse, void* stream) {
+  if (B < 1 || Hkv < 1 || G < 1 || n_q < 1 || D < 1 || D > 256 || n_parts < 0)
+    return WMTP_ERR_INVALID_ARG;
+  if (!split_indptr && (splits_per_group < 0 || (long)B * Hkv * splits_per_group > n_parts))
+    return WMTP_ERR_INVALID_ARG;
+  if ((long)B * Hkv * n_q * G > (long)INT_MAX) return WMTP_ERR_INVALID_ARG;
+  if (!part_o || !part_lse || !o) return WMTP_ERR_INVALID_ARG;
+  if (!aligned4(part_o) || !aligned4(part_lse) || !aligned4(o) || (lse && !aligned4(lse)) ||
+      (split_indptr && !aligned4(split_indptr)))
+    return WMTP_ERR_INVALID_ARG;
+  CombineArgs c;
+  c.part_o = part_o;
+  c.part_lse = part_lse;
+  c.indptr = split_indptr;
+  c.n_parts = n_parts;
+  c.splits_per_group = splits_per_group;
+  c.B = B;
+  c.Hkv = Hkv;
+  c.G = G;
+  c.n_q = n_q;
+  c.D = D;
+  c.R = n_q * G;
+  c.o = o;
+  c.lse = lse;
+  return from_hip(launch_combine(c, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

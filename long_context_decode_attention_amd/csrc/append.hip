@@ -1,0 +1,108 @@
+// Writers of the tiled page layout: the draft ring append and the paged append.
+//
+// Tiled pages: tile t = (page * Hkv + g) * 2 + (pos % 64) / 32 holds 32 * D
+// elements; K tile element (pos, d) at (d / 32) * 1024 + (pos % 32) * 32 + d % 32,
+// V tile element (pos, d) at d * 32 + pos % 32.
+#include "common.h"
+#include "internal.h"
+
+namespace wmtp {
+
+namespace {
+
+// Store the 8 dims d0 .. d0+7 of one position (16 bytes of K and of V from the
+// row-major source) into tile `tile`, position-in-tile `tok`.
+__device__ __forceinline__ void store_kv8(uint16_t* kc, uint16_t* vc, size_t tile, int tok, int d0,
+                                          int D, const uint16_t* ksrc, const uint16_t* vsrc) {
+  const u32x4 kv = *reinterpret_cast<const u32x4*>(ksrc);
+  const u32x4 vv = *reinterpret_cast<const u32x4*>(vsrc);
+  uint16_t* kt = kc + tile * (size_t)(32 * D);
+  uint16_t* vt = vc + tile * (size_t)(32 * D);
+  *reinterpret_cast<u32x4*>(kt + (d0 >> 5) * 1024 + tok * 32 + (d0 & 31)) = kv;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    vt[(d0 + 2 * w) * 32 + tok] = (uint16_t)(vv[w] & 0xFFFFu);
+    vt[(d0 + 2 * w + 1) * 32 + tok] = (uint16_t)(vv[w] >> 16);
+  }
+}
+
+// One workgroup per request: every thread reads the old count before thread 0
+// stores the new one, so the count update cannot race with the reads.
+__global__ __launch_bounds__(256) void ring_append_kernel(RingAppendArgs a) {
+  const int b = blockIdx.x;
+  int64_t T0 = a.ring_T[b];
+  if (T0 < 0) T0 = 0;
+  __syncthreads();
+  const int64_t T1 = T0 + a.n_new;
+  const int64_t M = a.C - a.n_sink;
+  // Of the appended positions [T0, T1), a sink position keeps its slot for good,
+  // and a later position survives iff no later appended position shares its
+  // slot, i.e. iff p >= T1 - M.  Only survivors are written.
+  const int64_t s_lo = T0;
+  const int64_t s_hi = T1 < a.n_sink ? T1 : (int64_t)a.n_sink;
+  int64_t r_lo = T0 > a.n_sink ? T0 : (int64_t)a.n_sink;
+  if (T1 - M > r_lo) r_lo = T1 - M;
+  const int64_t r_hi = T1;
+  const int n_s = s_hi > s_lo ? (int)(s_hi - s_lo) : 0;
+  const int n_r = r_hi > r_lo ? (int)(r_hi - r_lo) : 0;
+  const int chunks = a.Hkv * (a.D >> 3);      // 16-byte pieces per position
+  const int total = (n_s + n_r) * chunks;
+  for (int idx = threadIdx.x; idx < total; idx += 256) {
+    const int e = idx / chunks;
+    const int c = idx - e * chunks;
+    const int64_t p = e < n_s ? s_lo + e : r_lo + (e - n_s);
+    const int64_t t_in = p - T0;
+    const int slot = p < a.n_sink ? (int)p : a.n_sink + (int)((p - a.n_sink) % M);
+    const int g = c / (a.D >> 3);
+    const int d0 = (c - g * (a.D >> 3)) * 8;
+    const size_t src = (((size_t)b * a.n_new + t_in) * a.Hkv + g) * a.D + d0;
+    const int page = b * (a.C >> 6) + (slot >> 6);
+    const int off = slot & 63;
+    const size_t tile = ((size_t)page * a.Hkv + g) * 2 + (off >> 5);
+    store_kv8(a.kc, a.vc, tile, off & 31, d0, a.D, a.k_new + src, a.v_new + src);
+    if (c == 0) a.ring_pos[(size_t)b * a.C + slot] = (int32_t)p;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) a.ring_T[b] = T1;
+}
+
+__global__ __launch_bounds__(256) void paged_append_kernel(PagedAppendArgs a) {
+  const int b = blockIdx.y;
+  const int chunks = a.Hkv * (a.D >> 3);
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (long)a.n_new * chunks) return;
+  const int t_in = (int)(idx / chunks);
+  const int c = (int)(idx - (long)t_in * chunks);
+  const long pos = (long)a.start_pos[b] + t_in;
+  if (pos < 0) return;
+  const long lpage = pos >> 6;
+  if (lpage >= a.max_pages) return;
+  const int ppage = a.block_table[(size_t)b * a.max_pages + lpage];
+  if ((unsigned)ppage >= (unsigned)a.num_pages) return;
+  const int g = c / (a.D >> 3);
+  const int d0 = (c - g * (a.D >> 3)) * 8;
+  const size_t src = (((size_t)b * a.n_new + t_in) * a.Hkv + g) * a.D + d0;
+  const int off = (int)(pos & 63);
+  const size_t tile = ((size_t)ppage * a.Hkv + g) * 2 + (off >> 5);
+  store_kv8(a.kc, a.vc, tile, off & 31, d0, a.D, a.k_new + src, a.v_new + src);
+}
+
+}  // namespace
+
+hipError_t launch_ring_append(const RingAppendArgs& a, hipStream_t stream) {
+  RingAppendArgs arg = a;
+  void* args[] = {&arg};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&ring_append_kernel), dim3(a.B), dim3(256),
+                         args, 0, stream);
+}
+
+hipError_t launch_paged_append(const PagedAppendArgs& a, hipStream_t stream) {
+  PagedAppendArgs arg = a;
+  void* args[] = {&arg};
+  const long work = (long)a.n_new * a.Hkv * (a.D >> 3);
+  const unsigned gx = (unsigned)((work + 255) / 256);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&paged_append_kernel), dim3(gx, a.B),
+                         dim3(256), args, 0, stream);
+}
+
+}  // namespace wmtp

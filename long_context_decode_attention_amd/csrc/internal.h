@@ -1,0 +1,82 @@
+// Host-side launch interface between the C ABI (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace wmtp {
+
+// Arguments of the split-KV attention kernel (draft full, draft window, verify).
+struct AttnArgs {
+  const uint16_t* q;            // bf16 [B][n_q][Hq][D]
+  const uint16_t* kc;           // K tiled pages
+  const uint16_t* vc;           // V tiled pages
+  const int32_t* block_table;   // paged mode: [B][max_pages]
+  const int32_t* seq_lens;      // paged mode: [B]
+  const int32_t* ring_pos;      // ring mode: [B][C]
+  const int64_t* ring_T;        // ring mode: [B]
+  float* out_o;                 // partials (split mode) or final o (direct mode)
+  float* out_lse;               // partials or final lse (may be null in direct mode)
+  int B, Hq, Hkv, G, n_q, R, D;
+  int num_pages;                // pages addressable through kc/vc
+  int max_pages;                // block-table row stride (paged mode)
+  int max_keys;                 // keys considered per sequence: min(max_seq_len, max_pages*64) or C
+  int nsplit;                   // key splits per (b, g)
+  int kb_per_split;             // 32-key tiles per split
+  int items;                    // B * Hkv * nsplit
+  int nrg;                      // row groups (16 * NRB rows each)
+  int direct;                   // 1: write final o/lse, 0: write partials
+  int C, n_sink, n_recent;      // ring mode
+  float scale_log2;             // softmax_scale * log2(e)
+};
+
+struct AttnPlan {
+  int G, R, nrb, nrg, nkb, kb_per_split, nsplit, items, grid;
+  int direct;
+  size_t part_o_bytes, lse_offset, ws_bytes;
+};
+
+bool plan_attention(int B, int Hq, int Hkv, int D, int n_q, int max_keys, int num_splits,
+                    int partials_only, AttnPlan* p);
+
+hipError_t launch_attention(const AttnArgs& a, const AttnPlan& p, bool ring, hipStream_t stream);
+
+struct CombineArgs {
+  const float* part_o;
+  const float* part_lse;
+  const int32_t* indptr;   // may be null
+  int n_parts;             // partials addressable; indptr entries are clamped to it
+  int splits_per_group;
+  int B, Hkv, G, n_q, D, R;
+  float* o;
+  float* lse;              // may be null
+};
+
+hipError_t launch_combine(const CombineArgs& c, hipStream_t stream);
+
+struct RingAppendArgs {
+  uint16_t* kc;
+  uint16_t* vc;
+  int32_t* ring_pos;
+  int64_t* ring_T;
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  int B, n_new, Hkv, D, C, n_sink;
+};
+
+hipError_t launch_ring_append(const RingAppendArgs& a, hipStream_t stream);
+
+struct PagedAppendArgs {
+  uint16_t* kc;
+  uint16_t* vc;
+  const int32_t* block_table;
+  const int32_t* start_pos;
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  int B, n_new, Hkv, D, num_pages, max_pages;
+};
+
+hipError_t launch_paged_append(const PagedAppendArgs& a, hipStream_t stream);
+
+}  // namespace wmtp

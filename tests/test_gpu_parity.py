@@ -1,0 +1,425 @@
+"""GPU parity: every C-ABI call against the float64 oracle on the same seeded inputs.
+
+Sizes are chosen so that the oracle finishes in seconds while the kernels still
+run many tiles, several splits and a ragged tail; the full 1M-context sizes are
+covered by sampled outputs in ``test_gpu_fullsize.py``.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import attention as OA
+from oracle import ring as OR
+from tests.gpu_common import DraftScenario, VerifyScenario, compare, dev_bf16, dev_i32, torch
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    t = torch()
+    assert t.cuda.is_available(), "GPU tests need a GPU"
+    import long_context_decode_attention_amd as lib
+    lib.load()
+    yield
+
+
+CFG = W.CONFIGS
+
+
+def _lib():
+    import long_context_decode_attention_amd as lib
+    return lib
+
+
+def _draft_chain(sc: DraftScenario, num_splits=0, check_window=True):
+    lib = _lib()
+    cfg = sc.cfg
+    res = []
+    for j in range(1, sc.gamma + 1):
+        sc.append(j)
+        q = sc.q(j)
+        qt = dev_bf16(q)
+        lens = sc.lens(j)
+        o_f, l_f = lib.draft_attn_full(qt, sc.kv.k, sc.kv.v, sc.kv.block_table, dev_i32(lens),
+                                       max(lens), 1.0, num_splits=num_splits)
+        o_w, l_w = lib.draft_attn_window(qt, sc.ring, 1.0, num_splits=num_splits)
+        torch().cuda.synchronize()
+        for b in range(sc.B):
+            of, lf = OA.draft_full(q[b], sc.K[b], sc.V[b], lens[b], 1.0)
+            compare(o_f[b], l_f[b], of, lf, f"full b={b} step={j} L={lens[b]}")
+            if check_window:
+                ow, lw = OA.draft_window(q[b], sc.K[b], sc.V[b], lens[b], cfg["n_sink"],
+                                         cfg["n_recent"], 1.0)
+                compare(o_w[b], l_w[b], ow, lw, f"window b={b} step={j} L={lens[b]}")
+        res.append((o_f, l_f, o_w, l_w))
+    return res
+
+
+# ------------------------------------------------------------------ draft: full and windowed
+
+def test_draft_ctx8k_full_size():
+    """Single decode query, 16/2 heads, D 128, context 8192, window 4 + 1020, one step."""
+    cfg = CFG["ctx8k_g16x2_d128"]
+    _draft_chain(DraftScenario(cfg, 1, [cfg["S"]], cfg["gamma"]))
+
+
+def test_draft_ctx128k_shape_three_steps():
+    """32/4 heads, D 128, window 4 + 4092, 3 chained steps; context cut to a ragged 20011."""
+    cfg = CFG["ctx128k_g32x4_d128"]
+    _draft_chain(DraftScenario(cfg, 2, [20011], 3))
+
+
+def test_draft_ctx1m_shape_permuted_pages():
+    """32/2 heads, D 256, permuted 64-token pages, 2 steps; context cut to 40000."""
+    cfg = CFG["ctx1m_g32x2_d256"]
+    _draft_chain(DraftScenario(cfg, 3, [40000], 2))
+
+
+def test_draft_ragged_batch():
+    """Batch 8 with ragged contexts in a shared permuted pool, 32/4 heads, D 128."""
+    cfg = CFG["ragged8_256k_1m_g32x4_d128"]
+    S = [int(x) for x in W.ragged_lengths(4, 8, 3000, 9000)]
+    _draft_chain(DraftScenario(cfg, 4, S, 2))
+
+
+def test_draft_g64x2_wrapped_ring():
+    """64/2 heads (G = 32, two row blocks), D 128; ring of 4096 wrapped (T > C)."""
+    cfg = CFG["nope8l_1m_g64x2_d128"]
+    _draft_chain(DraftScenario(cfg, 5, [11000], 2))
+
+
+@pytest.mark.parametrize("S", [0, 1, 3, 63, 64, 65, 1023, 1024, 1025])
+def test_draft_short_contexts(S):
+    """Contexts shorter than, equal to and just past the window and the tile sizes."""
+    cfg = dict(CFG["ctx8k_g16x2_d128"])
+    _draft_chain(DraftScenario(cfg, 10 + S, [S], 2))
+
+
+def test_draft_peaked_and_scaled():
+    """Sharper attention (q x 8) and an explicit 1/sqrt(D) softmax scale."""
+    cfg = CFG["ctx1m_g32x2_d256"]
+    sc = DraftScenario(cfg, 6, [9000], 1, peak=8.0)
+    lib = _lib()
+    sc.append(1)
+    q = sc.q(1)
+    lens = sc.lens(1)
+    s = 1.0 / math.sqrt(cfg["D"]) * 4.0
+    o, l = lib.draft_attn_full(dev_bf16(q), sc.kv.k, sc.kv.v, sc.kv.block_table, dev_i32(lens),
+                               lens[0], s)
+    ow, lw = lib.draft_attn_window(dev_bf16(q), sc.ring, s)
+    torch().cuda.synchronize()
+    of, lf = OA.draft_full(q[0], sc.K[0], sc.V[0], lens[0], s)
+    compare(o[0], l[0], of, lf, "peaked full")
+    ow_ref, lw_ref = OA.draft_window(q[0], sc.K[0], sc.V[0], lens[0], 4, 4092, s)
+    compare(ow[0], lw[0], ow_ref, lw_ref, "peaked window")
+
+
+def test_window_equals_full_when_window_covers_context():
+    cfg = CFG["ctx128k_g32x4_d128"]
+    sc = DraftScenario(cfg, 7, [3000], 1)
+    lib = _lib()
+    sc.append(1)
+    q = dev_bf16(sc.q(1))
+    lens = sc.lens(1)
+    o_f, l_f = lib.draft_attn_full(q, sc.kv.k, sc.kv.v, sc.kv.block_table, dev_i32(lens), lens[0])
+    o_w, l_w = lib.draft_attn_window(q, sc.ring)
+    torch().cuda.synchronize()
+    assert float((o_f - o_w).abs().max()) <= 1e-5
+    assert float((l_f - l_w).abs().max()) <= 1e-5
+
+
+def test_needle_outside_window_moves_full_only():
+    """A planted high-logit key just outside the recent window changes the native
+    draft's output but not the windowed one."""
+    lib = _lib()
+    cfg = dict(CFG["ctx8k_g16x2_d128"])
+    S = 5000
+    sc = DraftScenario(cfg, 8, [S], 1)
+    q = sc.q(1)
+    L = S + 1
+    needle = L - cfg["n_recent"] - 1
+    qf = W.bf16_to_f32(q[0])
+    K2 = sc.K[0].copy()
+    for g in range(cfg["Hkv"]):
+        K2[needle, g] = W.bf16_round(4.0 * np.sign(qf[g * 8]) * np.ones(cfg["D"], np.float32))
+    sc2 = DraftScenario(cfg, 8, [S], 1)
+    sc2.K[0] = K2
+    from long_context_decode_attention_amd import scenario as scn
+    scn.fill_paged(sc2.kv, 0, needle, K2[needle:needle + 1], sc2.V[0][needle:needle + 1])
+    sc.append(1)
+    sc2.append(1)
+    qt = dev_bf16(q)
+    a = lib.draft_attn_full(qt, sc.kv.k, sc.kv.v, sc.kv.block_table, dev_i32([L]), L)
+    b = lib.draft_attn_full(qt, sc2.kv.k, sc2.kv.v, sc2.kv.block_table, dev_i32([L]), L)
+    wa = lib.draft_attn_window(qt, sc.ring)
+    wb = lib.draft_attn_window(qt, sc2.ring)
+    torch().cuda.synchronize()
+    of, lf = OA.draft_full(q[0], K2, sc2.V[0], L, 1.0)
+    compare(b[0][0], b[1][0], of, lf, "needle full")
+    assert float((a[0] - b[0]).abs().max()) > 0.05
+    assert torch().equal(wa[0], wb[0])
+
+
+# ------------------------------------------------------------------ split structure
+
+@pytest.mark.parametrize("num_splits", [1, 2, 7, 64])
+def test_split_count_invariance(num_splits):
+    lib = _lib()
+    cfg = CFG["ctx1m_g32x2_d256"]
+    sc = DraftScenario(cfg, 9, [30000], 1)
+    sc.append(1)
+    q = sc.q(1)
+    lens = sc.lens(1)
+    o, l = lib.draft_attn_full(dev_bf16(q), sc.kv.k, sc.kv.v, sc.kv.block_table, dev_i32(lens),
+                               lens[0], num_splits=num_splits)
+    torch().cuda.synchronize()
+    of, lf = OA.draft_full(q[0], sc.K[0], sc.V[0], lens[0], 1.0)
+    compare(o[0], l[0], of, lf, f"num_splits={num_splits}")
+
+
+def test_deterministic_bitwise():
+    lib = _lib()
+    cfg = CFG["ctx1m_g32x2_d256"]
+    sc = DraftScenario(cfg, 11, [25000], 1)
+    sc.append(1)
+    q = dev_bf16(sc.q(1))
+    lens = dev_i32(sc.lens(1))
+    r1 = lib.draft_attn_full(q, sc.kv.k, sc.kv.v, sc.kv.block_table, lens, 25001)
+    r2 = lib.draft_attn_full(q, sc.kv.k, sc.kv.v, sc.kv.block_table, lens, 25001)
+    w1 = lib.draft_attn_window(q, sc.ring)
+    w2 = lib.draft_attn_window(q, sc.ring)
+    torch().cuda.synchronize()
+    assert torch().equal(r1[0], r2[0]) and torch().equal(r1[1], r2[1])
+    assert torch().equal(w1[0], w2[0]) and torch().equal(w1[1], w2[1])
+
+
+def test_partials_only_then_combine_equals_direct():
+    lib = _lib()
+    cfg = CFG["ctx128k_g32x4_d128"]
+    sc = DraftScenario(cfg, 12, [20000], 1)
+    sc.append(1)
+    q = dev_bf16(sc.q(1))
+    lens = dev_i32(sc.lens(1))
+    B, Hq, Hkv, D = 1, cfg["Hq"], cfg["Hkv"], cfg["D"]
+    o, l = lib.draft_attn_full(q, sc.kv.k, sc.kv.v, sc.kv.block_table, lens, 20001)
+    ws = lib.draft_attn_full(q, sc.kv.k, sc.kv.v, sc.kv.block_table, lens, 20001,
+                             partials_only=True)
+    po, pl = lib.partials_view(ws, B, Hq, Hkv, D, 1, 20001)
+    splits = lib.plan_splits(B, Hq, Hkv, D, 1, 20001)
+    assert splits > 1
+    o2, l2 = lib.split_combine(po, pl, B, Hkv, Hq // Hkv, 1, splits_per_group=splits)
+    torch().cuda.synchronize()
+    assert torch().equal(o.view(-1), o2.view(-1)) and torch().equal(l.view(-1), l2.view(-1))
+
+
+def test_split_combine_against_oracle_csr():
+    """Direct test of the combine with a CSR split list, empty splits and an empty group."""
+    lib = _lib()
+    rng = np.random.default_rng(13)
+    B, Hkv, G, n_q, D = 2, 3, 4, 2, 128
+    R = G * n_q
+    counts = [3, 0, 5, 1, 7, 2]                      # group 1 has no split
+    indptr = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    P = int(indptr[-1])
+    po = rng.standard_normal((P, R, D)).astype(np.float32)
+    pl = (rng.standard_normal((P, R)) * 3).astype(np.float32)
+    pl[1, :] = -np.inf                               # an empty split
+    o, l = lib.split_combine(torch().tensor(po, device="cuda"), torch().tensor(pl, device="cuda"),
+                             B, Hkv, G, n_q, split_indptr=dev_i32(indptr))
+    torch().cuda.synchronize()
+    o = o.cpu().numpy()
+    l = l.cpu().numpy()
+    for grp in range(B * Hkv):
+        b, g = divmod(grp, Hkv)
+        a, e = indptr[grp], indptr[grp + 1]
+        if a == e:
+            ro, rl = np.zeros((R, D)), np.full(R, -np.inf)
+        else:
+            ro, rl = OA.combine(po[a:e], pl[a:e])
+        for r in range(R):
+            i, hl = divmod(r, G)
+            h = g * G + hl
+            got_o, got_l = o[b, i, h], l[b, i, h]
+            if np.isneginf(rl[r]):
+                assert np.isneginf(got_l) and np.all(got_o == 0)
+            else:
+                assert np.max(np.abs(got_o - ro[r])) <= 1e-5 * (1 + np.max(np.abs(ro[r])))
+                assert abs(got_l - rl[r]) <= 1e-5
+
+
+# ------------------------------------------------------------------ verify
+
+def _verify_case(cfg, seed, S, n_q, num_splits=0):
+    lib = _lib()
+    vs = VerifyScenario(cfg, seed, S, n_q)
+    vs.append_proposed()
+    lens = vs.lens()
+    o, l = lib.verify_attn(dev_bf16(vs.q), vs.kv.k, vs.kv.v, vs.kv.block_table, dev_i32(lens),
+                           max(lens), 1.0, num_splits=num_splits)
+    torch().cuda.synchronize()
+    for b in range(vs.B):
+        ro, rl = OA.verify(vs.q[b], vs.K[b], vs.V[b], lens[b], 1.0)
+        compare(o[b], l[b], ro, rl, f"verify b={b} L={lens[b]}")
+    return vs, o, l
+
+
+def test_verify_ctx1m_shape():
+    """8 causal queries, 32/2 heads, D 256 (128 query rows per kv head); context 20000."""
+    _verify_case(CFG["ctx1m_g32x2_d256"], 21, [20000], 8)
+
+
+def test_verify_ragged_batch():
+    cfg = CFG["ragged8_256k_1m_g32x4_d128"]
+    S = [int(x) for x in W.ragged_lengths(22, 8, 2000, 7000)]
+    _verify_case(cfg, 22, S, 4)
+
+
+def test_verify_g64x2_256_rows():
+    """G = 32 and 8 queries: 256 query rows per kv head."""
+    _verify_case(CFG["nope8l_1m_g64x2_d128"], 23, [6000], 8)
+
+
+@pytest.mark.parametrize("S", [0, 1, 60, 64, 100])
+def test_verify_short(S):
+    _verify_case(CFG["ctx1m_g32x2_d256"], 30 + S, [S], 8)
+
+
+def test_verify_same_in_both_arms():
+    """The verify call reads only the target KV: repeated calls (one per arm) agree bitwise."""
+    lib = _lib()
+    vs, o1, l1 = _verify_case(CFG["ctx128k_g32x4_d128"], 24, [9000], 4)
+    lens = vs.lens()
+    o2, l2 = lib.verify_attn(dev_bf16(vs.q), vs.kv.k, vs.kv.v, vs.kv.block_table, dev_i32(lens),
+                             max(lens))
+    torch().cuda.synchronize()
+    assert torch().equal(o1, o2) and torch().equal(l1, l2)
+
+
+def test_verify_single_query_equals_draft_full():
+    lib = _lib()
+    cfg = CFG["ctx1m_g32x2_d256"]
+    vs = VerifyScenario(cfg, 25, [7000], 1)
+    vs.append_proposed()
+    lens = vs.lens()
+    o, l = lib.verify_attn(dev_bf16(vs.q), vs.kv.k, vs.kv.v, vs.kv.block_table, dev_i32(lens),
+                           lens[0])
+    od, ld = lib.draft_attn_full(dev_bf16(vs.q[:, 0]), vs.kv.k, vs.kv.v, vs.kv.block_table,
+                                 dev_i32(lens), lens[0])
+    torch().cuda.synchronize()
+    assert torch().equal(o[:, 0], od) and torch().equal(l[:, 0], ld)
+
+
+# ------------------------------------------------------------------ appends (bit-exact)
+
+def _unpack_k(kc, D):
+    """Tiled K cache -> [page, Hkv, 64, D] bit patterns (layout of include/wmtp.h)."""
+    a = kc.view(torch().int16).cpu().numpy().view(np.uint16)     # [P, Hkv, 2, D/32, 32, 32]
+    P, Hkv = a.shape[:2]
+    a = a.transpose(0, 1, 2, 4, 3, 5)                              # [P, Hkv, half, pos, dtile, 32]
+    return a.reshape(P, Hkv, 64, D)
+
+
+def _unpack_v(vc, D):
+    a = vc.view(torch().int16).cpu().numpy().view(np.uint16)     # [P, Hkv, 2, D, 32]
+    P, Hkv = a.shape[:2]
+    a = a.transpose(0, 1, 2, 4, 3)                                 # [P, Hkv, half, pos, D]
+    return a.reshape(P, Hkv, 64, D)
+
+
+def test_paged_append_layout_bitexact():
+    cfg = CFG["ctx1m_g32x2_d256"]
+    sc = DraftScenario(cfg, 40, [1000, 77], 3, perm=True, poison=False)
+    for j in range(1, 4):
+        sc.append(j)
+    torch().cuda.synchronize()
+    Kp = _unpack_k(sc.kv.k, cfg["D"])
+    Vp = _unpack_v(sc.kv.v, cfg["D"])
+    bt = sc.kv.block_table.cpu().numpy()
+    for b in range(sc.B):
+        L = sc.S[b] + 3
+        for p in range(L):
+            page = bt[b, p // 64]
+            assert np.array_equal(Kp[page, :, p % 64], sc.K[b][p]), (b, p)
+            assert np.array_equal(Vp[page, :, p % 64], sc.V[b][p]), (b, p)
+
+
+@pytest.mark.parametrize("n_sink,C,T0,n_new", [(4, 1024, 0, 5000), (4, 1024, 3000, 1),
+                                               (4, 4096, 0, 10000), (0, 64, 10, 200),
+                                               (63, 128, 50, 3), (4, 1024, 2, 1)])
+def test_ring_append_bitexact(n_sink, C, T0, n_new):
+    """ring_pos against the oracle ring model, and every filled slot's K/V against
+    the logical K/V of the position it holds; bulk and single appends."""
+    lib = _lib()
+    from long_context_decode_attention_amd import scenario as scn
+    B, Hkv, D = 2, 2, 128
+    K = [W.kv_positions(50 + b, "draft_k", b, 0, T0 + n_new, Hkv, D) for b in range(B)]
+    V = [W.kv_positions(50 + b, "draft_v", b, 0, T0 + n_new, Hkv, D) for b in range(B)]
+    ring = lib.new_ring(B, C, Hkv, D, n_sink, C - n_sink)
+    model = OR.RingModel(B, C, n_sink)
+    for b in range(B):
+        scn.fill_ring(ring, b, K[b][:T0], V[b][:T0])
+        model.append(b, T0)
+    # then the rest: one bulk call for the batch
+    kn = np.stack([K[b][T0:] for b in range(B)])
+    vn = np.stack([V[b][T0:] for b in range(B)])
+    if n_new:
+        lib.ring_append(ring, dev_bf16(kn), dev_bf16(vn))
+    for b in range(B):
+        model.append(b, n_new)
+    torch().cuda.synchronize()
+    pos = ring.pos.cpu().numpy()
+    T = ring.T.cpu().numpy()
+    # ring page i of request b is pool page b * C/64 + i: [B, C/64, Hkv, 64, D] -> [B, C, Hkv, D]
+    Kp = _unpack_k(ring.k, D).reshape(B, C // 64, Hkv, 64, D).transpose(0, 1, 3, 2, 4)
+    Kp = Kp.reshape(B, C, Hkv, D)
+    Vp = _unpack_v(ring.v, D).reshape(B, C // 64, Hkv, 64, D).transpose(0, 1, 3, 2, 4)
+    Vp = Vp.reshape(B, C, Hkv, D)
+    for b in range(B):
+        assert T[b] == T0 + n_new
+        assert pos[b].tolist() == model.pos[b]
+        assert pos[b].tolist() == OR.expected_pos_after(T0 + n_new, n_sink, C)
+        for s in range(C):
+            p = pos[b, s]
+            if p >= 0:
+                assert np.array_equal(Kp[b, s], K[b][p]) and np.array_equal(Vp[b, s], V[b][p])
+
+
+def test_ring_rollback_with_slack():
+    """Slack slots absorb a rollback: after appending 3 speculative positions and
+    rolling T back by 3, the window read equals the oracle window."""
+    lib = _lib()
+    from long_context_decode_attention_amd import scenario as scn
+    Hq, Hkv, D, n_sink, n_recent, C = 16, 2, 128, 4, 1020 - 60, 1024
+    T = 5000
+    K = W.kv_positions(60, "draft_k", 0, 0, T + 3, Hkv, D)
+    V = W.kv_positions(60, "draft_v", 0, 0, T + 3, Hkv, D)
+    ring = lib.new_ring(1, C, Hkv, D, n_sink, n_recent)
+    scn.fill_ring(ring, 0, K[:T + 3], V[:T + 3])
+    ring.T.fill_(T)
+    q = W.queries(61, "q_draft", (1, Hq), D)
+    o, l = lib.draft_attn_window(dev_bf16(q), ring)
+    torch().cuda.synchronize()
+    ro, rl = OA.draft_window(q[0], K, V, T, n_sink, n_recent, 1.0)
+    compare(o[0], l[0], ro, rl, "window after rollback")
+
+
+# ------------------------------------------------------------------ argument checks
+
+def test_error_codes():
+    lib = _lib()
+    cfg = CFG["ctx8k_g16x2_d128"]
+    sc = DraftScenario(cfg, 70, [100], 1, poison=False)
+    q = dev_bf16(sc.q(1))
+    lens = dev_i32([100])
+    with pytest.raises(lib.WmtpError) as e:
+        lib.draft_attn_full(q, sc.kv.k, sc.kv.v, sc.kv.block_table, lens, 100, float("nan"))
+    assert e.value.status == 1
+    small = torch().empty(16, dtype=torch().uint8, device="cuda")
+    with pytest.raises(lib.WmtpError) as e:
+        lib.draft_attn_full(q, sc.kv.k, sc.kv.v, sc.kv.block_table, lens, 1 << 20, workspace=small,
+                            num_splits=4)
+    assert e.value.status == 3
