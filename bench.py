@@ -136,7 +136,7 @@ def main() -> int:
     l_f = torch.empty(B, Hq, device=dev)
     o_v = torch.empty(B, n_q, Hq, D, device=dev)
     l_v = torch.empty(B, n_q, Hq, device=dev)
-    ws_w = lib.new_workspace(lib.workspace_bytes(B, Hq, Hkv, D, 1, C), dev)
+    ws_w = lib.new_workspace(lib.workspace_bytes(B, Hq, Hkv, D, 1, C, ring=True), dev)
     ws_f = lib.new_workspace(lib.workspace_bytes(B, Hq, Hkv, D, 1, max_d, args.num_splits,
                                                  partials_only=True), dev)
     ws_v = lib.new_workspace(lib.workspace_bytes(B, Hq, Hkv, D, n_q, max_t), dev)

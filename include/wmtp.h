@@ -79,14 +79,19 @@ typedef enum wmtp_status {
 /* Human-readable name of a status code (static string, never NULL). */
 const char* wmtp_status_string(wmtp_status s);
 
+/* `call` argument of the two planning queries below */
+#define WMTP_CALL_PAGED 0 /* wmtp_draft_attn_full, wmtp_verify_attn */
+#define WMTP_CALL_RING 1  /* wmtp_draft_attn_window */
+
 /*
- * Split plan shared by the three attention calls.  n_q = 1 for the draft
- * calls; max_keys = max_seq_len for the paged calls and C for the ring call;
- * num_splits = 0 lets the library choose.  Returns the number of key splits
- * per (sequence, kv head) that a call with these arguments will use, or -1
- * if the sizes are invalid.
+ * Split plan of the attention calls.  n_q = 1 for the draft calls;
+ * max_keys = min(max_seq_len, max_pages * 64) for the paged calls and C for
+ * the ring call; num_splits = 0 lets the library choose.  Returns the number
+ * of key splits per (sequence, kv head) that a call with these arguments
+ * will use, or -1 if the sizes are invalid.
  */
-int wmtp_plan_splits(int B, int Hq, int Hkv, int D, int n_q, int max_keys, int num_splits);
+int wmtp_plan_splits(int call, int B, int Hq, int Hkv, int D, int n_q, int max_keys,
+                     int num_splits);
 
 /*
  * Workspace bytes the same call needs (0 when one split suffices and the
@@ -98,7 +103,7 @@ int wmtp_plan_splits(int B, int Hq, int Hkv, int D, int n_q, int max_keys, int n
  * each partial is a normalised output and its natural-log log-sum-exp
  * (-inf and zeros for a split with no key).
  */
-size_t wmtp_workspace_bytes(int B, int Hq, int Hkv, int D, int n_q, int max_keys,
+size_t wmtp_workspace_bytes(int call, int B, int Hq, int Hkv, int D, int n_q, int max_keys,
                             int num_splits, int partials_only);
 
 /*
@@ -227,7 +232,7 @@ wmtp_status wmtp_verify_attn(const uint16_t* q, const uint16_t* k_cache, const u
  *                 then group grp owns grp * splits_per_group ..
  *                 (grp + 1) * splits_per_group - 1
  *   splits_per_group (host) used when split_indptr is NULL
- *   B, Hkv, G, n_q, D (host)
+ *   B, Hkv, G, n_q, D (host); D a multiple of 16, at most 256
  *   o             fp32 [B][n_q][Hkv * G][D] out
  *   lse           fp32 [B][n_q][Hkv * G] out, may be NULL
  * A group with no key gets o = 0 and lse = -inf.

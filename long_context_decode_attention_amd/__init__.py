@@ -51,8 +51,8 @@ _U = ctypes.c_uint
 
 _SIGS = {
     "wmtp_status_string": ([_I], ctypes.c_char_p),
-    "wmtp_plan_splits": ([_I] * 7, _I),
-    "wmtp_workspace_bytes": ([_I] * 8, _SZ),
+    "wmtp_plan_splits": ([_I] * 8, _I),
+    "wmtp_workspace_bytes": ([_I] * 9, _SZ),
     "wmtp_draft_attn_full": ([_P] * 5 + [_I] * 7 + [_F, _P, _P, _P, _SZ, _I, _U, _P], _I),
     "wmtp_draft_attn_window": ([_P] * 5 + [_I] * 7 + [_F, _P, _P, _P, _SZ, _I, _U, _P], _I),
     "wmtp_ring_append": ([_P] * 6 + [_I] * 6 + [_P], _I),
@@ -198,16 +198,22 @@ def new_ring(B: int, C: int, Hkv: int, D: int, n_sink: int, n_recent: int, devic
 
 # ----------------------------------------------------------------------------- planning
 
-def plan_splits(B, Hq, Hkv, D, n_q, max_keys, num_splits=0) -> int:
-    n = load().wmtp_plan_splits(B, Hq, Hkv, D, n_q, max_keys, num_splits)
+CALL_PAGED = 0
+CALL_RING = 1
+
+
+def plan_splits(B, Hq, Hkv, D, n_q, max_keys, num_splits=0, ring=False) -> int:
+    n = load().wmtp_plan_splits(CALL_RING if ring else CALL_PAGED, B, Hq, Hkv, D, n_q, max_keys,
+                                num_splits)
     if n < 0:
         raise WmtpError("wmtp_plan_splits", 1)
     return n
 
 
-def workspace_bytes(B, Hq, Hkv, D, n_q, max_keys, num_splits=0, partials_only=False) -> int:
-    return int(load().wmtp_workspace_bytes(B, Hq, Hkv, D, n_q, max_keys, num_splits,
-                                           1 if partials_only else 0))
+def workspace_bytes(B, Hq, Hkv, D, n_q, max_keys, num_splits=0, partials_only=False,
+                    ring=False) -> int:
+    return int(load().wmtp_workspace_bytes(CALL_RING if ring else CALL_PAGED, B, Hq, Hkv, D, n_q,
+                                           max_keys, num_splits, 1 if partials_only else 0))
 
 
 def new_workspace(nbytes: int, device="cuda"):
@@ -215,11 +221,11 @@ def new_workspace(nbytes: int, device="cuda"):
     return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
 
 
-def partials_view(workspace, B, Hq, Hkv, D, n_q, max_keys, num_splits=0):
+def partials_view(workspace, B, Hq, Hkv, D, n_q, max_keys, num_splits=0, ring=False):
     """(part_o [P, R, D], part_lse [P, R]) views of a workspace left by a
     partials-only call with the same arguments."""
     torch = _torch()
-    splits = plan_splits(B, Hq, Hkv, D, n_q, max_keys, num_splits)
+    splits = plan_splits(B, Hq, Hkv, D, n_q, max_keys, num_splits, ring)
     P = B * Hkv * splits
     R = n_q * (Hq // Hkv)
     ob = P * R * D * 4
@@ -315,7 +321,7 @@ def draft_attn_window(q, ring: Ring, softmax_scale=1.0, o=None, lse=None, worksp
     _need(ring.v, torch.bfloat16, v_cache_shape(B * C // PAGE, Hkv, D), "ring.v")
     _need(ring.pos, torch.int32, (B, C), "ring.pos")
     _need(ring.T, torch.int64, (B,), "ring.T")
-    need = workspace_bytes(B, Hq, Hkv, D, 1, C, num_splits, partials_only)
+    need = workspace_bytes(B, Hq, Hkv, D, 1, C, num_splits, partials_only, ring=True)
     if workspace is None:
         workspace = new_workspace(need, q.device)
     _need(workspace, torch.uint8, None, "workspace")

@@ -27,7 +27,8 @@ wmtp_status run_attention(AttnArgs a, bool ring, int max_keys, float* o, float* 
                           unsigned flags, hipStream_t stream) {
   const int partials_only = (flags & WMTP_FLAG_PARTIALS_ONLY) ? 1 : 0;
   AttnPlan p;
-  if (!plan_attention(a.B, a.Hq, a.Hkv, a.D, a.n_q, max_keys, num_splits, partials_only, &p))
+  if (!plan_attention(a.B, a.Hq, a.Hkv, a.D, a.n_q, max_keys, num_splits, partials_only, ring,
+                      &p))
     return (a.n_q * (a.Hq / a.Hkv) > 256) ? WMTP_ERR_UNSUPPORTED : WMTP_ERR_INVALID_ARG;
   if (p.ws_bytes > 0) {
     if (!workspace || !aligned16(workspace)) return WMTP_ERR_WORKSPACE;
@@ -91,16 +92,22 @@ const char* wmtp_status_string(wmtp_status s) {
   return "unknown status";
 }
 
-int wmtp_plan_splits(int B, int Hq, int Hkv, int D, int n_q, int max_keys, int num_splits) {
+int wmtp_plan_splits(int call, int B, int Hq, int Hkv, int D, int n_q, int max_keys,
+                     int num_splits) {
   AttnPlan p;
-  if (!plan_attention(B, Hq, Hkv, D, n_q, max_keys, num_splits, 0, &p)) return -1;
+  if (call != WMTP_CALL_PAGED && call != WMTP_CALL_RING) return -1;
+  if (!plan_attention(B, Hq, Hkv, D, n_q, max_keys, num_splits, 0, call == WMTP_CALL_RING, &p))
+    return -1;
   return p.nsplit;
 }
 
-size_t wmtp_workspace_bytes(int B, int Hq, int Hkv, int D, int n_q, int max_keys, int num_splits,
-                            int partials_only) {
+size_t wmtp_workspace_bytes(int call, int B, int Hq, int Hkv, int D, int n_q, int max_keys,
+                            int num_splits, int partials_only) {
   AttnPlan p;
-  if (!plan_attention(B, Hq, Hkv, D, n_q, max_keys, num_splits, partials_only, &p)) return 0;
+  if (call != WMTP_CALL_PAGED && call != WMTP_CALL_RING) return 0;
+  if (!plan_attention(B, Hq, Hkv, D, n_q, max_keys, num_splits, partials_only,
+                      call == WMTP_CALL_RING, &p))
+    return 0;
   return p.ws_bytes;
 }
 
@@ -269,13 +276,13 @@ wmtp_status wmtp_paged_append(uint16_t* k_cache, uint16_t* v_cache, const int32_
 wmtp_status wmtp_split_combine(const float* part_o, const float* part_lse, int n_parts,
                                const int32_t* split_indptr, int splits_per_group, int B, int Hkv,
                                int G, int n_q, int D, float* o, float* lse, void* stream) {
-  if (B < 1 || Hkv < 1 || G < 1 || n_q < 1 || D < 1 || D > 256 || n_parts < 0)
+  if (B < 1 || Hkv < 1 || G < 1 || n_q < 1 || D < 16 || D > 256 || D % 16 != 0 || n_parts < 0)
     return WMTP_ERR_INVALID_ARG;
   if (!split_indptr && (splits_per_group < 0 || (long)B * Hkv * splits_per_group > n_parts))
     return WMTP_ERR_INVALID_ARG;
-  if ((long)B * Hkv * n_q * G > (long)INT_MAX) return WMTP_ERR_INVALID_ARG;
+  if ((long)B * Hkv * n_q * G * (D / 16) > (long)INT_MAX) return WMTP_ERR_INVALID_ARG;
   if (!part_o || !part_lse || !o) return WMTP_ERR_INVALID_ARG;
-  if (!aligned4(part_o) || !aligned4(part_lse) || !aligned4(o) || (lse && !aligned4(lse)) ||
+  if (!aligned16(part_o) || !aligned4(part_lse) || !aligned16(o) || (lse && !aligned4(lse)) ||
       (split_indptr && !aligned4(split_indptr)))
     return WMTP_ERR_INVALID_ARG;
   CombineArgs c;

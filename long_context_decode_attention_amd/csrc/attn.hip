@@ -26,149 +26,20 @@
 // a K operand fetches 16 rows of 64 contiguous bytes (a 2 KB dim-tile per key
 // block pair), a V operand 1 KB contiguous.  Each wave double-buffers its tiles
 // in registers: the loads of tile t+4 are in flight while tile t is computed.
-#include "common.h"
-#include "internal.h"
+#include "attn_device.h"
 
-#include <climits>
-#include <cmath>
+// Workgroups the split planner aims at: two per CU for the split-keys kernel
+// (one resident at a time), one per CU for the shared kernel.
+#ifndef WMTP_TARGET_WG_SPLIT
+#define WMTP_TARGET_WG_SPLIT 512
+#endif
+#ifndef WMTP_TARGET_WG_SHARED
+#define WMTP_TARGET_WG_SHARED 256
+#endif
 
 namespace wmtp {
 
 namespace {
-
-constexpr float kLn2 = 0.693147180559945309f;
-
-template <int D, bool RING>
-struct KTile {
-  bf16x8 k[2][D / 32];   // K operands: key block bb, head-dim step ks
-  int32_t pos[RING ? 8 : 1];   // ring mode: positions held by this lane's 8 slots
-};
-
-template <int D>
-struct VTile {
-  bf16x8 v[D / 16];      // V^T operands: head-dim block db
-};
-
-// Physical 32-key tile index of tile kb of (b, g), or ok = false when the
-// page id is outside the cache (its keys then count as absent).
-template <bool RING>
-__device__ __forceinline__ size_t tile_index(const AttnArgs& a, int b, int g, int kb, bool& ok) {
-  const int lpage = kb >> 1;
-  int ppage;
-  if constexpr (RING) {
-    ppage = b * (a.C >> 6) + lpage;
-  } else {
-    ppage = a.block_table[(size_t)b * a.max_pages + lpage];
-  }
-  ok = (unsigned)ppage < (unsigned)a.num_pages;
-  return ((size_t)ppage * a.Hkv + g) * 2 + (kb & 1);
-}
-
-template <int D, bool RING>
-__device__ __forceinline__ void load_k(KTile<D, RING>& t, const AttnArgs& a, size_t tile, int b,
-                                       int kb, int n, int j) {
-  constexpr int KS = D / 32;
-  const uint16_t* kt = a.kc + tile * (size_t)(32 * D);
-#pragma unroll
-  for (int bb = 0; bb < 2; ++bb) {
-    // A row n of key block bb is key 8*(n/4) + 4*bb + n%4 of the tile.
-    const int tok = 8 * (n >> 2) + 4 * bb + (n & 3);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) t.k[bb][ks] = ld_bf16x8(kt + ks * 1024 + tok * 32 + j * 8);
-  }
-  if constexpr (RING) {
-    const int32_t* rp = a.ring_pos + (size_t)b * a.C + kb * 32 + j * 8;
-    const int4 p0 = *reinterpret_cast<const int4*>(rp);
-    const int4 p1 = *reinterpret_cast<const int4*>(rp + 4);
-    t.pos[0] = p0.x; t.pos[1] = p0.y; t.pos[2] = p0.z; t.pos[3] = p0.w;
-    t.pos[4] = p1.x; t.pos[5] = p1.y; t.pos[6] = p1.z; t.pos[7] = p1.w;
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void load_v(VTile<D>& t, const AttnArgs& a, size_t tile, int n, int j) {
-  constexpr int DB = D / 16;
-  const uint16_t* vt = a.vc + tile * (size_t)(32 * D);
-#pragma unroll
-  for (int db = 0; db < DB; ++db) t.v[db] = ld_bf16x8(vt + (db * 16 + n) * 32 + j * 8);
-}
-
-template <int D, int NRB>
-struct SoftmaxState {
-  f32x4 acc[NRB][D / 16];   // O^T accumulators: lane (n, j) holds d = 16*db + 4*j + i, row n
-  float m[NRB];             // running row max of the scaled logits (log2 units)
-  float l[NRB];             // this lane's share of the running sum of weights
-};
-
-// Keys of this lane's 8 (kbase .. kbase+7) that exist for every row: inside the
-// sequence length, or (ring) holding a position of the current window.
-template <int D, bool RING>
-__device__ __forceinline__ uint32_t present_keys(const KTile<D, RING>& t, const AttnArgs& a,
-                                                 int kbase, int L, int T) {
-  uint32_t keep;
-  if constexpr (RING) {
-    keep = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int p = t.pos[i];
-      const bool ok = p >= 0 && p < T && (p < a.n_sink || p >= T - a.n_recent);
-      keep |= (ok ? 1u : 0u) << i;
-    }
-  } else {
-    const int rem = L - kbase;
-    keep = rem >= 8 ? 0xFFu : (rem <= 0 ? 0u : ((1u << rem) - 1u));
-  }
-  return keep;
-}
-
-// Online-softmax update of one row block from its S^T accumulators.  The weights
-// this lane feeds to the PV product are returned as two bf16 parts, p = hi + lo
-// (hi = bf16(p), lo = bf16(p - hi)), so that PV sees p to about 2^-16 relative
-// instead of bf16's 2^-9; the running sum adds the fp32 weights.
-template <int D, int NRB>
-__device__ __forceinline__ void softmax_update(SoftmaxState<D, NRB>& st, int rb, f32x4 s0,
-                                               f32x4 s1, uint32_t keep, int lr, float scale_log2,
-                                               bf16x8& p_hi, bf16x8& p_lo) {
-  constexpr int DB = D / 16;
-  // s0[i] is key kbase + i, s1[i] is key kbase + 4 + i, for this lane's row.
-  float x[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float v = (i < 4 ? s0[i] : s1[i - 4]) * scale_log2;
-    const bool ok = ((keep >> i) & 1u) && (i < lr);
-    x[i] = ok ? v : -INFINITY;
-  }
-  float mx = x[0];
-#pragma unroll
-  for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
-  mx = max_over_lane_groups(mx);
-  const float m_new = fmaxf(st.m[rb], mx);
-  const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-  const float alpha = fast_exp2(st.m[rb] - m_use);
-  st.m[rb] = m_new;
-
-  u32x4 hw, lw;
-  float psum = 0.f;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const float p0 = fast_exp2(x[2 * w] - m_use);
-    const float p1 = fast_exp2(x[2 * w + 1] - m_use);
-    psum += p0 + p1;
-    const uint32_t h0 = f32_to_bf16_bits(p0);
-    const uint32_t h1 = f32_to_bf16_bits(p1);
-    const uint32_t l0 = f32_to_bf16_bits(p0 - bf16_bits_to_f32(h0));
-    const uint32_t l1 = f32_to_bf16_bits(p1 - bf16_bits_to_f32(h1));
-    hw[w] = h0 | (h1 << 16);
-    lw[w] = l0 | (l1 << 16);
-  }
-  st.l[rb] = st.l[rb] * alpha + psum;
-  if (!__all(alpha == 1.0f)) {
-#pragma unroll
-    for (int db = 0; db < DB; ++db) st.acc[rb][db] *= alpha;
-  }
-  p_hi = __builtin_bit_cast(bf16x8, hw);
-  p_lo = __builtin_bit_cast(bf16x8, lw);
-}
 
 template <int D, int NRB, bool RING>
 __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
@@ -389,35 +260,56 @@ hipError_t launch_d(const AttnArgs& a, const AttnPlan& p, bool ring, hipStream_t
 }  // namespace
 
 bool plan_attention(int B, int Hq, int Hkv, int D, int n_q, int max_keys, int num_splits,
-                    int partials_only, AttnPlan* p) {
+                    int partials_only, bool ring, AttnPlan* p) {
   if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || n_q < 1 || max_keys < 0 || num_splits < 0)
     return false;
   if (D != 64 && D != 128 && D != 256) return false;
   p->G = Hq / Hkv;
   p->R = n_q * p->G;
   if (p->R > 256) return false;
-  // Two row blocks per wave need too many registers at D = 256 (they spill).
-  p->nrb = (p->R <= 16 || D == 256) ? 1 : 2;
-  p->nrg = (p->R + 16 * p->nrb - 1) / (16 * p->nrb);
   p->nkb = (max_keys + 31) / 32;
   const long groups = (long)B * Hkv;
+  long target;    // workgroups to aim at
+  int cap;        // most 32-key tiles per split
+  // Few rows: each wave holds every row and the four waves split the keys.
+  // Two row blocks per wave need too many registers at D = 256 (they spill).
+  if (ring || p->R <= 16 || (p->R <= 32 && D != 256)) {
+    p->shared = 0;
+    p->nrb = (p->R <= 16 || D == 256) ? 1 : 2;
+    p->nrg = (p->R + 16 * p->nrb - 1) / (16 * p->nrb);
+    target = WMTP_TARGET_WG_SPLIT;
+    cap = INT_MAX;
+  } else {
+    // Many rows: the waves split the rows and share each K/V tile through LDS.
+    // A workgroup holds 16 * rbw rows per wave; two row blocks per wave are too
+    // many registers at D = 256 for two waves per SIMD.
+    p->shared = 1;
+    const int nw = shared_kernel_waves();
+    const int rbw = (p->R > 16 * nw && D != 256) ? 2 : 1;
+    p->nrb = rbw;
+    p->nrg = (p->R + 16 * nw * rbw - 1) / (16 * nw * rbw);
+    target = WMTP_TARGET_WG_SHARED;
+    cap = shared_kernel_max_tiles();
+  }
   int kbps;
   if (num_splits > 0) {
     kbps = (p->nkb + num_splits - 1) / num_splits;
   } else {
-    // Aim at about 1024 workgroups (four per CU) with at least one tile per wave.
-    const long target = 1024;
+    // Rounded down (to a multiple of 4: one share per wave) so that a length just
+    // past a round number adds a small last split instead of stretching all.
     const long tiles = (long)p->nkb * groups * p->nrg;
-    long per = (tiles + target - 1) / target;
-    per = ((per + 3) / 4) * 4;
-    kbps = (int)(per < 4 ? 4 : per);
+    long per = tiles / target;
+    per = (per / 4) * 4;
+    kbps = (int)(per < 4 ? 4 : (per > INT_MAX ? INT_MAX : per));
   }
+  if (p->shared) kbps = (kbps + 1) & ~1;   // even: a split then spans at most cap/2 whole pages
+  if (kbps > cap) kbps = cap;
   if (kbps < 1) kbps = 1;
   p->kb_per_split = kbps;
   p->nsplit = p->nkb == 0 ? 1 : (p->nkb + kbps - 1) / kbps;
   p->direct = (p->nsplit == 1 && !partials_only) ? 1 : 0;
   const long items = groups * p->nsplit;
-  if (items > INT_MAX / 16) return false;
+  if (items * p->nrg > INT_MAX / 16) return false;
   p->items = (int)items;
   p->grid = p->nrg == 1 ? p->items : ((p->items + 7) / 8) * 8 * p->nrg;
   if (p->direct) {
@@ -433,6 +325,7 @@ bool plan_attention(int B, int Hq, int Hkv, int D, int n_q, int max_keys, int nu
 }
 
 hipError_t launch_attention(const AttnArgs& a, const AttnPlan& p, bool ring, hipStream_t stream) {
+  if (p.shared) return ring ? hipErrorInvalidValue : launch_attention_shared(a, p, stream);
   switch (a.D) {
     case 64: return launch_d<64>(a, p, ring, stream);
     case 128: return launch_d<128>(a, p, ring, stream);

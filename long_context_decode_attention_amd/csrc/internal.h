@@ -32,15 +32,20 @@ struct AttnArgs {
 };
 
 struct AttnPlan {
+  int shared;   // 0: attn_split_kernel (one wave holds all rows, waves split keys)
+                // 1: attn_shared_kernel (waves split rows, K/V tiles shared in LDS)
   int G, R, nrb, nrg, nkb, kb_per_split, nsplit, items, grid;
   int direct;
   size_t part_o_bytes, lse_offset, ws_bytes;
 };
 
 bool plan_attention(int B, int Hq, int Hkv, int D, int n_q, int max_keys, int num_splits,
-                    int partials_only, AttnPlan* p);
+                    int partials_only, bool ring, AttnPlan* p);
 
 hipError_t launch_attention(const AttnArgs& a, const AttnPlan& p, bool ring, hipStream_t stream);
+hipError_t launch_attention_shared(const AttnArgs& a, const AttnPlan& p, hipStream_t stream);
+int shared_kernel_waves();
+int shared_kernel_max_tiles();   // most 32-key tiles one split of the shared kernel covers
 
 struct CombineArgs {
   const float* part_o;

@@ -1,0 +1,195 @@
+"""CPU tests of the C ABI boundary (no GPU needed: nothing here launches a kernel).
+
+* libwmtp.so loads and exports every function include/wmtp.h declares;
+* argument checks return the documented status codes before any launch
+  (fake but aligned pointers are used only where a check fails first);
+* the split planner's answers are consistent;
+* the oracle and the HIP path do not import each other, and the product path
+  has no fallback when the library is missing.
+"""
+
+import ast
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wmtp.h")
+
+lib_mod = pytest.importorskip("long_context_decode_attention_amd")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR = 0, 1, 2, 3, 4
+FAKE = 0x10000          # 16-byte aligned, never dereferenced: every call below fails a check first
+
+
+def _lib():
+    if not os.path.exists(lib_mod.LIB_PATH):
+        pytest.skip("libwmtp.so not built")
+    return lib_mod.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:wmtp_status|int|size_t|const char\*)\s+(wmtp_\w+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_header_declares_the_five_calls():
+    names = declared_functions()
+    for n in ("wmtp_draft_attn_full", "wmtp_draft_attn_window", "wmtp_ring_append",
+              "wmtp_verify_attn", "wmtp_split_combine"):
+        assert n in names
+    assert set(names) == set(lib_mod.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib()
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    # and with C linkage (unmangled) in the dynamic symbol table
+    data = open(lib_mod.LIB_PATH, "rb").read()
+    for n in declared_functions():
+        assert n.encode() + b"\x00" in data, n
+
+
+def test_status_strings():
+    _lib()
+    assert lib_mod.status_string(OK) == "ok"
+    assert lib_mod.status_string(WORKSPACE) == "workspace missing or too small"
+    assert lib_mod.status_string(99) == "unknown status"
+
+
+def _full(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, sl=FAKE, B=1, Hq=32, Hkv=2, D=256, num_pages=16,
+             max_pages=16, max_seq_len=1024, scale=1.0, o=FAKE, lse=None, ws=None, ws_bytes=0,
+             num_splits=0, flags=0)
+    a.update(kw)
+    P = ctypes.c_void_p
+    return lib.wmtp_draft_attn_full(P(a["q"]), P(a["k"]), P(a["v"]), P(a["bt"]), P(a["sl"]), a["B"],
+                                    a["Hq"], a["Hkv"], a["D"], a["num_pages"], a["max_pages"],
+                                    a["max_seq_len"], a["scale"], P(a["o"]), P(a["lse"]),
+                                    P(a["ws"]), a["ws_bytes"], a["num_splits"], a["flags"], None)
+
+
+def test_draft_full_argument_checks():
+    lib = _lib()
+    assert _full(lib, q=None) == INVALID
+    assert _full(lib, o=None) == INVALID
+    assert _full(lib, D=100) == UNSUPPORTED
+    assert _full(lib, D=512) == UNSUPPORTED
+    assert _full(lib, Hq=33) == INVALID                  # not a multiple of Hkv
+    assert _full(lib, B=0) == INVALID
+    assert _full(lib, num_pages=0) == INVALID
+    assert _full(lib, scale=float("inf")) == INVALID
+    assert _full(lib, flags=8) == INVALID
+    assert _full(lib, q=FAKE + 2) == INVALID              # misaligned
+    # 1024 keys in 16 splits need a workspace: none given
+    assert _full(lib, num_splits=16) == WORKSPACE
+    assert _full(lib, num_splits=16, ws=FAKE, ws_bytes=64) == WORKSPACE
+
+
+def test_verify_and_window_argument_checks():
+    lib = _lib()
+    P = ctypes.c_void_p
+    # 8 queries x G = 64 is 512 rows: more than a kv head's 256-row limit
+    st = lib.wmtp_verify_attn(P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), 1, 8, 128, 2, 128, 16, 16,
+                              1024, 1.0, P(FAKE), None, None, 0, 0, 0, None)
+    assert st == UNSUPPORTED
+    st = lib.wmtp_verify_attn(P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), 1, 0, 32, 2, 128, 16, 16,
+                              1024, 1.0, P(FAKE), None, None, 0, 0, 0, None)
+    assert st == INVALID
+
+    def win(**kw):
+        a = dict(B=1, Hq=32, Hkv=2, D=256, C=4096, ns=4, nr=4092, pos=FAKE)
+        a.update(kw)
+        return lib.wmtp_draft_attn_window(P(FAKE), P(FAKE), P(FAKE), P(a["pos"]), P(FAKE), a["B"],
+                                          a["Hq"], a["Hkv"], a["D"], a["C"], a["ns"], a["nr"], 1.0,
+                                          P(FAKE), None, None, 0, 0, 0, None)
+    assert win(C=4100) == INVALID                      # not a multiple of 64
+    assert win(ns=4096) == INVALID                     # sink fills the ring
+    assert win(nr=4093) == INVALID                     # window larger than the ring
+    assert win(nr=0) == INVALID
+    assert win(pos=None) == INVALID
+    assert win(D=96) == UNSUPPORTED
+
+
+def test_append_and_combine_argument_checks():
+    lib = _lib()
+    P = ctypes.c_void_p
+    ra = lambda **kw: lib.wmtp_ring_append(  # noqa: E731
+        P(kw.get("k", FAKE)), P(FAKE), P(FAKE), P(FAKE), P(kw.get("kn", FAKE)), P(FAKE),
+        kw.get("B", 1), kw.get("n", 1), 2, kw.get("D", 128), kw.get("C", 1024), kw.get("ns", 4), None)
+    assert ra(C=1000) == INVALID
+    assert ra(ns=1024) == INVALID
+    assert ra(n=-1) == INVALID
+    assert ra(k=None) == INVALID
+    assert ra(kn=None) == INVALID
+    assert ra(D=100) == UNSUPPORTED
+    assert ra(n=0) == OK                               # nothing to append: no launch
+    pa = lambda **kw: lib.wmtp_paged_append(  # noqa: E731
+        P(FAKE), P(FAKE), P(kw.get("bt", FAKE)), P(FAKE), P(FAKE), P(FAKE), 1, kw.get("n", 1), 2, 128,
+        kw.get("np", 4), 4, None)
+    assert pa(bt=None) == INVALID
+    assert pa(np=0) == INVALID
+    assert pa(n=0) == OK
+    sc = lambda **kw: lib.wmtp_split_combine(  # noqa: E731
+        P(FAKE), P(FAKE), kw.get("n_parts", 8), P(kw.get("indptr")), kw.get("spg", 4), 1, 2, 4, 1,
+        kw.get("D", 128), P(kw.get("o", FAKE)), None, None)
+    assert sc(spg=5) == INVALID                        # 2 groups x 5 splits > 8 partials
+    assert sc(D=100) == INVALID
+    assert sc(o=None) == INVALID
+
+
+def test_plan_and_workspace_consistency():
+    _lib()
+    L = 1 << 20
+    # native draft at 1M: several splits, each partial R x D floats plus its lse
+    n = lib_mod.plan_splits(1, 32, 2, 256, 1, L)
+    assert n > 1
+    ws = lib_mod.workspace_bytes(1, 32, 2, 256, 1, L)
+    po = 2 * n * 16 * 256 * 4
+    assert ws == (po + 255) // 256 * 256 + 2 * n * 16 * 4
+    # a requested split count is an upper bound; one split writes directly
+    assert lib_mod.plan_splits(1, 32, 2, 256, 1, L, 7) <= 7
+    assert lib_mod.workspace_bytes(1, 32, 2, 256, 1, 100, 1) == 0
+    assert lib_mod.workspace_bytes(1, 32, 2, 256, 1, 100, 1, partials_only=True) > 0
+    # the ring call plans with the ring's capacity
+    assert lib_mod.plan_splits(1, 32, 2, 256, 1, 4096, ring=True) >= 1
+    with pytest.raises(lib_mod.WmtpError):
+        lib_mod.plan_splits(1, 32, 3, 256, 1, L)
+
+
+def _imports(path):
+    names = set()
+    for dirpath, _, files in os.walk(path):
+        for f in files:
+            if f.endswith(".py"):
+                tree = ast.parse(open(os.path.join(dirpath, f)).read())
+                for node in ast.walk(tree):
+                    if isinstance(node, ast.Import):
+                        names.update(a.name.split(".")[0] for a in node.names)
+                    elif isinstance(node, ast.ImportFrom) and node.module and node.level == 0:
+                        names.add(node.module.split(".")[0])
+    return names
+
+
+def test_oracle_and_hip_path_are_independent():
+    assert "long_context_decode_attention_amd" not in _imports(os.path.join(ROOT, "oracle"))
+    assert "workloads" not in _imports(os.path.join(ROOT, "oracle"))
+    product = _imports(os.path.join(ROOT, "long_context_decode_attention_amd"))
+    assert "oracle" not in product and "workloads" not in product
+    assert "long_context_decode_attention_amd" not in _imports(os.path.join(ROOT, "workloads"))
+    assert "oracle" not in _imports(os.path.join(ROOT, "workloads"))
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    saved = lib_mod._lib
+    lib_mod._lib = None
+    try:
+        with pytest.raises(RuntimeError, match="not built"):
+            lib_mod.load(str(tmp_path / "libwmtp.so"))
+    finally:
+        lib_mod._lib = saved
