@@ -39,9 +39,10 @@
  * positions.  Page p, kv head g holds two tiles of 32 positions; tile
  * t = (p * Hkv + g) * 2 + (pos % 64) / 32 occupies 32 * D bf16 elements at
  * element offset t * 32 * D of its cache, laid out as
- *     K tile: [D/32][32 positions][32 dims]: (pos, d) at
- *             (d / 32) * 1024 + (pos % 32) * 32 + d % 32
- *     V tile: [D][32 positions]:             (pos, d) at d * 32 + pos % 32
+ *     K tile: [D/16][32 positions][16 dims]: (pos, d) at
+ *             (d / 16) * 512 + (pos % 32) * 16 + d % 16
+ *     V tile: [2][D][16 positions]:          (pos, d) at
+ *             ((pos % 32) / 16) * 16 * D + d * 16 + pos % 16
  * so a cache of num_pages pages holds num_pages * Hkv * 64 * D elements.
  * A draft ring of capacity C (a multiple of 64) for request r is the same
  * layout: C / 64 pages, ring page i of request r is page r * (C / 64) + i,
@@ -119,7 +120,8 @@ size_t wmtp_workspace_bytes(int call, int B, int Hq, int Hkv, int D, int n_q, in
  *                position included; sequence b reads positions [0, L_b)
  *   B, Hq, Hkv, D, num_pages, max_pages, max_seq_len   (host) sizes;
  *                max_seq_len bounds every seq_lens entry
- *   softmax_scale (host) logits are softmax_scale * (q . k)
+ *   softmax_scale (host) logits are softmax_scale * (q . k); finite and
+ *                > 0 (1/sqrt(D) in the usual case), else WMTP_ERR_INVALID_ARG
  *   o            fp32 [B][Hq][D] out
  *   lse          fp32 [B][Hq] out, natural log; may be NULL
  *   workspace, workspace_bytes   scratch of wmtp_workspace_bytes() bytes

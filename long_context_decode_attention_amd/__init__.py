@@ -6,8 +6,8 @@ used for device memory and streams.  If the library is not built this module
 still imports, but every call raises: there is no fallback path.
 
 KV caches use the tiled page layout of the C ABI: a page of 64 positions and one
-kv head is two tiles of 32 positions; K tiles are ``[D/32][32 pos][32 dims]``,
-V tiles ``[D][32 pos]``.  :func:`new_paged_cache` and :func:`new_ring` allocate
+kv head is two tiles of 32 positions; K tiles are ``[D/16][32 pos][16 dims]``,
+V tiles ``[2][D][16 pos]``.  :func:`new_paged_cache` and :func:`new_ring` allocate
 tensors with those shapes; the append calls write them.
 """
 
@@ -144,11 +144,11 @@ def _need(t, dtype, shape, name):
 
 
 def k_cache_shape(num_pages: int, Hkv: int, D: int) -> tuple:
-    return (num_pages, Hkv, 2, D // 32, 32, 32)
+    return (num_pages, Hkv, 2, D // 16, 32, 16)
 
 
 def v_cache_shape(num_pages: int, Hkv: int, D: int) -> tuple:
-    return (num_pages, Hkv, 2, D, 32)
+    return (num_pages, Hkv, 2, 2, D, 16)
 
 
 def new_paged_cache(num_pages: int, Hkv: int, D: int, device="cuda"):
@@ -182,7 +182,7 @@ class Ring:
 
     @property
     def D(self) -> int:
-        return self.v.shape[3]
+        return self.v.shape[4]
 
 
 def new_ring(B: int, C: int, Hkv: int, D: int, n_sink: int, n_recent: int, device="cuda") -> Ring:

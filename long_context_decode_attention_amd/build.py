@@ -4,7 +4,11 @@
 
 Every HIP source under csrc/ is compiled for gfx950 only.  Packed fp32 VALU
 instructions are switched off for the device code (`-packed-fp32-ops`); the
-host pass warns that it does not know that feature, which is harmless.
+host pass warns that it does not know that feature, which is harmless.  Device
+code is built with `-fno-honor-nans`: the kernels never rely on NaN semantics
+(absent keys are masked with selects and integer masks, not NaN tests), and it
+spares the max reductions of the softmax a canonicalising instruction per input.
+Host code keeps full IEEE semantics, so argument checks still see NaN.
 """
 
 from __future__ import annotations
@@ -36,6 +40,7 @@ def command(out: str = LIB, extra: list | None = None) -> list:
     return [
         hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-shared", "-fPIC",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-Xarch_device", "-fno-honor-nans",
         "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
         *(extra or []), *sources(), "-o", out,
     ]

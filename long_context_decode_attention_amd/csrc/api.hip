@@ -124,7 +124,8 @@ static wmtp_status paged_attention(const uint16_t* q, const uint16_t* k_cache,
   if (num_pages < 1 || max_pages < 1 || max_seq_len < 0 || num_splits < 0)
     return WMTP_ERR_INVALID_ARG;
   if ((flags & ~WMTP_FLAG_PARTIALS_ONLY) != 0) return WMTP_ERR_INVALID_ARG;
-  if (!std::isfinite(softmax_scale)) return WMTP_ERR_INVALID_ARG;
+  // the kernels take row maxima of raw scores before scaling: the scale must be positive
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return WMTP_ERR_INVALID_ARG;
   if (!q || !k_cache || !v_cache || !block_table || !seq_lens) return WMTP_ERR_INVALID_ARG;
   if (!(flags & WMTP_FLAG_PARTIALS_ONLY) && !o) return WMTP_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || (o && !aligned16(o)) ||
@@ -187,7 +188,8 @@ wmtp_status wmtp_draft_attn_window(const uint16_t* q, const uint16_t* ring_k,
     return WMTP_ERR_INVALID_ARG;
   if ((long)B * C > (long)INT_MAX) return WMTP_ERR_INVALID_ARG;
   if ((flags & ~WMTP_FLAG_PARTIALS_ONLY) != 0) return WMTP_ERR_INVALID_ARG;
-  if (!std::isfinite(softmax_scale)) return WMTP_ERR_INVALID_ARG;
+  // the kernels take row maxima of raw scores before scaling: the scale must be positive
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return WMTP_ERR_INVALID_ARG;
   if (!q || !ring_k || !ring_v || !ring_pos || !ring_T) return WMTP_ERR_INVALID_ARG;
   if (!(flags & WMTP_FLAG_PARTIALS_ONLY) && !o) return WMTP_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(ring_k) || !aligned16(ring_v) || !aligned16(ring_pos) ||

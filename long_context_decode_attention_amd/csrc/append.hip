@@ -18,11 +18,12 @@ __device__ __forceinline__ void store_kv8(uint16_t* kc, uint16_t* vc, size_t til
   const u32x4 vv = *reinterpret_cast<const u32x4*>(vsrc);
   uint16_t* kt = kc + tile * (size_t)(32 * D);
   uint16_t* vt = vc + tile * (size_t)(32 * D);
-  *reinterpret_cast<u32x4*>(kt + (d0 >> 5) * 1024 + tok * 32 + (d0 & 31)) = kv;
+  *reinterpret_cast<u32x4*>(kt + (d0 >> 4) * 512 + tok * 16 + (d0 & 15)) = kv;
+  uint16_t* vp = vt + (tok >> 4) * (16 * D) + (tok & 15);
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    vt[(d0 + 2 * w) * 32 + tok] = (uint16_t)(vv[w] & 0xFFFFu);
-    vt[(d0 + 2 * w + 1) * 32 + tok] = (uint16_t)(vv[w] >> 16);
+    vp[(d0 + 2 * w) * 16] = (uint16_t)(vv[w] & 0xFFFFu);
+    vp[(d0 + 2 * w + 1) * 16] = (uint16_t)(vv[w] >> 16);
   }
 }
 

@@ -1,32 +1,24 @@
 // Split-KV decode attention for gfx950: the native draft (every cached key),
-// the windowed draft (the valid slots of a sink-plus-recent ring) and the
-// causal verify of n_q proposed positions share this kernel.
+// the windowed draft (the valid slots of a sink-plus-recent ring) and a verify
+// with at most 32 query rows per kv head share this kernel.
 //
 // Work decomposition.  One workgroup (4 waves) owns one key split of one
-// (sequence b, kv head g) pair and a group of up to 16 * NRB query rows of that
-// kv head (the G query heads of the group, times n_q verify queries).  The
-// split is a run of 32-key tiles; wave w of the workgroup takes tiles
-// w, w + 4, w + 8, ... so the four waves stream neighbouring memory.  Each wave
-// keeps its own online-softmax state; the four are merged through LDS at the
-// end and the workgroup writes one partial (o, lse) per row, or the final
-// result when the sequence has a single split.
+// (sequence b, kv head g) pair and a group of up to 32 * NB query rows of that
+// kv head (the G query heads of the group, times n_q verify queries).  The split
+// is a run of 32-key tiles; wave w of the workgroup takes tiles w, w + 4, ...,
+// so the four waves stream neighbouring memory.  Each wave keeps its own
+// online-softmax state; the four are merged through LDS at the end and the
+// workgroup writes one partial (o, lse) per row, or the final result when the
+// sequence has a single split.
 //
-// Per 32-key tile a wave computes, with bf16 MFMA 16x16x32 and fp32 accumulation,
-//     S^T[key][row] = K[key][:] . Q[row][:]          (2 key blocks x D/32 steps)
-//     O^T[d][row]  += V^T[d][key] . P^T[key][row]    (D/16 blocks, 2 steps:
-//                                                     P as bf16 hi + lo parts)
-// Keys sit on the MFMA M axis of S^T, so the S^T accumulator a lane receives
-// (column = its query row, rows 4*(lane/16)+i) holds exactly the 8 keys that
-// the same lane must feed as the contraction slice of P^T for the PV product;
-// the key order inside the first product is chosen so that these are keys
-// 8*(lane/16) .. +7.  No value crosses lanes between the two products except
-// the row maximum, reduced over the four lane groups.
-//
-// Operand loads are 16 bytes per lane straight from the tiled page layout:
-// a K operand fetches 16 rows of 64 contiguous bytes (a 2 KB dim-tile per key
-// block pair), a V operand 1 KB contiguous.  Each wave double-buffers its tiles
-// in registers: the loads of tile t+4 are in flight while tile t is computed.
+// Per tile a wave runs the products of attn_device.h on MFMA 32x32x16.  K and V
+// operands are 16-byte non-temporal loads straight from the tiled page layout
+// into registers; the next tile's K loads are issued as soon as the S^T
+// products have consumed the current ones, V likewise after PV, so one tile of
+// each is always in flight.
 #include "attn_device.h"
+
+#include <type_traits>
 
 // Workgroups the split planner aims at: two per CU for the split-keys kernel
 // (one resident at a time), one per CU for the shared kernel.
@@ -41,14 +33,90 @@ namespace wmtp {
 
 namespace {
 
-template <int D, int NRB, bool RING>
+template <int D, bool RING>
+struct KTile {
+  bf16x8 k[D / 16];             // K operands, head-dim step ks
+  int32_t pos[RING ? 16 : 1];   // ring mode: positions held by this lane's 16 slots
+};
+
+template <int D>
+struct VTile {
+  bf16x8 v[D / 32][2];          // V^T operands, head-dim block db, key step kk
+};
+
+// Physical 32-key tile index of tile kb of (b, g); ok = false when the page id
+// is outside the cache: the index is then that of page 0, and the tile's keys
+// count as absent.
+template <bool RING>
+__device__ __forceinline__ size_t tile_index(const AttnArgs& a, int b, int g, int kb, bool& ok) {
+  const int lpage = kb >> 1;
+  int ppage;
+  if constexpr (RING) {
+    ppage = b * (a.C >> 6) + lpage;
+  } else {
+    ppage = a.block_table[(size_t)b * a.max_pages + lpage];
+  }
+  ok = (unsigned)ppage < (unsigned)a.num_pages;
+  if (!ok) ppage = 0;   // still loaded (so that every load is unconditional), then ignored
+  return ((size_t)ppage * a.Hkv + g) * 2 + (kb & 1);
+}
+
+template <int D, bool RING>
+__device__ __forceinline__ void load_k(KTile<D, RING>& t, const AttnArgs& a, size_t tile, int b,
+                                       int kb, int m, int h) {
+  const uint16_t* kt = a.kc + tile * (size_t)(32 * D);
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) t.k[ks] = ld_bf16x8_stream(kt + k_operand_offset(ks, m, h));
+  if constexpr (RING) {
+    // slots 8h..8h+7 and 16+8h..16+8h+7 of the tile
+    const int32_t* rp = a.ring_pos + (size_t)b * a.C + kb * 32 + 8 * h;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int4 p0 = *reinterpret_cast<const int4*>(rp + 16 * r);
+      const int4 p1 = *reinterpret_cast<const int4*>(rp + 16 * r + 4);
+      t.pos[8 * r + 0] = p0.x; t.pos[8 * r + 1] = p0.y; t.pos[8 * r + 2] = p0.z;
+      t.pos[8 * r + 3] = p0.w; t.pos[8 * r + 4] = p1.x; t.pos[8 * r + 5] = p1.y;
+      t.pos[8 * r + 6] = p1.z; t.pos[8 * r + 7] = p1.w;
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void load_v(VTile<D>& t, const AttnArgs& a, size_t tile, int m, int h) {
+  const uint16_t* vt = a.vc + tile * (size_t)(32 * D);
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) t.v[db][kk] = ld_bf16x8_stream(vt + v_operand_offset<D>(db, kk, m, h));
+}
+
+// Which of this lane's 16 keys exist for every row: inside the sequence length,
+// or (ring) holding a position of the current window.
+template <int D, bool RING>
+__device__ __forceinline__ uint32_t present_keys(const KTile<D, RING>& t, const AttnArgs& a,
+                                                 int kb, int L, int T, int h) {
+  if constexpr (RING) {
+    uint32_t keep = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int p = t.pos[i];
+      const bool ok = p >= 0 && p < T && (p < a.n_sink || p >= T - a.n_recent);
+      keep |= (ok ? 1u : 0u) << i;
+    }
+    return keep;
+  } else {
+    return keys_below(L - kb * 32, h);
+  }
+}
+
+template <int D, int NB, bool RING>
 __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
-  constexpr int KS = D / 32;
-  constexpr int DB = D / 16;
+  constexpr int KS = D / 16;
+  constexpr int DB = D / 32;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n = lane & 15;
-  const int j = lane >> 4;
+  const int m = lane & 31;   // MFMA row / column of this lane
+  const int h = lane >> 5;   // lane group
 
   // Workgroup -> (item, row group).  With several row groups, the workgroups of
   // one item are spaced 8 apart in launch order so that they land on the same
@@ -69,7 +137,7 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
   const int bg = item / a.nsplit;
   const int g = bg % a.Hkv;
   const int b = bg / a.Hkv;
-  const int row0 = rg * 16 * NRB;
+  const int row0 = rg * 32 * NB;
 
   int L, T = 0;
   if (RING) {
@@ -84,127 +152,182 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
   const int kb0 = s * a.kb_per_split;
   const int kb1 = min(kb0 + a.kb_per_split, nkb);
 
-  // Q^T operands: lane (n, j) holds row row0 + 16*rb + n, dims 32*ks + 8*j .. +7.
-  bf16x8 qop[NRB][KS];
-  int lim[NRB];
-#pragma unroll
-  for (int rb = 0; rb < NRB; ++rb) {
-    const int row = row0 + rb * 16 + n;
+  // Q^T operands, staged once in LDS in MFMA lane order (sm_q[rb][ks][lane]:
+  // row row0 + 32*rb + m, dims 16*ks + 8*h .. +7) and read back per tile; in
+  // registers they would push the tile buffers into scratch at D = 256.
+  __shared__ bf16x8 sm_q[NB][KS][64];
+  for (int idx = threadIdx.x; idx < NB * KS * 64; idx += 256) {
+    const int ln = idx & 63;
+    const int ks = (idx >> 6) % KS;
+    const int rb = idx / (64 * KS);
+    const int row = row0 + rb * 32 + (ln & 31);
+    bf16x8 v = zero_bf16x8();
     if (row < a.R) {
       const int qi = row / a.G;
       const int hl = row - qi * a.G;
-      const uint16_t* qp =
-          a.q + ((size_t)(b * a.n_q + qi) * a.Hq + g * a.G + hl) * D + j * 8;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qop[rb][ks] = ld_bf16x8(qp + ks * 32);
-      lim[rb] = RING ? L : L - a.n_q + qi + 1;
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qop[rb][ks] = zero_bf16x8();
-      lim[rb] = L;
+      v = ld_bf16x8(a.q + ((size_t)(b * a.n_q + qi) * a.Hq + g * a.G + hl) * D + ks * 16 +
+                    (ln >> 5) * 8);
     }
+    sm_q[rb][ks][ln] = v;
+  }
+  __syncthreads();
+  int lim[NB];
+#pragma unroll
+  for (int rb = 0; rb < NB; ++rb) {
+    const int row = row0 + rb * 32 + m;
+    lim[rb] = (row < a.R && !RING) ? L - a.n_q + row / a.G + 1 : L;
   }
 
-  SoftmaxState<D, NRB> st;
+  SoftmaxState<D, NB> st;
 #pragma unroll
-  for (int rb = 0; rb < NRB; ++rb) {
+  for (int rb = 0; rb < NB; ++rb) {
     st.m[rb] = -INFINITY;
     st.l[rb] = 0.f;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) st.acc[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int db = 0; db < DB; ++db) st.acc[rb][db] = f32x16{};
   }
 
-  // Main loop over this wave's tiles.  K registers are refilled with the next
-  // tile as soon as the S^T products have consumed them, V registers as soon as
-  // the PV products have: one tile of each is always in flight.
+  // Loop over this wave's tiles.  K registers are refilled with the next tile as
+  // soon as the S^T products have consumed them, V registers as soon as the PV
+  // products have: one tile of each is always in flight.  Loads are
+  // unconditional (a tile with a bad page id is loaded from page 0 and then
+  // masked), so the loop carries the tile registers without copies.
   KTile<D, RING> kt;
   VTile<D> vt;
   int kb = kb0 + wave;
   bool ok = false;
   if (kb < kb1) {
     const size_t tile = tile_index<RING>(a, b, g, kb, ok);
-    if (ok) {
-      load_k<D, RING>(kt, a, tile, b, kb, n, j);
-      load_v<D>(vt, a, tile, n, j);
-    }
+    load_k<D, RING>(kt, a, tile, b, kb, m, h);
+    load_v<D>(vt, a, tile, m, h);
   }
-  while (kb < kb1) {
-    const int kbn = kb + 4;
-    bool ok_n = false;
-    size_t tile_n = 0;
-    if (kbn < kb1) tile_n = tile_index<RING>(a, b, g, kbn, ok_n);
-    const int kbase = kb * 32 + 8 * j;   // this lane's 8 keys: kbase .. kbase + 7
-    if (ok) {
-      const uint32_t keep = present_keys<D, RING>(kt, a, kbase, L, T);
-      f32x4 s[NRB][2];
-#pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) {
-        s[rb][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-        s[rb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          s[rb][0] = mfma16x16x32(kt.k[0][ks], qop[rb][ks], s[rb][0]);
-          s[rb][1] = mfma16x16x32(kt.k[1][ks], qop[rb][ks], s[rb][1]);
-        }
-      }
-      if (ok_n) load_k<D, RING>(kt, a, tile_n, b, kbn, n, j);
-      bf16x8 p_hi[NRB], p_lo[NRB];
-#pragma unroll
-      for (int rb = 0; rb < NRB; ++rb)
-        softmax_update<D, NRB>(st, rb, s[rb][0], s[rb][1], keep, lim[rb] - kbase, a.scale_log2,
-                               p_hi[rb], p_lo[rb]);
-      // Absent keys may hold any bits (even NaN): zero their values so that
-      // 0-weight * value stays 0 in the PV product.
-      if (!__all(keep == 0xFFu)) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db) vt.v[db] = mask_bf16x8(vt.v[db], keep);
-      }
-#pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          st.acc[rb][db] = mfma16x16x32(vt.v[db], p_hi[rb], st.acc[rb][db]);
-          st.acc[rb][db] = mfma16x16x32(vt.v[db], p_lo[rb], st.acc[rb][db]);
-        }
-      }
-      if (ok_n) load_v<D>(vt, a, tile_n, n, j);
-    } else if (ok_n) {
-      load_k<D, RING>(kt, a, tile_n, b, kbn, n, j);
-      load_v<D>(vt, a, tile_n, n, j);
-    }
+  int kbn = kb;
+  bool ok_n = false;
+  size_t tile_n = 0;
+  float x[NB][16], mx[NB];
+  uint32_t keep = 0;
+  bool mask_v = false;
+  auto next_tile = [&]() {
+    kbn = kb + 4;
+    tile_n = tile_index<RING>(a, b, g, kbn, ok_n);
+  };
+  auto advance = [&]() {
     ok = ok_n;
     kb = kbn;
+  };
+  // S^T of tile kb, refill K (when there is a next tile), masked scores.
+  auto scores_of = [&](auto has_next) {
+    keep = ok ? present_keys<D, RING>(kt, a, kb, L, T, h) : 0u;
+    bool all_vis;
+    if (RING) {
+      all_vis = __all(keep == 0xFFFFu);
+      mask_v = !all_vis;
+    } else {
+      // every key present and visible to every row (smallest causal limit L - n_q + 1)
+      all_vis = ok && (kb + 1) * 32 <= L - a.n_q + 1;
+      mask_v = !ok || (kb + 1) * 32 > L;
+    }
+    f32x16 sacc[NB];
+#pragma unroll
+    for (int rb = 0; rb < NB; ++rb) {
+      sacc[rb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) sacc[rb] = mfma32x32x16(kt.k[ks], sm_q[rb][ks][lane], sacc[rb]);
+    }
+    if constexpr (decltype(has_next)::value) load_k<D, RING>(kt, a, tile_n, b, kbn, m, h);
+#pragma unroll
+    for (int rb = 0; rb < NB; ++rb) {
+      const uint32_t vis = RING ? keep : keep & keys_below(lim[rb] - kb * 32, h);
+      mx[rb] = masked_scores(x[rb], sacc[rb], vis, all_vis, a.scale_log2);
+    }
+  };
+  // Weights, PV, refill V (when there is a next tile).
+  auto finish = [&](auto has_next) {
+    bf16x8 p_hi[NB][2], p_lo[NB][2];
+#pragma unroll
+    for (int rb = 0; rb < NB; ++rb) weights<D, NB>(st, rb, x[rb], a.scale_log2, p_hi[rb], p_lo[rb]);
+    if (mask_v) {
+      // Absent keys may hold any bits (even NaN): zero their values so that
+      // 0-weight * value stays 0 in the PV product.
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) vt.v[db][kk] = mask8(vt.v[db][kk], (keep >> (8 * kk)) & 0xFFu);
+    }
+    pv<D, NB>(st, vt.v, p_hi, p_lo);
+    if constexpr (decltype(has_next)::value) load_v<D>(vt, a, tile_n, m, h);
+  };
+  const std::true_type more;
+  const std::false_type last;
+
+  // Fast loop over the tiles that have a successor: no accumulator rescale.  It
+  // leaves early when tile kb needs one; its scores are then already in x / mx.
+  bool general = false;
+  while (kb + 4 < kb1) {
+    next_tile();
+    scores_of(more);
+    if (first_max_or_rescale<D, NB>(st, mx)) {
+      general = true;
+      break;
+    }
+    finish(more);
+    advance();
+  }
+  // General loop, from the tile the fast loop left on.
+  if (general) {
+    raise_and_rescale<D, NB>(st, mx);
+    finish(more);
+    advance();
+    while (kb + 4 < kb1) {
+      next_tile();
+      scores_of(more);
+      raise_and_rescale<D, NB>(st, mx);
+      finish(more);
+      advance();
+    }
+  }
+  // The wave's last tile.
+  if (kb < kb1) {
+    scores_of(last);
+    if (general || first_max_or_rescale<D, NB>(st, mx)) raise_and_rescale<D, NB>(st, mx);
+    finish(last);
   }
 
   // ---- merge the four waves' states through LDS, one row block at a time ----
-  __shared__ float sm_m[4][16];
-  __shared__ float sm_l[4][16];
-  __shared__ f32x4 sm_acc[3][DB][64];
+  __shared__ float sm_m[4][32];
+  __shared__ float sm_l[4][32];
+  __shared__ f32x4 sm_acc[3][DB][4][64];
 
 #pragma unroll
-  for (int rb = 0; rb < NRB; ++rb) {
-    const float lsum = sum_over_lane_groups(st.l[rb]);
+  for (int rb = 0; rb < NB; ++rb) {
+    const float lsum = sum_over_row(st.l[rb]);
     __syncthreads();   // previous round's readers are done with the buffers
-    if (j == 0) {
-      sm_m[wave][n] = st.m[rb];
-      sm_l[wave][n] = lsum;
+    if (h == 0) {
+      sm_m[wave][m] = st.m[rb];
+      sm_l[wave][m] = lsum;
     }
     __syncthreads();
-    float M = sm_m[0][n];
+    float M = sm_m[0][m];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) M = fmaxf(M, sm_m[w][n]);
+    for (int w = 1; w < 4; ++w) M = fmaxf(M, sm_m[w][m]);
     const float Mu = (M == -INFINITY) ? 0.f : M;
     float Ltot = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) Ltot += sm_l[w][n] * fast_exp2(sm_m[w][n] - Mu);
+    for (int w = 0; w < 4; ++w) Ltot += sm_l[w][m] * fast_exp2(sm_m[w][m] - Mu);
     const float f = fast_exp2(st.m[rb] - Mu);
     if (wave > 0) {
 #pragma unroll
-      for (int db = 0; db < DB; ++db) sm_acc[wave - 1][db][lane] = st.acc[rb][db] * f;
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const f32x4 v = {st.acc[rb][db][4 * c], st.acc[rb][db][4 * c + 1],
+                           st.acc[rb][db][4 * c + 2], st.acc[rb][db][4 * c + 3]};
+          sm_acc[wave - 1][db][c][lane] = v * f;
+        }
     }
     __syncthreads();
     if (wave == 0) {
-      const int row = row0 + rb * 16 + n;
+      const int row = row0 + rb * 32 + m;
       if (row < a.R) {
         const float inv = Ltot > 0.f ? 1.f / Ltot : 0.f;
         float* op;
@@ -220,41 +343,32 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
           lp = a.out_lse + (size_t)item * a.R + row;
         }
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          f32x4 v = st.acc[rb][db] * f;
-          v += sm_acc[0][db][lane];
-          v += sm_acc[1][db][lane];
-          v += sm_acc[2][db][lane];
-          *reinterpret_cast<f32x4*>(op + db * 16 + 4 * j) = v * inv;
-        }
-        if (j == 0 && lp) *lp = Ltot > 0.f ? (M + fast_log2(Ltot)) * kLn2 : -INFINITY;
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            f32x4 v = {st.acc[rb][db][4 * c], st.acc[rb][db][4 * c + 1],
+                       st.acc[rb][db][4 * c + 2], st.acc[rb][db][4 * c + 3]};
+            v = v * f + sm_acc[0][db][c][lane] + sm_acc[1][db][c][lane] + sm_acc[2][db][c][lane];
+            *reinterpret_cast<f32x4*>(op + db * 32 + 8 * c + 4 * h) = v * inv;
+          }
+        if (h == 0 && lp) *lp = Ltot > 0.f ? (M + fast_log2(Ltot)) * kLn2 : -INFINITY;
       }
     }
   }
 }
 
-template <int D, int NRB, bool RING>
+template <int D, int NB, bool RING>
 hipError_t launch_one(const AttnArgs& a, int grid, hipStream_t stream) {
   AttnArgs arg = a;
   void* args[] = {&arg};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_split_kernel<D, NRB, RING>),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_split_kernel<D, NB, RING>),
                          dim3(grid), dim3(256), args, 0, stream);
 }
 
 template <int D>
 hipError_t launch_d(const AttnArgs& a, const AttnPlan& p, bool ring, hipStream_t stream) {
-  if constexpr (D == 256) {   // one row block per wave only (two would spill)
-    if (p.nrb != 1) return hipErrorInvalidValue;
-    return ring ? launch_one<D, 1, true>(a, p.grid, stream)
-                : launch_one<D, 1, false>(a, p.grid, stream);
-  } else {
-    if (ring) {
-      return p.nrb == 1 ? launch_one<D, 1, true>(a, p.grid, stream)
-                        : launch_one<D, 2, true>(a, p.grid, stream);
-    }
-    return p.nrb == 1 ? launch_one<D, 1, false>(a, p.grid, stream)
-                      : launch_one<D, 2, false>(a, p.grid, stream);
-  }
+  if (p.nrb != 1) return hipErrorInvalidValue;
+  return ring ? launch_one<D, 1, true>(a, p.grid, stream) : launch_one<D, 1, false>(a, p.grid, stream);
 }
 
 }  // namespace
@@ -273,21 +387,23 @@ bool plan_attention(int B, int Hq, int Hkv, int D, int n_q, int max_keys, int nu
   int cap;        // most 32-key tiles per split
   // Few rows: each wave holds every row and the four waves split the keys.
   // Two row blocks per wave need too many registers at D = 256 (they spill).
-  if (ring || p->R <= 16 || (p->R <= 32 && D != 256)) {
+  if (ring || p->R <= 32) {
     p->shared = 0;
-    p->nrb = (p->R <= 16 || D == 256) ? 1 : 2;
-    p->nrg = (p->R + 16 * p->nrb - 1) / (16 * p->nrb);
+    p->nrb = 1;                             // one 32-row block per wave
+    p->nrg = (p->R + 31) / 32;
     target = WMTP_TARGET_WG_SPLIT;
     cap = INT_MAX;
   } else {
     // Many rows: the waves split the rows and share each K/V tile through LDS.
-    // A workgroup holds 16 * rbw rows per wave; two row blocks per wave are too
-    // many registers at D = 256 for two waves per SIMD.
+    // A wave holds 32 * rbw rows: the fewest that cover R, at most one block at
+    // D = 256 and two below (register file); beyond that the rows go to row groups.
     p->shared = 1;
     const int nw = shared_kernel_waves();
-    const int rbw = (p->R > 16 * nw && D != 256) ? 2 : 1;
+    const int rbw_max = D == 256 ? 1 : 2;
+    int rbw = 1;
+    while (rbw < rbw_max && 32 * nw * rbw < p->R) rbw *= 2;
     p->nrb = rbw;
-    p->nrg = (p->R + 16 * nw * rbw - 1) / (16 * nw * rbw);
+    p->nrg = (p->R + 32 * nw * rbw - 1) / (32 * nw * rbw);
     target = WMTP_TARGET_WG_SHARED;
     cap = shared_kernel_max_tiles();
   }

@@ -1,6 +1,18 @@
 // Device-side pieces shared by the split-KV attention kernels (attn.hip,
-// attn_shared.hip): operand addressing in the tiled page layout, the
-// online-softmax update, and the partial / final output write.
+// attn_shared.hip): MFMA operand addressing in the tiled page layout, the
+// online-softmax steps, and the output write.
+//
+// Products per 32-position tile and 32 query rows (MFMA 32x32x16, bf16 in, fp32
+// accumulate):
+//     S^T[key][row] = K[key][:] . Q[row][:]         D/16 steps
+//     O^T[d][row]  += V^T[d][key] . P^T[key][row]   D/32 blocks x 2 steps (x2: P hi, lo)
+// Keys sit on the M axis of S^T.  The K rows are fed in an order (bits 2 and 3 of
+// the MFMA row index swapped) that makes S^T register i of lane (n, h), n = lane
+// % 32, h = lane / 32, hold key 16*(i/8) + 8*h + i%8 of row n; registers 0..7 and
+// 8..15 are then exactly the lane's contraction slices of P^T for the two PV
+// steps (keys 8h..8h+7 and 16+8h..16+8h+7), and the matching V^T operand is 16
+// contiguous bytes of the V tile.  No value crosses lanes between the products
+// except the row maximum, over the two lanes n and n + 32.
 #pragma once
 
 #include "common.h"
@@ -13,169 +25,216 @@ namespace wmtp {
 
 constexpr float kLn2 = 0.693147180559945309f;
 
-// Element offset, inside a 32-position K tile, of the 16 bytes lane (n, j)
-// feeds as the MFMA A operand of key block bb, head-dim step ks.  A row n of
-// key block bb is key 8*(n/4) + 4*bb + n%4 of the tile, so that the S^T
-// accumulator rows a lane receives are keys 8*(lane/16) .. +7.
-__device__ __forceinline__ int k_operand_offset(int bb, int ks, int n, int j) {
-  const int tok = 8 * (n >> 2) + 4 * bb + (n & 3);
-  return ks * 1024 + tok * 32 + j * 8;
+// MFMA row m of the S^T product holds tile key m with bits 2 and 3 swapped.
+__device__ __forceinline__ int s_row_key(int m) {
+  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
 
-// Element offset, inside a 32-position V tile, of lane (n, j)'s 16 bytes of
-// the V^T operand of head-dim block db: dims 16*db + n, keys 8*j .. +7.
-__device__ __forceinline__ int v_operand_offset(int db, int n, int j) {
-  return (db * 16 + n) * 32 + j * 8;
+// Element offset, inside a 32-position K tile ([D/16][32 pos][16 dims]), of the
+// 16 bytes lane (m, h) feeds as A operand of head-dim step ks (dims 16*ks + 8*h
+// ..).  The 64 lanes of one step read the step's whole 1 KB block.
+__device__ __forceinline__ int k_operand_offset(int ks, int m, int h) {
+  return ks * 512 + s_row_key(m) * 16 + h * 8;
 }
 
-template <int D, bool RING>
-struct KTile {
-  bf16x8 k[2][D / 32];   // K operands: key block bb, head-dim step ks
-  int32_t pos[RING ? 8 : 1];   // ring mode: positions held by this lane's 8 slots
-};
-
+// Element offset, inside a 32-position V tile ([2][D][16 pos]), of lane (m, h)'s
+// 16 bytes of the V^T operand of head-dim block db, key step kk: dim 32*db + m,
+// keys 16*kk + 8*h .. +7.  The 64 lanes read one contiguous 1 KB block.
 template <int D>
-struct VTile {
-  bf16x8 v[D / 16];      // V^T operands: head-dim block db
-};
-
-// Physical 32-key tile index of tile kb of (b, g), or ok = false when the
-// page id is outside the cache (its keys then count as absent).
-template <bool RING>
-__device__ __forceinline__ size_t tile_index(const AttnArgs& a, int b, int g, int kb, bool& ok) {
-  const int lpage = kb >> 1;
-  int ppage;
-  if constexpr (RING) {
-    ppage = b * (a.C >> 6) + lpage;
-  } else {
-    ppage = a.block_table[(size_t)b * a.max_pages + lpage];
-  }
-  ok = (unsigned)ppage < (unsigned)a.num_pages;
-  return ((size_t)ppage * a.Hkv + g) * 2 + (kb & 1);
+__device__ __forceinline__ int v_operand_offset(int db, int kk, int m, int h) {
+  return kk * (16 * D) + (db * 32 + m) * 16 + h * 8;
 }
 
-template <int D, bool RING>
-__device__ __forceinline__ void load_k(KTile<D, RING>& t, const AttnArgs& a, size_t tile, int b,
-                                       int kb, int n, int j) {
-  constexpr int KS = D / 32;
-  const uint16_t* kt = a.kc + tile * (size_t)(32 * D);
-#pragma unroll
-  for (int bb = 0; bb < 2; ++bb) {
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      t.k[bb][ks] = ld_bf16x8_stream(kt + k_operand_offset(bb, ks, n, j));
-  }
-  if constexpr (RING) {
-    const int32_t* rp = a.ring_pos + (size_t)b * a.C + kb * 32 + j * 8;
-    const int4 p0 = *reinterpret_cast<const int4*>(rp);
-    const int4 p1 = *reinterpret_cast<const int4*>(rp + 4);
-    t.pos[0] = p0.x; t.pos[1] = p0.y; t.pos[2] = p0.z; t.pos[3] = p0.w;
-    t.pos[4] = p1.x; t.pos[5] = p1.y; t.pos[6] = p1.z; t.pos[7] = p1.w;
-  }
-}
+// Tile-relative key held by S^T register i of lane group h.
+__host__ __device__ constexpr int s_key(int i, int h) { return 16 * (i >> 3) + 8 * h + (i & 7); }
 
-template <int D>
-__device__ __forceinline__ void load_v(VTile<D>& t, const AttnArgs& a, size_t tile, int n, int j) {
-  constexpr int DB = D / 16;
-  const uint16_t* vt = a.vc + tile * (size_t)(32 * D);
-#pragma unroll
-  for (int db = 0; db < DB; ++db) t.v[db] = ld_bf16x8_stream(vt + v_operand_offset(db, n, j));
-}
-
-template <int D, int NRB>
+template <int D, int NB>
 struct SoftmaxState {
-  f32x4 acc[NRB][D / 16];   // O^T accumulators: lane (n, j) holds d = 16*db + 4*j + i, row n
-  float m[NRB];             // running row max of the scaled logits (log2 units)
-  float l[NRB];             // this lane's share of the running sum of weights
+  f32x16 acc[NB][D / 32];   // O^T: lane (n, h) register i holds d = 32*db + 8*(i/4) + 4*h + i%4
+  float m[NB];              // running row max of the scaled logits (log2 units)
+  float l[NB];              // this lane's share of the running sum of weights
 };
 
-// Keys of this lane's 8 (kbase .. kbase+7) that exist for every row: inside the
-// sequence length, or (ring) holding a position of the current window.
-template <int D, bool RING>
-__device__ __forceinline__ uint32_t present_keys(const KTile<D, RING>& t, const AttnArgs& a,
-                                                 int kbase, int L, int T) {
-  uint32_t keep;
-  if constexpr (RING) {
-    keep = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int p = t.pos[i];
-      const bool ok = p >= 0 && p < T && (p < a.n_sink || p >= T - a.n_recent);
-      keep |= (ok ? 1u : 0u) << i;
-    }
-  } else {
-    const int rem = L - kbase;
-    keep = rem >= 8 ? 0xFFu : (rem <= 0 ? 0u : ((1u << rem) - 1u));
-  }
-  return keep;
+// 16 bits: which of this lane's keys are below `count` (tile-relative): keys
+// 8h..8h+7 are bits 0..7, keys 16+8h..16+8h+7 bits 8..15.
+__device__ __forceinline__ uint32_t keys_below(int count, int h) {
+  const int r0 = count - 8 * h;
+  const int r1 = r0 - 16;
+  const uint32_t b0 = r0 >= 8 ? 0xFFu : (r0 <= 0 ? 0u : ((1u << r0) - 1u));
+  const uint32_t b1 = r1 >= 8 ? 0xFFu : (r1 <= 0 ? 0u : ((1u << r1) - 1u));
+  return b0 | (b1 << 8);
 }
 
-// Online-softmax update of one row block from its S^T accumulators.  The weights
-// this lane feeds to the PV product are returned as two bf16 parts, p = hi + lo
-// (hi = bf16(p), lo = bf16(p - hi)), so that PV sees p to about 2^-16 relative
-// instead of bf16's 2^-9; the running sum adds the fp32 weights.
-//
-// The running maximum m (log2 units, uniform over the four lanes of a row) is
-// only raised when some score of the wave exceeds it by more than kLazyMax:
-// weights are exp2(x - m) <= 2^kLazyMax either way, so nothing overflows, and
-// the result (sum p v / sum p, lse = m + log2 sum p) does not depend on which m
-// was used.  Most tiles then need neither the cross-lane max nor a rescale of
-// the accumulators.
-constexpr float kLazyMax = 8.0f;
+// Max / sum over the two lanes of a row (n and n + 32).
+__device__ __forceinline__ float max_over_row(float v) { return fmaxf(v, __shfl_xor(v, 32)); }
+__device__ __forceinline__ float sum_over_row(float v) { return v + __shfl_xor(v, 32); }
 
-template <int D, int NRB>
-__device__ __forceinline__ void softmax_update(SoftmaxState<D, NRB>& st, int rb, f32x4 s0,
-                                               f32x4 s1, uint32_t keep, int lr, float scale_log2,
-                                               bf16x8& p_hi, bf16x8& p_lo) {
-  constexpr int DB = D / 16;
-  // s0[i] is key kbase + i, s1[i] is key kbase + 4 + i, for this lane's row.
-  float x[8];
-  if (keep == 0xFFu && lr >= 8) {
+// Online softmax in log2 units: scores x = s * c with c = scale * log2(e) > 0,
+// weights p = exp2(x - m).  The running maximum m of a row (the same on its two
+// lanes) is raised lazily, only when a score exceeds it by more than kLazyMax.
+// Weights then stay below 2^kLazyMax and row sums below 2^(kLazyMax + 32), far
+// inside the fp32 and bf16 range, and the result (sum p v / sum p, lse = m +
+// log2 sum p) does not depend on which m was used.  With so wide a margin a
+// raise after a row's first visible key is rare, so the kernels run a fast loop
+// that never rescales the accumulators and fall back to a general loop only
+// when a rescale is due; a row whose m is still -inf takes its first maximum in
+// the fast loop, since its accumulators and sum are still zero.  The weights
+// reach PV as two bf16 parts, p = hi + lo (hi = bf16(p), lo = bf16(p - hi)), so
+// PV sees p to about 2^-16 relative instead of bf16's 2^-9; the running sum adds
+// the fp32 weights.
+constexpr float kLazyMax = 64.0f;
+
+// This lane's keys visible to a row whose keys below `lr` (tile-relative) are in
+// its causal range, among the present ones.
+__device__ __forceinline__ uint32_t visible_keys(uint32_t keep, int lr, int h) {
+  return keep & keys_below(lr, h);
+}
+
+__device__ __forceinline__ float lane_max16(const float (&x)[16]) {
+  float a = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+  float b = fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7]));
+  float c = fmaxf(fmaxf(x[8], x[9]), fmaxf(x[10], x[11]));
+  float d = fmaxf(fmaxf(x[12], x[13]), fmaxf(x[14], x[15]));
+  return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+
+// Raw scores of one row block, -inf where the key is not visible, and the lane
+// maximum in log2 units.  all_vis (wave-uniform): every key is visible to every
+// row, the common case, which skips the masking.
+__device__ __forceinline__ float masked_scores(float (&x)[16], const f32x16& s, uint32_t vis,
+                                               bool all_vis, float c) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = (i < 4 ? s0[i] : s1[i - 4]) * scale_log2;
-  } else {
+  for (int i = 0; i < 16; ++i) x[i] = s[i];
+  if (!all_vis) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float v = (i < 4 ? s0[i] : s1[i - 4]) * scale_log2;
-      const bool ok = ((keep >> i) & 1u) && (i < lr);
-      x[i] = ok ? v : -INFINITY;
+    for (int i = 0; i < 16; ++i) x[i] = ((vis >> i) & 1u) ? x[i] : -INFINITY;
+  }
+  return lane_max16(x) * c;
+}
+
+// Does this lane's row need its maximum raised?  (m = -inf: -inf <= -inf holds
+// only when this lane saw no key either.)
+__device__ __forceinline__ bool needs_raise(float lane_mx, float m) {
+  return !(lane_mx <= m + kLazyMax);
+}
+
+// Ties an accumulator block to the accumulation registers at this point, so that
+// the compiler keeps the O^T blocks there for the whole loop.
+__device__ __forceinline__ void pin_acc(f32x16& v) { asm volatile("" : "+a"(v)); }
+
+// Fast-loop maximum update: rows without a maximum take their first one.
+// Returns true (wave-uniform) when some row that has a maximum needs it raised:
+// the caller then hands the tile to the general loop.
+template <int D, int NB>
+__device__ __forceinline__ bool first_max_or_rescale(SoftmaxState<D, NB>& st,
+                                                     const float (&mx)[NB]) {
+  bool raise = false, rescale = false;
+#pragma unroll
+  for (int rb = 0; rb < NB; ++rb) {
+    const bool r = needs_raise(mx[rb], st.m[rb]);
+    raise |= r;
+    rescale |= r && st.m[rb] != -INFINITY;
+  }
+  if (__any(rescale)) return true;
+  if (__any(raise)) {
+#pragma unroll
+    for (int rb = 0; rb < NB; ++rb) {
+      const float row_mx = max_over_row(mx[rb]);
+      if (st.m[rb] == -INFINITY) st.m[rb] = row_mx;
     }
   }
-  float mx = x[0];
+  return false;
+}
+
+// General-loop maximum update: raise where needed and rescale the row's
+// accumulators and sum by exp2(m_old - m_new).
+template <int D, int NB>
+__device__ __forceinline__ void raise_and_rescale(SoftmaxState<D, NB>& st, const float (&mx)[NB]) {
+  constexpr int DB = D / 32;
 #pragma unroll
-  for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
-  // m = -inf: -inf <= -inf holds only when this lane saw no key either.
-  const bool raise = !(mx <= st.m[rb] + kLazyMax);
-  if (__any(raise)) {
-    const float m_new = fmaxf(st.m[rb], max_over_lane_groups(mx));
+  for (int rb = 0; rb < NB; ++rb) {
+    if (!__any(needs_raise(mx[rb], st.m[rb]))) continue;
+    const float m_new = fmaxf(st.m[rb], max_over_row(mx[rb]));
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
     const float alpha = fast_exp2(st.m[rb] - m_use);
     st.m[rb] = m_new;
     st.l[rb] *= alpha;
     if (!__all(alpha == 1.0f)) {
 #pragma unroll
-      for (int db = 0; db < DB; ++db) st.acc[rb][db] *= alpha;
+      for (int db = 0; db < DB; ++db) {
+        st.acc[rb][db] *= alpha;
+        pin_acc(st.acc[rb][db]);
+      }
     }
   }
-  const float m_use = (st.m[rb] == -INFINITY) ? 0.f : st.m[rb];
+}
 
-  u32x4 hw, lw;
+// Weights of one row block as the P^T operands of the two PV steps.
+template <int D, int NB>
+__device__ __forceinline__ void weights(SoftmaxState<D, NB>& st, int rb, const float (&x)[16],
+                                        float c, bf16x8 (&p_hi)[2], bf16x8 (&p_lo)[2]) {
+  const float neg_m = (st.m[rb] == -INFINITY) ? 0.f : -st.m[rb];
   float psum = 0.f;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const float p0 = fast_exp2(x[2 * w] - m_use);
-    const float p1 = fast_exp2(x[2 * w + 1] - m_use);
-    psum += p0 + p1;
-    const uint32_t h0 = f32_to_bf16_bits(p0);
-    const uint32_t h1 = f32_to_bf16_bits(p1);
-    const uint32_t l0 = f32_to_bf16_bits(p0 - bf16_bits_to_f32(h0));
-    const uint32_t l1 = f32_to_bf16_bits(p1 - bf16_bits_to_f32(h1));
-    hw[w] = h0 | (h1 << 16);
-    lw[w] = l0 | (l1 << 16);
+  for (int kk = 0; kk < 2; ++kk) {
+    u32x4 hw, lw;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float p0 = fast_exp2(fmaf(x[8 * kk + 2 * w], c, neg_m));
+      const float p1 = fast_exp2(fmaf(x[8 * kk + 2 * w + 1], c, neg_m));
+      psum += p0 + p1;
+      const uint32_t hp = pack_bf16x2(p0, p1);
+      const uint32_t lp = pack_bf16x2(p0 - __builtin_bit_cast(float, hp << 16),
+                                      p1 - __builtin_bit_cast(float, hp & 0xFFFF0000u));
+      hw[w] = hp;
+      lw[w] = lp;
+    }
+    p_hi[kk] = __builtin_bit_cast(bf16x8, hw);
+    p_lo[kk] = __builtin_bit_cast(bf16x8, lw);
   }
   st.l[rb] += psum;
-  p_hi = __builtin_bit_cast(bf16x8, hw);
-  p_lo = __builtin_bit_cast(bf16x8, lw);
+}
+
+// Zero the bf16 lanes of an 8-key operand whose keep bits (bit j = key j of the
+// operand) are clear, so that absent keys (any bits, even NaN) add 0 in PV.
+__device__ __forceinline__ bf16x8 mask8(bf16x8 v, uint32_t bits8) { return mask_bf16x8(v, bits8); }
+
+// PV of one tile for NB row blocks: V^T operands v[db][kk]; the hi products of
+// every accumulator first, then the lo products, so that no MFMA waits on the
+// one just before it.
+template <int D, int NB>
+__device__ __forceinline__ void pv(SoftmaxState<D, NB>& st, const bf16x8 (&v)[D / 32][2],
+                                   const bf16x8 (&p_hi)[NB][2], const bf16x8 (&p_lo)[NB][2]) {
+  constexpr int DB = D / 32;
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int rb = 0; rb < NB; ++rb)
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        st.acc[rb][db] = mfma32x32x16(v[db][kk], p_hi[rb][kk], st.acc[rb][db]);
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int rb = 0; rb < NB; ++rb)
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        st.acc[rb][db] = mfma32x32x16(v[db][kk], p_lo[rb][kk], st.acc[rb][db]);
+}
+
+// Normalised output of one row block of this lane: o[d] for the lane's 16 dims.
+template <int D, int NB>
+__device__ __forceinline__ void write_row(float* op, const SoftmaxState<D, NB>& st, int rb,
+                                          float inv, int h) {
+  constexpr int DB = D / 32;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const f32x4 v = {st.acc[rb][db][4 * c] * inv, st.acc[rb][db][4 * c + 1] * inv,
+                       st.acc[rb][db][4 * c + 2] * inv, st.acc[rb][db][4 * c + 3] * inv};
+      *reinterpret_cast<f32x4*>(op + db * 32 + 8 * c + 4 * h) = v;
+    }
 }
 
 }  // namespace wmtp

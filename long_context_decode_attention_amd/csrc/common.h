@@ -12,6 +12,7 @@ constexpr int kWave = 64;        // wavefront width on CDNA
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // 16-byte global load as 8 bf16 lanes.
@@ -52,6 +53,16 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// C[32x32] += A[32x16] * B[16x32], bf16 inputs, fp32 accumulate.
+// Lane l supplies A row (l % 32) and B column (l % 32), 8 contraction elements
+// each (the same 8 for A and B); it receives C column (l % 32), rows
+// 8 * (i / 4) + 4 * (l / 32) + i % 4 in register i (i = 0..15).  On gfx950 this
+// shape runs at the full bf16 matrix rate even with one wave per SIMD, where
+// 16x16x32 reaches about a third of it.
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
@@ -70,6 +81,14 @@ __device__ __forceinline__ float sum_over_lane_groups(float v) {
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
   __bf16 h = (__bf16)x;   // round to nearest even (v_cvt_pk_bf16_f32)
   return __builtin_bit_cast(uint16_t, h);
+}
+
+// Two floats rounded to bf16 (nearest even) and packed: a in bits 0..15, b in
+// bits 16..31 (one v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {

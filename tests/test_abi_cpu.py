@@ -84,6 +84,9 @@ def test_draft_full_argument_checks():
     assert _full(lib, B=0) == INVALID
     assert _full(lib, num_pages=0) == INVALID
     assert _full(lib, scale=float("inf")) == INVALID
+    assert _full(lib, scale=float("nan")) == INVALID
+    assert _full(lib, scale=0.0) == INVALID
+    assert _full(lib, scale=-0.5) == INVALID
     assert _full(lib, flags=8) == INVALID
     assert _full(lib, q=FAKE + 2) == INVALID              # misaligned
     # 1024 keys in 16 splits need a workspace: none given
@@ -193,3 +196,18 @@ def test_missing_library_fails_loudly(tmp_path):
             lib_mod.load(str(tmp_path / "libwmtp.so"))
     finally:
         lib_mod._lib = saved
+
+
+def test_cache_and_ring_shapes():
+    """The binding's tensor shapes hold the tiled layout of include/wmtp.h: a page
+    of one kv head is 64 * D elements in K and in V, and a ring reports its own
+    B, Hkv and D back."""
+    torch = pytest.importorskip("torch")
+    for D in (64, 128, 256):
+        k, v = lib_mod.new_paged_cache(3, 2, D, device="cpu")
+        assert k.numel() == v.numel() == 3 * 2 * 64 * D
+        assert k.dtype == v.dtype == torch.bfloat16
+        r = lib_mod.new_ring(2, 128, 2, D, 4, 100, device="cpu")
+        assert (r.B, r.Hkv, r.D) == (2, 2, D)
+        assert r.k.shape[0] == 2 * 128 // 64
+        assert int(r.pos.min()) == -1 and int(r.T.sum()) == 0

@@ -164,6 +164,62 @@ def test_needle_outside_window_moves_full_only():
     assert torch().equal(wa[0], wb[0])
 
 
+@pytest.mark.parametrize("call", ["full", "window", "verify"])
+def test_logit_jump_takes_the_rescale_path(call):
+    """Two keys whose logits sit about 1000 above every other key's, placed after
+    many ordinary tiles: the running maximum must be raised far beyond the
+    kernels' lazy margin, which sends the tile to the general (rescaling) loop;
+    the second key, a few units below the first and later in the sequence, checks
+    that tiles after the rescale are still accumulated with the right weight."""
+    lib = _lib()
+    cfg = CFG["ctx1m_g32x2_d256"]
+    D, Hkv, Hq = cfg["D"], cfg["Hkv"], cfg["Hq"]
+    G = Hq // Hkv
+    rng = np.random.default_rng(1234)
+    u = np.sign(rng.standard_normal((Hkv, D))).astype(np.float32)
+    S = 3000
+    # q.k about 4 D = 1024 and 4 below it; with one split both spikes fall in the
+    # same wave's tiles (59 and 79), the second after the rescale
+    spikes = ((1900, 4.0), (2540, 3.99))
+    if call == "verify":
+        n_q = 8
+        sc = VerifyScenario(cfg, 41, [S], n_q)
+        qf = 0.25 * W.bf16_to_f32(sc.q) + np.repeat(u, G, axis=0)[None, None]
+        q = W.bf16_round(qf)
+        from long_context_decode_attention_amd import scenario as scn
+        for p_, c in spikes:
+            sc.K[0][p_] = W.bf16_round(c * u)
+            scn.fill_paged(sc.kv, 0, p_, sc.K[0][p_:p_ + 1], sc.V[0][p_:p_ + 1])
+        sc.append_proposed()
+        L = S + n_q
+        o, l = lib.verify_attn(dev_bf16(q), sc.kv.k, sc.kv.v, sc.kv.block_table, dev_i32([L]), L,
+                               num_splits=1)
+        torch().cuda.synchronize()
+        ro, rl = OA.verify(q[0], sc.K[0], sc.V[0], L, 1.0)
+        compare(o[0], l[0], ro, rl, "verify logit jump")
+        return
+    sc = DraftScenario(cfg, 42, [S], 1)
+    qf = 0.25 * W.bf16_to_f32(sc.q(1)) + np.repeat(u, G, axis=0)[None]
+    q = W.bf16_round(qf)
+    from long_context_decode_attention_amd import scenario as scn
+    for p_, c in spikes:
+        sc.K[0][p_] = W.bf16_round(c * u)
+        scn.fill_paged(sc.kv, 0, p_, sc.K[0][p_:p_ + 1], sc.V[0][p_:p_ + 1])
+    sc.ring = lib.new_ring(1, cfg["C"], Hkv, D, cfg["n_sink"], cfg["n_recent"])
+    scn.fill_ring(sc.ring, 0, sc.K[0][:S], sc.V[0][:S])
+    sc.append(1)
+    L = S + 1
+    if call == "full":
+        o, l = lib.draft_attn_full(dev_bf16(q), sc.kv.k, sc.kv.v, sc.kv.block_table, dev_i32([L]), L,
+                                   num_splits=1)
+        ro, rl = OA.draft_full(q[0], sc.K[0], sc.V[0], L, 1.0)
+    else:
+        o, l = lib.draft_attn_window(dev_bf16(q), sc.ring, num_splits=1)
+        ro, rl = OA.draft_window(q[0], sc.K[0], sc.V[0], L, cfg["n_sink"], cfg["n_recent"], 1.0)
+    torch().cuda.synchronize()
+    compare(o[0], l[0], ro, rl, f"{call} logit jump")
+
+
 # ------------------------------------------------------------------ split structure
 
 @pytest.mark.parametrize("num_splits", [1, 2, 7, 64])
@@ -317,16 +373,18 @@ def test_verify_single_query_equals_draft_full():
 
 def _unpack_k(kc, D):
     """Tiled K cache -> [page, Hkv, 64, D] bit patterns (layout of include/wmtp.h)."""
-    a = kc.view(torch().int16).cpu().numpy().view(np.uint16)     # [P, Hkv, 2, D/32, 32, 32]
+    a = kc.view(torch().int16).cpu().numpy().view(np.uint16)
     P, Hkv = a.shape[:2]
-    a = a.transpose(0, 1, 2, 4, 3, 5)                              # [P, Hkv, half, pos, dtile, 32]
+    a = a.reshape(P, Hkv, 2, D // 16, 32, 16)                      # [P, Hkv, half, dblock, pos, 16]
+    a = a.transpose(0, 1, 2, 4, 3, 5)                              # [P, Hkv, half, pos, dblock, 16]
     return a.reshape(P, Hkv, 64, D)
 
 
 def _unpack_v(vc, D):
-    a = vc.view(torch().int16).cpu().numpy().view(np.uint16)     # [P, Hkv, 2, D, 32]
+    a = vc.view(torch().int16).cpu().numpy().view(np.uint16)
     P, Hkv = a.shape[:2]
-    a = a.transpose(0, 1, 2, 4, 3)                                 # [P, Hkv, half, pos, D]
+    a = a.reshape(P, Hkv, 2, 2, D, 16)                             # [P, Hkv, half, kstep, D, 16]
+    a = a.transpose(0, 1, 2, 3, 5, 4)                              # [P, Hkv, half, kstep, 16, D]
     return a.reshape(P, Hkv, 64, D)
 
 
