@@ -27,7 +27,7 @@ namespace wmtp {
 
 namespace {
 
-constexpr int kStages = 4;      // LDS tile stages: tiles t, t+1 resident, t+2, t+3 in flight
+constexpr int kSlots = 5;       // LDS slots per ring (K, V): one resident, four in flight
 constexpr int kPageRegs = 4;   // page ids preloaded per split: 64 per register
 
 // Wait until at most N vector-memory operations of this wave are outstanding.
@@ -99,7 +99,7 @@ __device__ __forceinline__ void pv_tile(SoftmaxState<D, RBW>& st, const float (&
     for (int db = 0; db < DH; ++db)
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
-        vop[db][kk] = *reinterpret_cast<const bf16x8*>(base + (KS + 2 * (d0 + db) + kk) * 1024);
+        vop[db][kk] = *reinterpret_cast<const bf16x8*>(base + (2 * (d0 + db) + kk) * 1024);
     if (mask_v) {
 #pragma unroll
       for (int db = 0; db < DH; ++db)
@@ -126,16 +126,137 @@ __device__ __forceinline__ void pv_tile(SoftmaxState<D, RBW>& st, const float (&
   }
 }
 
+// Scheduling anchors: an empty volatile asm that "redefines" a register.  The
+// volatile statements keep their relative order, so a value produced before one
+// anchor and consumed after the next cannot move across either; this is how the
+// fast tile below keeps its interleaved issue order.
+template <typename T>
+__device__ __forceinline__ void anchor(T& v) { asm volatile("" : "+v"(v)); }
+
+// One tile of the fast loop, as one branch-free block: S(t+1) into s_acc from the
+// LDS stage at kbase, the weights of tile t from its scores x, and PV(t) from the
+// stage at vbase.  Every key of tile t is present and visible to every row, and
+// no rescale is due.  Step ks issues the S^T MFMA(s) of head-dim step ks and
+// then the softmax work of 256/D of tile t's scores per row block, which the
+// VALU executes while the matrix core runs the MFMA; anchors at every step keep
+// that order.  K operand reads run four steps ahead of their MFMAs and the V
+// operand reads are spread over the same steps, so PV(t) finds them in
+// registers.  dma(i), i < NLOAD, issues the wave's i-th global-to-LDS load of
+// the refill for later tiles; all of them go out between the last V operand
+// read and the PV MFMAs.
+template <int D, int RBW, int NLOAD, typename Dma>
+__device__ __forceinline__ void fast_tile(SoftmaxState<D, RBW>& st, f32x16 (&s_acc)[RBW],
+                                          const bf16x8 (&qop)[RBW][D / 16],
+                                          float (&x)[RBW][16], float c,
+                                          const unsigned char* kbase, const unsigned char* vbase,
+                                          Dma&& dma) {
+  constexpr int KS = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int kAhead = KS < 4 ? KS : 4;
+  constexpr int E = 256 / D;                   // scores per row block handled per step
+  static_assert(E * KS == 16, "scores per step");
+
+  float neg_m[RBW], p[RBW][16], psum[RBW];
+#pragma unroll
+  for (int rb = 0; rb < RBW; ++rb) {
+    neg_m[rb] = -st.m[rb];                     // finite: every row has seen a full tile
+    psum[rb] = 0.f;
+  }
+  uint32_t hw[RBW][8], lw[RBW][8];             // packed P^T words: key pair w of row block
+  bf16x8 kop[KS];
+  bf16x8 vop[KS];                              // V operand (db, kk) at index 2 * db + kk
+#pragma unroll
+  for (int ks = 0; ks < kAhead; ++ks) kop[ks] = *reinterpret_cast<const bf16x8*>(kbase + ks * 1024);
+#pragma unroll
+  for (int rb = 0; rb < RBW; ++rb) s_acc[rb] = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    // step boundary: the previous step's results and this step's inputs
+    anchor(kop[ks]);
+    if (ks >= kAhead) anchor(vop[ks - kAhead]);
+#pragma unroll
+    for (int rb = 0; rb < RBW; ++rb) {
+      anchor(psum[rb]);
+#pragma unroll
+      for (int j = 0; j < E; ++j) anchor(x[rb][ks * E + j]);
+      if (ks > 0 && (E > 1 || (ks & 1) == 0)) {
+        // pairs completed by the previous step
+#pragma unroll
+        for (int j = 0; j < (E + 1) / 2; ++j) {
+          const int w = ((ks - 1) * E) / 2 + j;
+          anchor(hw[rb][w]);
+          anchor(lw[rb][w]);
+        }
+      }
+    }
+    if (ks + kAhead < KS)
+      kop[ks + kAhead] = *reinterpret_cast<const bf16x8*>(kbase + (ks + kAhead) * 1024);
+    vop[ks] = *reinterpret_cast<const bf16x8*>(vbase + ks * 1024);
+#pragma unroll
+    for (int rb = 0; rb < RBW; ++rb) s_acc[rb] = mfma32x32x16(kop[ks], qop[rb][ks], s_acc[rb]);
+#pragma unroll
+    for (int rb = 0; rb < RBW; ++rb) {
+#pragma unroll
+      for (int j = 0; j < E; ++j) {
+        const int i = ks * E + j;
+        p[rb][i] = fast_exp2(fmaf(x[rb][i], c, neg_m[rb]));
+        psum[rb] += p[rb][i];
+        if (i & 1) {
+          const uint32_t hp = pack_bf16x2(p[rb][i - 1], p[rb][i]);
+          hw[rb][i >> 1] = hp;
+          lw[rb][i >> 1] = pack_bf16x2(p[rb][i - 1] - __builtin_bit_cast(float, hp << 16),
+                                       p[rb][i] - __builtin_bit_cast(float, hp & 0xFFFF0000u));
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int ks = KS - kAhead; ks < KS; ++ks) anchor(vop[ks]);
+  // The refill loads go here, where this wave has no LDS read in flight: a
+  // global-to-LDS load waits for the wave's outstanding LDS reads before it
+  // issues, which costs little only at this point.
+#pragma unroll
+  for (int i = 0; i < NLOAD; ++i) dma(i);
+  bf16x8 p_hi[RBW][2], p_lo[RBW][2];
+#pragma unroll
+  for (int rb = 0; rb < RBW; ++rb) {
+    st.l[rb] += psum[rb];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      p_hi[rb][kk] = __builtin_bit_cast(bf16x8, u32x4{hw[rb][4 * kk], hw[rb][4 * kk + 1],
+                                                      hw[rb][4 * kk + 2], hw[rb][4 * kk + 3]});
+      p_lo[rb][kk] = __builtin_bit_cast(bf16x8, u32x4{lw[rb][4 * kk], lw[rb][4 * kk + 1],
+                                                      lw[rb][4 * kk + 2], lw[rb][4 * kk + 3]});
+    }
+  }
+  // PV(t): the hi products of every accumulator, then the lo products, so that
+  // no MFMA waits on the one just before it.
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int rb = 0; rb < RBW; ++rb)
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        st.acc[rb][db] = mfma32x32x16(vop[2 * db + kk], p_hi[rb][kk], st.acc[rb][db]);
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int rb = 0; rb < RBW; ++rb)
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        st.acc[rb][db] = mfma32x32x16(vop[2 * db + kk], p_lo[rb][kk], st.acc[rb][db]);
+}
+
 template <int D, int RBW, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  constexpr int NOPS = 2 * KS;           // 1 KB operands per tile: D/16 of K, D/16 of V^T
-  constexpr int NL = NOPS / NW;          // wave loads per tile per wave
-  constexpr int STAGE = NOPS * 1024;     // bytes per stage
-  static_assert(NOPS % NW == 0, "operands split evenly over the waves");
+  constexpr int HALF = KS * 1024;        // bytes of a K (or V) half of a tile: KS 1 KB operands
+  constexpr int NH = KS / NW;            // wave loads per half tile
+  static_assert(KS % NW == 0, "operands split evenly over the waves");
 
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[kStages * STAGE];
+  // K ring then V ring, kSlots half tiles each (160 KB at D = 256).
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kSlots * HALF];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -215,75 +336,97 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
   }
   wait_vmcnt<0>();
 
-  // Issue the NL wave loads of tile kb into stage `stage`.  A page id outside
-  // the cache still issues its loads (from page 0) so that every tile costs the
-  // same number of outstanding loads; the tile is then skipped.
-  auto issue = [&](int kb, int stage) -> bool {
+  // Half tiles stream through two rings of LDS slots, K and V, filled by
+  // direct global-to-LDS loads: the K half of tile u goes to K slot u % kSlots,
+  // its V half to V slot u % kSlots.  Step t reads K(t+1) (for S(t+1)) and V(t)
+  // (for PV(t)), so each ring has one resident half and four in flight: after
+  // the barrier of step t, K(t+5) refills the slot K(t) left and V(t+4) the slot
+  // V(t-1) left.  A page id outside the cache still issues its loads (from page
+  // 0) so that every half costs the same number of loads; the tile is skipped.
+  uint32_t ok_tile = 0;                 // bit u % 8: tile u has a valid page
+  auto page_of = [&](int u, bool& ok) -> size_t {
+    const int kb = kb0 + u;
     const int idx = (kb >> 1) - page0;   // 0 .. 64*kPageRegs - 1, wave-uniform
     int ppage = -1;
 #pragma unroll
     for (int r = 0; r < kPageRegs; ++r)
       if ((idx >> 6) == r) ppage = __builtin_amdgcn_readlane(my_page[r], idx & 63);
-    const bool ok = (unsigned)ppage < (unsigned)a.num_pages;
+    ok = (unsigned)ppage < (unsigned)a.num_pages;
     if (!ok) ppage = 0;
-    const size_t tile = ((size_t)ppage * a.Hkv + g) * 2 + (kb & 1);
-    const uint16_t* kt = a.kc + tile * (size_t)(32 * D);
-    const uint16_t* vt = a.vc + tile * (size_t)(32 * D);
-    unsigned char* base = smem + stage * STAGE;
+    return ((size_t)ppage * a.Hkv + g) * 2 + (kb & 1);
+  };
+  auto k_slot = [&](int u) { return smem + (u % kSlots) * HALF; };
+  auto v_slot = [&](int u) { return smem + (kSlots + u % kSlots) * HALF; };
+  auto issue_k = [&](int u) {
+    bool ok;
+    const uint16_t* kt = a.kc + page_of(u, ok) * (size_t)(32 * D);
+    ok_tile = (ok_tile & ~(1u << (u & 7))) | ((ok ? 1u : 0u) << (u & 7));
+    unsigned char* base = k_slot(u);
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
+    for (int i = 0; i < NH; ++i) {
       const int op = wave + NW * i;
-      const uint16_t* src;
-      if (op < KS) {
-        src = kt + k_operand_offset(op, m, h);
-      } else {
-        const int vo = op - KS;
-        src = vt + v_operand_offset<D>(vo >> 1, vo & 1, m, h);
-      }
       // cache policy 2 = non-temporal (the tile is read from HBM once)
-      __builtin_amdgcn_global_load_lds(
-          (void*)src, (__attribute__((address_space(3))) void*)(base + op * 1024), 16, 0, 2);
+      __builtin_amdgcn_global_load_lds((void*)(kt + k_operand_offset(op, m, h)),
+                                       (__attribute__((address_space(3))) void*)(base + op * 1024),
+                                       16, 0, 2);
     }
-    return ok;
+  };
+  auto issue_v = [&](int u) {
+    bool ok;
+    const uint16_t* vt = a.vc + page_of(u, ok) * (size_t)(32 * D);
+    unsigned char* base = v_slot(u);
+#pragma unroll
+    for (int i = 0; i < NH; ++i) {
+      const int op = wave + NW * i;   // V operand (op / 2, op % 2)
+      __builtin_amdgcn_global_load_lds((void*)(vt + v_operand_offset<D>(op >> 1, op & 1, m, h)),
+                                       (__attribute__((address_space(3))) void*)(base + op * 1024),
+                                       16, 0, 2);
+    }
   };
 
-  // Pipeline: issue tiles 0..2, publish tile 0, issue S(0); step t then publishes
-  // tile t+1, issues tile t+3, issues S(t+1) and finishes tile t.
-  uint32_t ok_stage = 0;               // bit s: the tile in stage s has a valid page
+  // Prologue: K(0..4) and V(0..3) in the order the steps would have issued them,
+  // publish K(0), issue S(0).
 #pragma unroll
-  for (int i = 0; i < 3; ++i)
-    if (i < ntile && issue(kb0 + i, i)) ok_stage |= 1u << i;
-  f32x16 s_cur[RBW], s_next[RBW];
+  for (int u = 0; u < kSlots; ++u) {
+    if (u < ntile) issue_k(u);
+    if (u >= 1 && u - 1 < ntile) issue_v(u - 1);
+  }
+  f32x16 s_acc[RBW];
   if (ntile > 0) {
-    if (ntile >= 3) {
-      wait_vmcnt<2 * NL>();
-    } else if (ntile == 2) {
-      wait_vmcnt<NL>();
+    if (ntile >= kSlots) {
+      wait_vmcnt<(kSlots - 1) * 2 * NH>();   // K(1..4), V(0..3) may still be in flight
     } else {
       wait_vmcnt<0>();
     }
     lds_barrier();
-    if (any_row) s_tile<D, RBW>(s_cur, qop, smem + lane * 16);
+    if (any_row) s_tile<D, RBW>(s_acc, qop, k_slot(0) + lane * 16);
   }
 
-  // Publish tile t+1, refill the stage of tile t-1 with tile t+3, issue S(t+1).
-  auto advance = [&](int t) {
-    // Tile t+1 has landed once only the loads of tile t+2 (if issued) remain.
-    if (t + 2 < ntile) {
-      wait_vmcnt<NL>();
+  // Publish K(t+1) and V(t); then refill the freed slots (issue_for).
+  auto publish = [&](int t) {
+    // Issued after K(t+1), V(t): K(t+2..t+4) and V(t+1..t+3), all present
+    // unless the split ends within the next few tiles.
+    if (t + kSlots - 1 < ntile) {
+      wait_vmcnt<(kSlots - 2) * 2 * NH>();
     } else {
       wait_vmcnt<0>();
     }
     lds_barrier();
-    if (t + 3 < ntile) {
-      const int st3 = (t + 3) % kStages;
-      ok_stage = (ok_stage & ~(1u << st3)) | ((issue(kb0 + t + 3, st3) ? 1u : 0u) << st3);
-    }
-    if (any_row && t + 1 < ntile)
-      s_tile<D, RBW>(s_next, qop, smem + ((t + 1) % kStages) * STAGE + lane * 16);
+  };
+  auto issue_for = [&](int t) {
+    if (t + kSlots < ntile) issue_k(t + kSlots);
+    if (t + kSlots - 1 < ntile) issue_v(t + kSlots - 1);
+  };
+  auto sync_stage = [&](int t) {
+    publish(t);
+    issue_for(t);
+  };
+  auto next_scores = [&](int t) {
+    if (any_row && t + 1 < ntile) s_tile<D, RBW>(s_acc, qop, k_slot(t + 1) + lane * 16);
   };
 
-  // Masked scores of tile t (from s_cur) and the facts its PV needs.
+  // Masked scores of tile t (from s_acc, which then is free) and the facts its
+  // PV needs.
   float x[RBW][16], mx[RBW];
   uint32_t keep = 0;
   bool mask_v = false;
@@ -295,41 +438,92 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
     keep = keys_below(L - kb * 32, h);
     mask_v = (kb + 1) * 32 > L;
 #pragma unroll
-    for (int rb = 0; rb < RBW; ++rb)
-      mx[rb] = masked_scores(x[rb], s_cur[rb], keys_below(lim[rb] - kb * 32, h), all_vis,
+    for (int rb = 0; rb < RBW; ++rb) {
+      mx[rb] = masked_scores(x[rb], s_acc[rb], keys_below(lim[rb] - kb * 32, h), all_vis,
                              a.scale_log2);
-  };
-  auto tile_ok = [&](int t) { return any_row && ((ok_stage >> (t % kStages)) & 1u); };
-  auto stage_base = [&](int t) { return smem + (t % kStages) * STAGE + lane * 16; };
-
-  // Fast loop: no accumulator rescale.  Leaves with t < ntile when tile t needs
-  // one; its scores are then already in x / mx.
-  int t = 0;
-  for (; t < ntile; ++t) {
-    advance(t);
-    if (tile_ok(t)) {
-      scores_of(t);
-      if (first_max_or_rescale<D, RBW>(st, mx)) break;
-      pv_tile<D, RBW>(st, x, a.scale_log2, stage_base(t), keep, mask_v);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(x[rb][i]));
     }
+  };
+  auto tile_ok = [&](int t) { return any_row && ((ok_tile >> (t & 7)) & 1u); };
+
+  // Fast loop over tiles that have a successor, are full (every key present and
+  // visible to every row) and need no rescale: one branch-free block per tile.
+  // Any other tile hands over to the general loop below, which finishes the
+  // split; s_acc holds S(t) at the hand-over either way.
+  int t = 0;
+  bool synced = false;   // the general loop's first tile is published, its refill not issued
+  if (any_row) {
+    // The fast loop also spreads step t's refill, K(t+5) and V(t+4), over the
+    // tile's MFMA steps: it runs while both exist.
+    for (; t + kSlots < ntile; ++t) {
+      publish(t);
+      const int kb = kb0 + t;
+      if (!tile_ok(t) || (kb + 1) * 32 > L - a.n_q + 1) {
+        synced = true;
+        break;
+      }
+      bool rescale = false;
+      float row_mx[RBW];
 #pragma unroll
-    for (int rb = 0; rb < RBW; ++rb) s_cur[rb] = s_next[rb];
-  }
-  // General loop, from the tile the fast loop left on.
-  if (t < ntile) {
-    raise_and_rescale<D, RBW>(st, mx);
-    pv_tile<D, RBW>(st, x, a.scale_log2, stage_base(t), keep, mask_v);
+      for (int rb = 0; rb < RBW; ++rb) {
 #pragma unroll
-    for (int rb = 0; rb < RBW; ++rb) s_cur[rb] = s_next[rb];
-    for (++t; t < ntile; ++t) {
-      advance(t);
-      if (tile_ok(t)) {
-        scores_of(t);
-        raise_and_rescale<D, RBW>(st, mx);
-        pv_tile<D, RBW>(st, x, a.scale_log2, stage_base(t), keep, mask_v);
+        for (int i = 0; i < 16; ++i) x[rb][i] = s_acc[rb][i];
+        mx[rb] = lane_max16(x[rb]) * a.scale_log2;
+        row_mx[rb] = max_over_row(mx[rb]);
+        rescale |= st.m[rb] != -INFINITY && needs_raise(mx[rb], st.m[rb]);
+      }
+      if (__any(rescale)) {
+        synced = true;
+        break;
       }
 #pragma unroll
-      for (int rb = 0; rb < RBW; ++rb) s_cur[rb] = s_next[rb];
+      for (int rb = 0; rb < RBW; ++rb) st.m[rb] = st.m[rb] == -INFINITY ? row_mx[rb] : st.m[rb];
+      bool ok_k, ok_v;
+      const uint16_t* kt = a.kc + page_of(t + kSlots, ok_k) * (size_t)(32 * D);
+      const uint16_t* vt = a.vc + page_of(t + kSlots - 1, ok_v) * (size_t)(32 * D);
+      {
+        const int u = t + kSlots;
+        ok_tile = (ok_tile & ~(1u << (u & 7))) | ((ok_k ? 1u : 0u) << (u & 7));
+      }
+      unsigned char* kdst = k_slot(t + kSlots);
+      unsigned char* vdst = v_slot(t + kSlots - 1);
+      auto dma = [&](int i) {
+        if (i < NH) {
+          const int op = wave + NW * i;
+          __builtin_amdgcn_global_load_lds(
+              (void*)(kt + k_operand_offset(op, m, h)),
+              (__attribute__((address_space(3))) void*)(kdst + op * 1024), 16, 0, 2);
+        } else {
+          const int op = wave + NW * (i - NH);
+          __builtin_amdgcn_global_load_lds(
+              (void*)(vt + v_operand_offset<D>(op >> 1, op & 1, m, h)),
+              (__attribute__((address_space(3))) void*)(vdst + op * 1024), 16, 0, 2);
+        }
+      };
+      fast_tile<D, RBW, 2 * NH>(st, s_acc, qop, x, a.scale_log2, k_slot(t + 1) + lane * 16,
+                                v_slot(t) + lane * 16, dma);
+#pragma unroll
+      for (int rb = 0; rb < RBW; ++rb)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) pin_acc(st.acc[rb][db]);
+    }
+  }
+  // General loop: masking, rescales, the split's last tile, and waves that own
+  // no row (which only take part in the stage pipeline).
+  for (; t < ntile; ++t) {
+    if (synced) {
+      issue_for(t);
+    } else {
+      sync_stage(t);
+    }
+    synced = false;
+    const bool ok_t = tile_ok(t);
+    if (ok_t) scores_of(t);
+    next_scores(t);
+    if (ok_t) {
+      raise_and_rescale<D, RBW>(st, mx);
+      pv_tile<D, RBW>(st, x, a.scale_log2, v_slot(t) + lane * 16, keep, mask_v);
     }
   }
 
