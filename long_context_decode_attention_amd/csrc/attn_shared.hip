@@ -447,77 +447,71 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
   };
   auto tile_ok = [&](int t) { return any_row && ((ok_tile >> (t & 7)) & 1u); };
 
-  // Fast loop over tiles that have a successor, are full (every key present and
-  // visible to every row) and need no rescale: one branch-free block per tile.
-  // Any other tile hands over to the general loop below, which finishes the
-  // split; s_acc holds S(t) at the hand-over either way.
+  // Tiles run through a fast path or a general one.  The fast path takes a tile
+  // that is full (every key present and visible to every row), whose rows all
+  // have a running maximum that no score of the tile exceeds by more than the
+  // lazy margin, and whose refill, K(t+5) and V(t+4), exists: one branch-free
+  // block, no cross-lane work.  Any other tile (a split's first and last
+  // tiles, the causal boundary, bad pages, a rescale) takes the general path,
+  // and the fast path resumes after it.  Waves that own no row take only part
+  // in the stage pipeline.  s_acc holds S(t) when tile t starts either way.
   int t = 0;
-  bool synced = false;   // the general loop's first tile is published, its refill not issued
-  if (any_row) {
-    // The fast loop also spreads step t's refill, K(t+5) and V(t+4), over the
-    // tile's MFMA steps: it runs while both exist.
-    for (; t + kSlots < ntile; ++t) {
-      publish(t);
-      const int kb = kb0 + t;
-      if (!tile_ok(t) || (kb + 1) * 32 > L - a.n_q + 1) {
-        synced = true;
-        break;
-      }
-      bool rescale = false;
-      float row_mx[RBW];
+  while (t < ntile) {
+    bool synced = false;   // tile t is published, its refill not yet issued
+    if (any_row) {
+      for (; t + kSlots < ntile; ++t) {
+        publish(t);
+        const int kb = kb0 + t;
+        bool slow = !tile_ok(t) || (kb + 1) * 32 > L - a.n_q + 1;
 #pragma unroll
-      for (int rb = 0; rb < RBW; ++rb) {
+        for (int rb = 0; rb < RBW; ++rb) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) x[rb][i] = s_acc[rb][i];
-        mx[rb] = lane_max16(x[rb]) * a.scale_log2;
-        row_mx[rb] = max_over_row(mx[rb]);
-        rescale |= st.m[rb] != -INFINITY && needs_raise(mx[rb], st.m[rb]);
-      }
-      if (__any(rescale)) {
-        synced = true;
-        break;
-      }
-#pragma unroll
-      for (int rb = 0; rb < RBW; ++rb) st.m[rb] = st.m[rb] == -INFINITY ? row_mx[rb] : st.m[rb];
-      bool ok_k, ok_v;
-      const uint16_t* kt = a.kc + page_of(t + kSlots, ok_k) * (size_t)(32 * D);
-      const uint16_t* vt = a.vc + page_of(t + kSlots - 1, ok_v) * (size_t)(32 * D);
-      {
-        const int u = t + kSlots;
-        ok_tile = (ok_tile & ~(1u << (u & 7))) | ((ok_k ? 1u : 0u) << (u & 7));
-      }
-      unsigned char* kdst = k_slot(t + kSlots);
-      unsigned char* vdst = v_slot(t + kSlots - 1);
-      auto dma = [&](int i) {
-        if (i < NH) {
-          const int op = wave + NW * i;
-          __builtin_amdgcn_global_load_lds(
-              (void*)(kt + k_operand_offset(op, m, h)),
-              (__attribute__((address_space(3))) void*)(kdst + op * 1024), 16, 0, 2);
-        } else {
-          const int op = wave + NW * (i - NH);
-          __builtin_amdgcn_global_load_lds(
-              (void*)(vt + v_operand_offset<D>(op >> 1, op & 1, m, h)),
-              (__attribute__((address_space(3))) void*)(vdst + op * 1024), 16, 0, 2);
+          for (int i = 0; i < 16; ++i) x[rb][i] = s_acc[rb][i];
+          mx[rb] = lane_max16(x[rb]) * a.scale_log2;
+          // m = -inf (no maximum yet) needs a raise as well
+          slow |= needs_raise(mx[rb], st.m[rb]);
         }
-      };
-      fast_tile<D, RBW, 2 * NH>(st, s_acc, qop, x, a.scale_log2, k_slot(t + 1) + lane * 16,
-                                v_slot(t) + lane * 16, dma);
+        if (__any(slow)) {
+          synced = true;
+          break;
+        }
+        bool ok_k, ok_v;
+        const uint16_t* kt = a.kc + page_of(t + kSlots, ok_k) * (size_t)(32 * D);
+        const uint16_t* vt = a.vc + page_of(t + kSlots - 1, ok_v) * (size_t)(32 * D);
+        {
+          const int u = t + kSlots;
+          ok_tile = (ok_tile & ~(1u << (u & 7))) | ((ok_k ? 1u : 0u) << (u & 7));
+        }
+        unsigned char* kdst = k_slot(t + kSlots);
+        unsigned char* vdst = v_slot(t + kSlots - 1);
+        auto dma = [&](int i) {
+          if (i < NH) {
+            const int op = wave + NW * i;
+            __builtin_amdgcn_global_load_lds(
+                (void*)(kt + k_operand_offset(op, m, h)),
+                (__attribute__((address_space(3))) void*)(kdst + op * 1024), 16, 0, 2);
+          } else {
+            const int op = wave + NW * (i - NH);
+            __builtin_amdgcn_global_load_lds(
+                (void*)(vt + v_operand_offset<D>(op >> 1, op & 1, m, h)),
+                (__attribute__((address_space(3))) void*)(vdst + op * 1024), 16, 0, 2);
+          }
+        };
+        fast_tile<D, RBW, 2 * NH>(st, s_acc, qop, x, a.scale_log2, k_slot(t + 1) + lane * 16,
+                                  v_slot(t) + lane * 16, dma);
 #pragma unroll
-      for (int rb = 0; rb < RBW; ++rb)
+        for (int rb = 0; rb < RBW; ++rb)
 #pragma unroll
-        for (int db = 0; db < DB; ++db) pin_acc(st.acc[rb][db]);
+          for (int db = 0; db < DB; ++db) pin_acc(st.acc[rb][db]);
+      }
     }
-  }
-  // General loop: masking, rescales, the split's last tile, and waves that own
-  // no row (which only take part in the stage pipeline).
-  for (; t < ntile; ++t) {
+    if (t >= ntile) break;
+    // general path for tile t
     if (synced) {
       issue_for(t);
     } else {
       sync_stage(t);
     }
-    synced = false;
     const bool ok_t = tile_ok(t);
     if (ok_t) scores_of(t);
     next_scores(t);
@@ -525,6 +519,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
       raise_and_rescale<D, RBW>(st, mx);
       pv_tile<D, RBW>(st, x, a.scale_log2, v_slot(t) + lane * 16, keep, mask_v);
     }
+    ++t;
   }
 
   // Each wave writes its own rows.
