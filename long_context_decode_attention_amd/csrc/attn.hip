@@ -20,10 +20,12 @@
 
 #include <type_traits>
 
-// Workgroups the split planner aims at: two per CU for the split-keys kernel
-// (one resident at a time), one per CU for the shared kernel.
+// Workgroups the split planner aims at: one per CU for both kernels, so that a
+// long sequence runs in a single round (measured at 1M keys: 256 workgroups
+// stream at 6.85 TB/s against 6.55 TB/s for 512, whose second round adds a
+// workgroup prologue, a merge and a tail).
 #ifndef WMTP_TARGET_WG_SPLIT
-#define WMTP_TARGET_WG_SPLIT 512
+#define WMTP_TARGET_WG_SPLIT 256
 #endif
 #ifndef WMTP_TARGET_WG_SHARED
 #define WMTP_TARGET_WG_SHARED 256
@@ -58,6 +60,20 @@ __device__ __forceinline__ size_t tile_index(const AttnArgs& a, int b, int g, in
   }
   ok = (unsigned)ppage < (unsigned)a.num_pages;
   if (!ok) ppage = 0;   // still loaded (so that every load is unconditional), then ignored
+  return ((size_t)ppage * a.Hkv + g) * 2 + (kb & 1);
+}
+
+// First 32-key tile of the split of workgroup item `item`.
+__device__ __forceinline__ int kb0_of(const AttnArgs& a, int item) {
+  return (item % a.nsplit) * a.kb_per_split;
+}
+
+// Tile index of tile kb of kv head g on physical page `ppage` (paged caches), with
+// the same bad-page rule as tile_index.
+__device__ __forceinline__ size_t tile_of_page(const AttnArgs& a, int ppage, int g, int kb,
+                                               bool& ok) {
+  ok = (unsigned)ppage < (unsigned)a.num_pages;
+  if (!ok) ppage = 0;
   return ((size_t)ppage * a.Hkv + g) * 2 + (kb & 1);
 }
 
@@ -139,38 +155,76 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
   const int b = bg / a.Hkv;
   const int row0 = rg * 32 * NB;
 
-  int L, T = 0;
-  if (RING) {
-    L = a.C;
-    const int64_t t64 = a.ring_T[b];
-    T = t64 < 0 ? 0 : (t64 > (int64_t)INT_MAX ? INT_MAX : (int)t64);
-  } else {
-    const int l = a.seq_lens[b];
-    L = l < 0 ? 0 : (l > a.max_keys ? a.max_keys : l);
-  }
-  const int nkb = (L + 31) >> 5;
-  const int kb0 = s * a.kb_per_split;
-  const int kb1 = min(kb0 + a.kb_per_split, nkb);
 
   // Q^T operands, staged once in LDS in MFMA lane order (sm_q[rb][ks][lane]:
   // row row0 + 32*rb + m, dims 16*ks + 8*h .. +7) and read back per tile; in
-  // registers they would push the tile buffers into scratch at D = 256.
+  // registers they would push the tile buffers into scratch at D = 256.  The Q
+  // loads go out first, then the wave's first tile, and only then are the Q
+  // values stored and published, so that the two memory latencies overlap.
   __shared__ bf16x8 sm_q[NB][KS][64];
-  for (int idx = threadIdx.x; idx < NB * KS * 64; idx += 256) {
+  constexpr int kQPer = NB * KS * 64 / 256;   // Q operands per thread
+  static_assert(kQPer * 256 == NB * KS * 64, "Q operands split evenly over the threads");
+  // The sequence length and the wave's first page id are read first: the tile
+  // loads depend on them.
+  const int len_raw = RING ? 0 : a.seq_lens[b];
+  const int64_t t64 = RING ? a.ring_T[b] : 0;
+  const int kb_first = kb0_of(a, item) + wave;
+  const int page_first =
+      RING ? 0 : a.block_table[(size_t)b * a.max_pages + min(kb_first >> 1, a.max_pages - 1)];
+  bf16x8 qv[kQPer];
+  bool qok[kQPer];
+#pragma unroll
+  for (int r = 0; r < kQPer; ++r) {
+    const int idx = threadIdx.x + 256 * r;
     const int ln = idx & 63;
     const int ks = (idx >> 6) % KS;
     const int rb = idx / (64 * KS);
     const int row = row0 + rb * 32 + (ln & 31);
-    bf16x8 v = zero_bf16x8();
-    if (row < a.R) {
-      const int qi = row / a.G;
-      const int hl = row - qi * a.G;
-      v = ld_bf16x8(a.q + ((size_t)(b * a.n_q + qi) * a.Hq + g * a.G + hl) * D + ks * 16 +
-                    (ln >> 5) * 8);
-    }
-    sm_q[rb][ks][ln] = v;
+    qok[r] = row < a.R;
+    const int rr = qok[r] ? row : 0;   // rows past R load row 0, then read as zero
+    const int qi = rr / a.G;
+    const int hl = rr - qi * a.G;
+    qv[r] = ld_bf16x8(a.q + ((size_t)(b * a.n_q + qi) * a.Hq + g * a.G + hl) * D + ks * 16 +
+                      (ln >> 5) * 8);
   }
-  __syncthreads();
+  int L, T = 0;
+  if (RING) {
+    L = a.C;
+    T = t64 < 0 ? 0 : (t64 > (int64_t)INT_MAX ? INT_MAX : (int)t64);
+  } else {
+    L = len_raw < 0 ? 0 : (len_raw > a.max_keys ? a.max_keys : len_raw);
+  }
+  const int nkb = (L + 31) >> 5;
+  const int kb0 = s * a.kb_per_split;
+  const int kb1 = min(kb0 + a.kb_per_split, nkb);
+  asm volatile("" ::: "memory");
+  // Loop over this wave's tiles.  K registers are refilled with the next tile as
+  // soon as the S^T products have consumed them, V registers as soon as the PV
+  // products have: one tile of each is always in flight.  Loads are
+  // unconditional (a tile with a bad page id is loaded from page 0 and then
+  // masked), so the loop carries the tile registers without copies.
+  KTile<D, RING> kt;
+  VTile<D> vt;
+  int kb = kb0 + wave;
+  bool ok = false;
+  {
+    // unconditional (a wave without tiles loads a valid tile it never uses), so
+    // that the Q stores below wait only for the Q loads
+    const int kbl = kb < kb1 ? kb : 0;
+    const size_t tile = RING ? tile_index<RING>(a, b, g, kbl, ok)
+                             : tile_of_page(a, kb < kb1 ? page_first : 0, g, kbl, ok);
+    load_k<D, RING>(kt, a, tile, b, kbl, m, h);
+    load_v<D>(vt, a, tile, m, h);
+  }
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int r = 0; r < kQPer; ++r) {
+    const int idx = threadIdx.x + 256 * r;
+    sm_q[idx / (64 * KS)][(idx >> 6) % KS][idx & 63] = qok[r] ? qv[r] : zero_bf16x8();
+  }
+  // publish the staged Q: wait for this wave's LDS stores only, so the tile
+  // loads stay in flight across the barrier
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   int lim[NB];
 #pragma unroll
   for (int rb = 0; rb < NB; ++rb) {
@@ -187,20 +241,6 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
     for (int db = 0; db < DB; ++db) st.acc[rb][db] = f32x16{};
   }
 
-  // Loop over this wave's tiles.  K registers are refilled with the next tile as
-  // soon as the S^T products have consumed them, V registers as soon as the PV
-  // products have: one tile of each is always in flight.  Loads are
-  // unconditional (a tile with a bad page id is loaded from page 0 and then
-  // masked), so the loop carries the tile registers without copies.
-  KTile<D, RING> kt;
-  VTile<D> vt;
-  int kb = kb0 + wave;
-  bool ok = false;
-  if (kb < kb1) {
-    const size_t tile = tile_index<RING>(a, b, g, kb, ok);
-    load_k<D, RING>(kt, a, tile, b, kb, m, h);
-    load_v<D>(vt, a, tile, m, h);
-  }
   int kbn = kb;
   bool ok_n = false;
   size_t tile_n = 0;
@@ -294,9 +334,13 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
   }
 
   // ---- merge the four waves' states through LDS, one row block at a time ----
+  // Every wave stores its rescaled O^T chunks (chunk u = 4*db + c: dims
+  // 32*db + 8*c + 4*h .. +3 of row m), then wave w sums and writes chunks
+  // [w*U/4, (w+1)*U/4) of all four waves.
+  constexpr int U = DB * 4;
   __shared__ float sm_m[4][32];
   __shared__ float sm_l[4][32];
-  __shared__ f32x4 sm_acc[3][DB][4][64];
+  __shared__ f32x4 sm_acc[4][U][64];
 
 #pragma unroll
   for (int rb = 0; rb < NB; ++rb) {
@@ -315,44 +359,38 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
 #pragma unroll
     for (int w = 0; w < 4; ++w) Ltot += sm_l[w][m] * fast_exp2(sm_m[w][m] - Mu);
     const float f = fast_exp2(st.m[rb] - Mu);
-    if (wave > 0) {
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const f32x4 v = {st.acc[rb][db][4 * c], st.acc[rb][db][4 * c + 1],
-                           st.acc[rb][db][4 * c + 2], st.acc[rb][db][4 * c + 3]};
-          sm_acc[wave - 1][db][c][lane] = v * f;
-        }
-    }
-    __syncthreads();
-    if (wave == 0) {
-      const int row = row0 + rb * 32 + m;
-      if (row < a.R) {
-        const float inv = Ltot > 0.f ? 1.f / Ltot : 0.f;
-        float* op;
-        float* lp;
-        if (a.direct) {
-          const int qi = row / a.G;
-          const int hl = row - qi * a.G;
-          const size_t oidx = (size_t)(b * a.n_q + qi) * a.Hq + g * a.G + hl;
-          op = a.out_o + oidx * D;
-          lp = a.out_lse ? a.out_lse + oidx : nullptr;
-        } else {
-          op = a.out_o + ((size_t)item * a.R + row) * D;
-          lp = a.out_lse + (size_t)item * a.R + row;
-        }
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            f32x4 v = {st.acc[rb][db][4 * c], st.acc[rb][db][4 * c + 1],
-                       st.acc[rb][db][4 * c + 2], st.acc[rb][db][4 * c + 3]};
-            v = v * f + sm_acc[0][db][c][lane] + sm_acc[1][db][c][lane] + sm_acc[2][db][c][lane];
-            *reinterpret_cast<f32x4*>(op + db * 32 + 8 * c + 4 * h) = v * inv;
-          }
-        if (h == 0 && lp) *lp = Ltot > 0.f ? (M + fast_log2(Ltot)) * kLn2 : -INFINITY;
+      for (int c = 0; c < 4; ++c) {
+        const f32x4 v = {st.acc[rb][db][4 * c], st.acc[rb][db][4 * c + 1],
+                         st.acc[rb][db][4 * c + 2], st.acc[rb][db][4 * c + 3]};
+        sm_acc[wave][4 * db + c][lane] = v * f;
       }
+    __syncthreads();
+    const int row = row0 + rb * 32 + m;
+    if (row < a.R) {
+      const float inv = Ltot > 0.f ? 1.f / Ltot : 0.f;
+      float* op;
+      float* lp;
+      if (a.direct) {
+        const int qi = row / a.G;
+        const int hl = row - qi * a.G;
+        const size_t oidx = (size_t)(b * a.n_q + qi) * a.Hq + g * a.G + hl;
+        op = a.out_o + oidx * D;
+        lp = a.out_lse ? a.out_lse + oidx : nullptr;
+      } else {
+        op = a.out_o + ((size_t)item * a.R + row) * D;
+        lp = a.out_lse + (size_t)item * a.R + row;
+      }
+#pragma unroll
+      for (int j = 0; j < U / 4; ++j) {
+        const int u = wave * (U / 4) + j;
+        const f32x4 v = sm_acc[0][u][lane] + sm_acc[1][u][lane] + sm_acc[2][u][lane] +
+                        sm_acc[3][u][lane];
+        *reinterpret_cast<f32x4*>(op + (u >> 2) * 32 + 8 * (u & 3) + 4 * h) = v * inv;
+      }
+      if (wave == 0 && h == 0 && lp) *lp = Ltot > 0.f ? (M + fast_log2(Ltot)) * kLn2 : -INFINITY;
     }
   }
 }
