@@ -1,13 +1,18 @@
 // Log-sum-exp merge of per-split attention results:
 //     lse = ln sum_s exp(lse_s),   o = sum_s exp(lse_s - lse) * o_s
 //
-// One workgroup per (group, query row, column chunk): 256 threads = SL split
-// lanes x CL column lanes (a float4 each), SL * CL = 256.  The host picks CL
-// per shape: wide chunks (contiguous 1 KB reads of a partial row) when there are
-// many rows, narrow ones when there are few, so that the grid fills the chip.
-// Split lane sl visits splits sl, sl + SL, ... with eight independent 16-byte
-// loads in flight; the split lanes are then summed through LDS in a fixed
-// order, so the result does not depend on timing.
+// Two mappings of a workgroup's 256 threads onto (split lanes) x (column chunks
+// of a float4 each), chosen per shape by the host:
+//  * few rows (R < 64): SL split lanes of a chunk adjacent in one wave, summed by
+//    a butterfly of lane shuffles; SL is the smallest power of two covering the
+//    split count (at most 64), so small merges leave no lane idle.
+//  * many rows: CL column lanes adjacent (a contiguous 16 * CL-byte piece of a
+//    partial row per load) and the split lanes in different waves, summed
+//    through LDS; CL is the widest that still gives about 512 workgroups.  The
+//    partials of a many-row verify are tens of MB: coalescing decides there.
+// Either way split lane sl visits splits sl, sl + SL, ... with eight independent
+// 16-byte loads in flight, and the sums run in a fixed order, so the result
+// does not depend on timing.
 #include "common.h"
 #include "internal.h"
 
@@ -21,7 +26,22 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr int kUnroll = 8;
 
-__global__ __launch_bounds__(256) void combine_kernel(CombineArgs c, int CL) {
+template <int SL>
+__device__ __forceinline__ float max_over_split_lanes(float v) {
+#pragma unroll
+  for (int o = 1; o < SL; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+template <int SL>
+__device__ __forceinline__ float sum_over_split_lanes(float v) {
+#pragma unroll
+  for (int o = 1; o < SL; o <<= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Many rows: CL column lanes adjacent, SL = 256 / CL split lanes in LDS.
+__global__ __launch_bounds__(256) void combine_wide_kernel(CombineArgs c, int CL) {
   const int SL = 256 / CL;
   const int t = threadIdx.x;
   const int cl = t % CL;
@@ -45,7 +65,6 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs c, int CL) {
   __shared__ f32x4 sm_acc[256];
   __shared__ float sm_w[256];
 
-  // pass 1: the largest split lse of this row
   float mx = -INFINITY;
   for (int p = p0 + t; p < p1; p += 256) mx = fmaxf(mx, c.part_lse[(size_t)p * c.R + row]);
 #pragma unroll
@@ -55,7 +74,6 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs c, int CL) {
   const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float Mu = (M == -INFINITY) ? 0.f : M;
 
-  // pass 2: this lane's share of sum_s w_s * o_s and sum_s w_s
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
   const size_t stride = (size_t)c.R * c.D;
@@ -98,26 +116,123 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs c, int CL) {
     const size_t oidx = (size_t)(b * c.n_q + qi) * (c.Hkv * c.G) + g * c.G + hl;
     const float inv = wt > 0.f ? 1.f / wt : 0.f;
     *reinterpret_cast<f32x4*>(c.o + oidx * c.D + col) = tot * inv;
-    if (chunk == 0 && cl == 0 && c.lse)
-      c.lse[oidx] = wt > 0.f ? M + fast_log2(wt) * kLn2 : -INFINITY;
+    if (chunk == 0 && cl == 0 && c.lse) c.lse[oidx] = wt > 0.f ? M + fast_log2(wt) * kLn2 : -INFINITY;
   }
+}
+
+// Few rows: SL split lanes adjacent in a wave.
+template <int SL>
+__global__ __launch_bounds__(256) void combine_kernel(CombineArgs c) {
+  constexpr int CL = 256 / SL;
+  const int t = threadIdx.x;
+  const int sl = t % SL;
+  const int cl = t / SL;
+  const int nblk = c.D / (4 * CL);            // column-chunk blocks per row
+  const int blk = blockIdx.x % nblk;
+  const int rest = blockIdx.x / nblk;
+  const int row = rest % c.R;
+  const int grp = rest / c.R;
+  int p0, p1;
+  if (c.indptr) {
+    p0 = min(max(c.indptr[grp], 0), c.n_parts);
+    p1 = min(max(c.indptr[grp + 1], p0), c.n_parts);
+  } else {
+    p0 = grp * c.splits_per_group;
+    p1 = p0 + c.splits_per_group;
+  }
+  const int col = (blk * CL + cl) * 4;
+
+  // pass 1: the largest split lse of this row
+  float mx = -INFINITY;
+  for (int p = p0 + sl; p < p1; p += SL) mx = fmaxf(mx, c.part_lse[(size_t)p * c.R + row]);
+  const float M = max_over_split_lanes<SL>(mx);
+  const float Mu = (M == -INFINITY) ? 0.f : M;
+
+  // pass 2: this lane's share of sum_s w_s * o_s and sum_s w_s
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;
+  const size_t stride = (size_t)c.R * c.D;
+  const float* base = c.part_o + (size_t)row * c.D + col;
+  for (int p = p0 + sl; p < p1; p += SL * kUnroll) {
+    f32x4 v[kUnroll];
+    float w[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int q = p + u * SL;
+      if (q < p1) {
+        v[u] = *reinterpret_cast<const f32x4*>(base + (size_t)q * stride);
+        const float l = c.part_lse[(size_t)q * c.R + row];
+        w[u] = (l == -INFINITY) ? 0.f : fast_exp2((l - Mu) * kLog2e);
+      } else {
+        v[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        w[u] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      acc += v[u] * w[u];
+      wsum += w[u];
+    }
+  }
+  acc.x = sum_over_split_lanes<SL>(acc.x);
+  acc.y = sum_over_split_lanes<SL>(acc.y);
+  acc.z = sum_over_split_lanes<SL>(acc.z);
+  acc.w = sum_over_split_lanes<SL>(acc.w);
+  wsum = sum_over_split_lanes<SL>(wsum);
+  if (sl == 0) {
+    const int qi = row / c.G;
+    const int hl = row - qi * c.G;
+    const int b = grp / c.Hkv;
+    const int g = grp - b * c.Hkv;
+    const size_t oidx = (size_t)(b * c.n_q + qi) * (c.Hkv * c.G) + g * c.G + hl;
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    *reinterpret_cast<f32x4*>(c.o + oidx * c.D + col) = acc * inv;
+    if (col == 0 && c.lse) c.lse[oidx] = wsum > 0.f ? M + fast_log2(wsum) * kLn2 : -INFINITY;
+  }
+}
+
+template <int SL>
+hipError_t launch_sl(const CombineArgs& c, hipStream_t stream) {
+  constexpr int CL = 256 / SL;
+  CombineArgs arg = c;
+  void* args[] = {&arg};
+  const long grid = (long)c.B * c.Hkv * c.R * (c.D / (4 * CL));
+  return hipLaunchKernel(reinterpret_cast<const void*>(&combine_kernel<SL>), dim3((unsigned)grid),
+                         dim3(256), args, 0, stream);
 }
 
 }  // namespace
 
 hipError_t launch_combine(const CombineArgs& c, hipStream_t stream) {
-  CombineArgs arg = c;
-  // Widest column chunk that still gives about 512 workgroups; at least 16 columns.
-  const long pairs = (long)c.B * c.Hkv * c.R;
-  // CL: a power of two (so that 256 / CL split lanes is whole) dividing D / 4.
-  int CL = 4;
-  while (CL < 64 && (c.D / 4) % (2 * CL) == 0) CL *= 2;
-  while (CL > 4 && pairs * (c.D / (4 * CL)) < 512) CL /= 2;
-  int cl_arg = CL;
-  void* args[] = {&arg, &cl_arg};
-  const long grid = pairs * (c.D / (4 * CL));
-  return hipLaunchKernel(reinterpret_cast<const void*>(&combine_kernel), dim3((unsigned)grid),
-                         dim3(256), args, 0, stream);
+  if (c.R >= 64) {
+    // CL: a power of two dividing D / 4, the widest that gives about 512 workgroups.
+    const long pairs = (long)c.B * c.Hkv * c.R;
+    int CL = 4;
+    while (CL < 64 && (c.D / 4) % (2 * CL) == 0) CL *= 2;
+    while (CL > 4 && pairs * (c.D / (4 * CL)) < 512) CL /= 2;
+    CombineArgs arg = c;
+    int cl_arg = CL;
+    void* args[] = {&arg, &cl_arg};
+    const long grid = pairs * (c.D / (4 * CL));
+    return hipLaunchKernel(reinterpret_cast<const void*>(&combine_wide_kernel), dim3((unsigned)grid),
+                           dim3(256), args, 0, stream);
+  }
+  // Split lanes: the smallest power of two covering the splits of a group (all 64
+  // with a CSR split list, whose counts the host does not see), and no fewer
+  // than 256 / (D / 4) so that a workgroup's column lanes fit in one row.
+  int splits = c.indptr ? 64 : c.splits_per_group;
+  int sl = 1;
+  while (sl < splits && sl < 64) sl *= 2;
+  while (256 / sl > c.D / 4) sl *= 2;
+  switch (sl) {
+    case 1: return launch_sl<1>(c, stream);
+    case 2: return launch_sl<2>(c, stream);
+    case 4: return launch_sl<4>(c, stream);
+    case 8: return launch_sl<8>(c, stream);
+    case 16: return launch_sl<16>(c, stream);
+    case 32: return launch_sl<32>(c, stream);
+    default: return launch_sl<64>(c, stream);
+  }
 }
 
 }  // namespace wmtp
