@@ -237,6 +237,7 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
   for (int rb = 0; rb < NB; ++rb) {
     st.m[rb] = -INFINITY;
     st.l[rb] = 0.f;
+    st.l_drop[rb] = 0.f;
 #pragma unroll
     for (int db = 0; db < DB; ++db) st.acc[rb][db] = f32x16{};
   }
@@ -449,11 +450,13 @@ bool plan_attention(int B, int Hq, int Hkv, int D, int n_q, int max_keys, int nu
   if (num_splits > 0) {
     kbps = (p->nkb + num_splits - 1) / num_splits;
   } else {
-    // Rounded down (to a multiple of 4: one share per wave) so that a length just
-    // past a round number adds a small last split instead of stretching all.
-    const long tiles = (long)p->nkb * groups * p->nrg;
-    long per = tiles / target;
-    per = (per / 4) * 4;
+    // As many splits per (group, row group) as keep the workgroups within the
+    // target, the tiles spread evenly over them: at one workgroup per CU, a
+    // workgroup past the target would run as a second round on its own (a
+    // length just past a round number would otherwise add a one-tile split).
+    const long units = groups * p->nrg;
+    const long per_unit = units < target ? target / units : 1;
+    const long per = ((long)p->nkb + per_unit - 1) / per_unit;
     kbps = (int)(per < 4 ? 4 : (per > INT_MAX ? INT_MAX : per));
   }
   if (p->shared) kbps = (kbps + 1) & ~1;   // even: a split then spans at most cap/2 whole pages

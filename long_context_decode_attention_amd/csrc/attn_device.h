@@ -53,6 +53,8 @@ struct SoftmaxState {
   f32x16 acc[NB][D / 32];   // O^T: lane (n, h) register i holds d = 32*db + 8*(i/4) + 4*h + i%4
   float m[NB];              // running row max of the scaled logits (log2 units)
   float l[NB];              // this lane's share of the running sum of weights
+  float l_drop[NB];         // the part of l that PV did not see: the low bf16 parts of
+                            // the weights of tiles whose PV took the high parts only
 };
 
 // 16 bits: which of this lane's keys are below `count` (tile-relative): keys
@@ -159,6 +161,7 @@ __device__ __forceinline__ void raise_and_rescale(SoftmaxState<D, NB>& st, const
     const float alpha = fast_exp2(st.m[rb] - m_use);
     st.m[rb] = m_new;
     st.l[rb] *= alpha;
+    st.l_drop[rb] *= alpha;
     if (!__all(alpha == 1.0f)) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {

@@ -29,6 +29,9 @@ namespace {
 
 constexpr int kSlots = 5;       // LDS slots per ring (K, V): one resident, four in flight
 constexpr int kPageRegs = 4;   // page ids preloaded per split: 64 per register
+// A tile in which some weight exceeds this fraction of its row's running sum is
+// heavy and goes to the general path (see the kernel).
+constexpr float kHeavyWeight = 1.0f / 32.0f;
 
 // Wait until at most N vector-memory operations of this wave are outstanding.
 // gfx9 encoding: vmcnt in bits [3:0] and [15:14]; expcnt (bits [6:4]) and
@@ -48,6 +51,23 @@ __device__ __forceinline__ void wait_vmcnt() {
 // read of a tile is consumed by that tile's MFMAs before the next barrier.
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_barrier" ::: "memory");
+}
+
+// One 1 KB global-to-LDS load (global_load_lds_dwordx4, non-temporal): lane i's
+// 16 bytes at base + voff (base wave-uniform, voff the lane's byte offset) land
+// at dst + 16 * i.  Written as inline asm because the
+// compiler treats the builtin as an LDS write that may alias every LDS read in
+// flight and waits for all of them first; the slots refilled here are never
+// read while their loads are outstanding (a barrier separates the last read of
+// a slot from its refill, and the explicit vmcnt waits plus a barrier its
+// refill from the next read), so no such wait is needed.  The load is counted
+// in vmcnt like any other, which the explicit waits below account for.
+__device__ __forceinline__ void lds_load_async(const void* base, uint32_t voff, unsigned char* dst) {
+  const unsigned m0 = (unsigned)(size_t)((__attribute__((address_space(3))) unsigned char*)dst);
+  unsigned saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+               "global_load_lds_dwordx4 %1, %2 nt\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "v"(voff), "s"(base), "s"(m0) : "memory");
 }
 
 // Compiler-level fence for memory operations: LDS reads after it are not hoisted
@@ -142,8 +162,9 @@ __device__ __forceinline__ void anchor(T& v) { asm volatile("" : "+v"(v)); }
 // that order.  K operand reads run four steps ahead of their MFMAs and the V
 // operand reads are spread over the same steps, so PV(t) finds them in
 // registers.  dma(i), i < NLOAD, issues the wave's i-th global-to-LDS load of
-// the refill for later tiles; all of them go out between the last V operand
-// read and the PV MFMAs.
+// the refill for later tiles, right after the S^T MFMA of step i, where its
+// issue time overlaps that MFMA.  PV(t) takes the hi bf16 parts of the weights
+// only (the precision argument is at the fast loop in the kernel).
 template <int D, int RBW, int NLOAD, typename Dma>
 __device__ __forceinline__ void fast_tile(SoftmaxState<D, RBW>& st, f32x16 (&s_acc)[RBW],
                                           const bf16x8 (&qop)[RBW][D / 16],
@@ -156,13 +177,14 @@ __device__ __forceinline__ void fast_tile(SoftmaxState<D, RBW>& st, f32x16 (&s_a
   constexpr int E = 256 / D;                   // scores per row block handled per step
   static_assert(E * KS == 16, "scores per step");
 
-  float neg_m[RBW], p[RBW][16], psum[RBW];
+  float neg_m[RBW], p[RBW][16], psum[RBW], pdrop[RBW];
 #pragma unroll
   for (int rb = 0; rb < RBW; ++rb) {
     neg_m[rb] = -st.m[rb];                     // finite: every row has seen a full tile
     psum[rb] = 0.f;
+    pdrop[rb] = 0.f;
   }
-  uint32_t hw[RBW][8], lw[RBW][8];             // packed P^T words: key pair w of row block
+  uint32_t hw[RBW][8];                         // packed P^T words: key pair w of row block
   bf16x8 kop[KS];
   bf16x8 vop[KS];                              // V operand (db, kk) at index 2 * db + kk
 #pragma unroll
@@ -177,6 +199,7 @@ __device__ __forceinline__ void fast_tile(SoftmaxState<D, RBW>& st, f32x16 (&s_a
 #pragma unroll
     for (int rb = 0; rb < RBW; ++rb) {
       anchor(psum[rb]);
+      anchor(pdrop[rb]);
 #pragma unroll
       for (int j = 0; j < E; ++j) anchor(x[rb][ks * E + j]);
       if (ks > 0 && (E > 1 || (ks & 1) == 0)) {
@@ -185,7 +208,6 @@ __device__ __forceinline__ void fast_tile(SoftmaxState<D, RBW>& st, f32x16 (&s_a
         for (int j = 0; j < (E + 1) / 2; ++j) {
           const int w = ((ks - 1) * E) / 2 + j;
           anchor(hw[rb][w]);
-          anchor(lw[rb][w]);
         }
       }
     }
@@ -194,6 +216,7 @@ __device__ __forceinline__ void fast_tile(SoftmaxState<D, RBW>& st, f32x16 (&s_a
     vop[ks] = *reinterpret_cast<const bf16x8*>(vbase + ks * 1024);
 #pragma unroll
     for (int rb = 0; rb < RBW; ++rb) s_acc[rb] = mfma32x32x16(kop[ks], qop[rb][ks], s_acc[rb]);
+    if (ks < NLOAD) dma(ks);
 #pragma unroll
     for (int rb = 0; rb < RBW; ++rb) {
 #pragma unroll
@@ -203,9 +226,10 @@ __device__ __forceinline__ void fast_tile(SoftmaxState<D, RBW>& st, f32x16 (&s_a
         psum[rb] += p[rb][i];
         if (i & 1) {
           const uint32_t hp = pack_bf16x2(p[rb][i - 1], p[rb][i]);
+          const float d0 = p[rb][i - 1] - __builtin_bit_cast(float, hp << 16);
+          const float d1 = p[rb][i] - __builtin_bit_cast(float, hp & 0xFFFF0000u);
           hw[rb][i >> 1] = hp;
-          lw[rb][i >> 1] = pack_bf16x2(p[rb][i - 1] - __builtin_bit_cast(float, hp << 16),
-                                       p[rb][i] - __builtin_bit_cast(float, hp & 0xFFFF0000u));
+          pdrop[rb] += d0 + d1;
         }
       }
     }
@@ -216,21 +240,19 @@ __device__ __forceinline__ void fast_tile(SoftmaxState<D, RBW>& st, f32x16 (&s_a
   // global-to-LDS load waits for the wave's outstanding LDS reads before it
   // issues, which costs little only at this point.
 #pragma unroll
-  for (int i = 0; i < NLOAD; ++i) dma(i);
-  bf16x8 p_hi[RBW][2], p_lo[RBW][2];
+  for (int i = KS; i < NLOAD; ++i) dma(i);
+  bf16x8 p_hi[RBW][2];
 #pragma unroll
   for (int rb = 0; rb < RBW; ++rb) {
     st.l[rb] += psum[rb];
+    st.l_drop[rb] += pdrop[rb];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < 2; ++kk)
       p_hi[rb][kk] = __builtin_bit_cast(bf16x8, u32x4{hw[rb][4 * kk], hw[rb][4 * kk + 1],
                                                       hw[rb][4 * kk + 2], hw[rb][4 * kk + 3]});
-      p_lo[rb][kk] = __builtin_bit_cast(bf16x8, u32x4{lw[rb][4 * kk], lw[rb][4 * kk + 1],
-                                                      lw[rb][4 * kk + 2], lw[rb][4 * kk + 3]});
-    }
   }
-  // PV(t): the hi products of every accumulator, then the lo products, so that
-  // no MFMA waits on the one just before it.
+  // PV(t) with the hi parts of the weights; l_drop holds what they leave out,
+  // so that the output is normalised by exactly the weights PV saw.
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
@@ -238,13 +260,6 @@ __device__ __forceinline__ void fast_tile(SoftmaxState<D, RBW>& st, f32x16 (&s_a
 #pragma unroll
       for (int db = 0; db < DB; ++db)
         st.acc[rb][db] = mfma32x32x16(vop[2 * db + kk], p_hi[rb][kk], st.acc[rb][db]);
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-    for (int rb = 0; rb < RBW; ++rb)
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-        st.acc[rb][db] = mfma32x32x16(vop[2 * db + kk], p_lo[rb][kk], st.acc[rb][db]);
 }
 
 template <int D, int RBW, int NW>
@@ -319,6 +334,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
   for (int rb = 0; rb < RBW; ++rb) {
     st.m[rb] = -INFINITY;
     st.l[rb] = 0.f;
+    st.l_drop[rb] = 0.f;
 #pragma unroll
     for (int db = 0; db < DB; ++db) st.acc[rb][db] = f32x16{};
   }
@@ -455,6 +471,16 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
   // tiles, the causal boundary, bad pages, a rescale) takes the general path,
   // and the fast path resumes after it.  Waves that own no row take only part
   // in the stage pipeline.  s_acc holds S(t) when tile t starts either way.
+  //
+  // Precision of the fast path.  The general path feeds PV each weight as two
+  // bf16 parts (hi + lo, relative error ~2^-17); the fast path feeds the hi
+  // parts alone and takes the dropped lo parts out of the output's normaliser
+  // (l_drop), so o stays an exact weighted mean with each of those weights
+  // perturbed by at most 2^-9 relative: |error| <= 2^-9 * sum_i w_i |v_i - o|
+  // over the fast tiles' keys.  A heavy tile, where some weight exceeds
+  // kHeavyWeight of its row's running sum (a needle, a few dominant keys, the
+  // start of a split), takes the general path, so no key that is a large share
+  // of the mass is rounded.  lse uses the exact sum.
   int t = 0;
   while (t < ntile) {
     bool synced = false;   // tile t is published, its refill not yet issued
@@ -470,6 +496,9 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
           mx[rb] = lane_max16(x[rb]) * a.scale_log2;
           // m = -inf (no maximum yet) needs a raise as well
           slow |= needs_raise(mx[rb], st.m[rb]);
+          // heavy: a weight above kHeavyWeight of the row's running sum (the
+          // row's keys are split over lanes n and n + 32)
+          slow |= fast_exp2(mx[rb] - st.m[rb]) > sum_over_row(st.l[rb]) * kHeavyWeight;
         }
         if (__any(slow)) {
           synced = true;
@@ -487,14 +516,10 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
         auto dma = [&](int i) {
           if (i < NH) {
             const int op = wave + NW * i;
-            __builtin_amdgcn_global_load_lds(
-                (void*)(kt + k_operand_offset(op, m, h)),
-                (__attribute__((address_space(3))) void*)(kdst + op * 1024), 16, 0, 2);
+            lds_load_async(kt, 2u * k_operand_offset(op, m, h), kdst + op * 1024);
           } else {
             const int op = wave + NW * (i - NH);
-            __builtin_amdgcn_global_load_lds(
-                (void*)(vt + v_operand_offset<D>(op >> 1, op & 1, m, h)),
-                (__attribute__((address_space(3))) void*)(vdst + op * 1024), 16, 0, 2);
+            lds_load_async(vt, 2u * v_operand_offset<D>(op >> 1, op & 1, m, h), vdst + op * 1024);
           }
         };
         fast_tile<D, RBW, 2 * NH>(st, s_acc, qop, x, a.scale_log2, k_slot(t + 1) + lane * 16,
@@ -527,8 +552,9 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
   for (int rb = 0; rb < RBW; ++rb) {
     const int row = row0 + rb * 32 + m;
     const float Ltot = sum_over_row(st.l[rb]);
+    const float Lpv = Ltot - sum_over_row(st.l_drop[rb]);
     if (row >= a.R) continue;
-    const float inv = Ltot > 0.f ? 1.f / Ltot : 0.f;
+    const float inv = Lpv > 0.f ? 1.f / Lpv : 0.f;
     float* op;
     float* lp;
     if (a.direct) {

@@ -344,6 +344,31 @@ def test_verify_short(S):
     _verify_case(CFG["ctx1m_g32x2_d256"], 30 + S, [S], 8)
 
 
+@pytest.mark.parametrize("cfg_name,S,n_q,num_splits,peak", [
+    ("ctx1m_g32x2_d256", 20000, 8, 2, 1.0),
+    ("ctx1m_g32x2_d256", 16000, 8, 1, 4.0),
+    ("nope8l_1m_g64x2_d128", 12000, 8, 1, 1.0),
+    ("ctx128k_g32x4_d128", 15000, 8, 2, 2.0),
+])
+def test_verify_long_splits(cfg_name, S, n_q, num_splits, peak):
+    """Splits of hundreds of 32-key tiles, so that most tiles take the verify's
+    fast path, whose PV sees the weights rounded to bf16 (the normaliser then
+    uses the same rounded weights); plain and peaked queries (q x peak)."""
+    lib = _lib()
+    cfg = CFG[cfg_name]
+    vs = VerifyScenario(cfg, 60 + S % 97, [S], n_q)
+    vs.append_proposed()
+    q = W.bf16_round(peak * W.bf16_to_f32(vs.q))
+    L = S + n_q
+    o, l = lib.verify_attn(dev_bf16(q), vs.kv.k, vs.kv.v, vs.kv.block_table, dev_i32([L]), L,
+                           1.0, num_splits=num_splits)
+    torch().cuda.synchronize()
+    ro, rl = OA.verify(q[0], vs.K[0], vs.V[0], L, 1.0)
+    err, lerr = compare(o[0], l[0], ro, rl, f"verify long splits {cfg_name} peak {peak}")
+    print(f"verify long splits {cfg_name} S={S} splits={num_splits} peak={peak}: "
+          f"max|o err| {err:.2e} (max|o| {float(np.max(np.abs(ro))):.2e}), max|lse err| {lerr:.2e}")
+
+
 def test_verify_same_in_both_arms():
     """The verify call reads only the target KV: repeated calls (one per arm) agree bitwise."""
     lib = _lib()
