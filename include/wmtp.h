@@ -175,6 +175,9 @@ wmtp_status wmtp_draft_attn_window(const uint16_t* q, const uint16_t* ring_k,
  * n_sink + n_recent is slack: the window call reads only the last n_recent,
  * so up to (C - n_sink - n_recent) rolled-back positions never evict a
  * position still in the window.  Rolling back is writing a smaller ring_T.
+ * Up to 64 positions run as one launch (one workgroup per request); longer
+ * appends run as a fill spread over many workgroups followed by a one-thread-
+ * per-request launch that advances ring_T, both on `stream`.
  *   ring_k, ring_v   bf16 tiled pages (in/out), B * C / 64 pages
  *   ring_pos         int32 [B][C] (in/out)
  *   ring_T           int64 [B] (in/out); negative values count as 0

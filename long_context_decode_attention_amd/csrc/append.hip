@@ -1,8 +1,9 @@
 // Writers of the tiled page layout: the draft ring append and the paged append.
 //
 // Tiled pages: tile t = (page * Hkv + g) * 2 + (pos % 64) / 32 holds 32 * D
-// elements; K tile element (pos, d) at (d / 32) * 1024 + (pos % 32) * 32 + d % 32,
-// V tile element (pos, d) at d * 32 + pos % 32.
+// elements; with tok = pos % 32, K tile element (tok, d) at (d / 16) * 512 +
+// tok * 16 + d % 16, V tile element (tok, d) at (tok / 16) * 16 * D + d * 16 +
+// tok % 16 (the 1 KB MFMA operand blocks the attention kernels read).
 #include "common.h"
 #include "internal.h"
 
@@ -27,18 +28,14 @@ __device__ __forceinline__ void store_kv8(uint16_t* kc, uint16_t* vc, size_t til
   }
 }
 
-// One workgroup per request: every thread reads the old count before thread 0
-// stores the new one, so the count update cannot race with the reads.
-__global__ __launch_bounds__(256) void ring_append_kernel(RingAppendArgs a) {
-  const int b = blockIdx.x;
-  int64_t T0 = a.ring_T[b];
-  if (T0 < 0) T0 = 0;
-  __syncthreads();
+// Of the appended positions [T0, T0 + n_new), a sink position keeps its slot for
+// good, and a later position survives iff no later appended position shares its
+// slot, i.e. iff p >= T1 - M.  Only survivors are written: items
+// [first, total) with stride `step` of the survivors' 16-byte pieces.
+__device__ __forceinline__ void ring_write(const RingAppendArgs& a, int b, int64_t T0, int first,
+                                           int step) {
   const int64_t T1 = T0 + a.n_new;
   const int64_t M = a.C - a.n_sink;
-  // Of the appended positions [T0, T1), a sink position keeps its slot for good,
-  // and a later position survives iff no later appended position shares its
-  // slot, i.e. iff p >= T1 - M.  Only survivors are written.
   const int64_t s_lo = T0;
   const int64_t s_hi = T1 < a.n_sink ? T1 : (int64_t)a.n_sink;
   int64_t r_lo = T0 > a.n_sink ? T0 : (int64_t)a.n_sink;
@@ -48,7 +45,7 @@ __global__ __launch_bounds__(256) void ring_append_kernel(RingAppendArgs a) {
   const int n_r = r_hi > r_lo ? (int)(r_hi - r_lo) : 0;
   const int chunks = a.Hkv * (a.D >> 3);      // 16-byte pieces per position
   const int total = (n_s + n_r) * chunks;
-  for (int idx = threadIdx.x; idx < total; idx += 256) {
+  for (int idx = first; idx < total; idx += step) {
     const int e = idx / chunks;
     const int c = idx - e * chunks;
     const int64_t p = e < n_s ? s_lo + e : r_lo + (e - n_s);
@@ -63,8 +60,37 @@ __global__ __launch_bounds__(256) void ring_append_kernel(RingAppendArgs a) {
     store_kv8(a.kc, a.vc, tile, off & 31, d0, a.D, a.k_new + src, a.v_new + src);
     if (c == 0) a.ring_pos[(size_t)b * a.C + slot] = (int32_t)p;
   }
+}
+
+// Appends of a few positions (the decode steps): one workgroup per request;
+// every thread reads the old count before thread 0 stores the new one.
+__global__ __launch_bounds__(256) void ring_append_kernel(RingAppendArgs a) {
+  const int b = blockIdx.x;
+  int64_t T0 = a.ring_T[b];
+  if (T0 < 0) T0 = 0;
   __syncthreads();
-  if (threadIdx.x == 0) a.ring_T[b] = T1;
+  ring_write(a, b, T0, threadIdx.x, 256);
+  __syncthreads();
+  if (threadIdx.x == 0) a.ring_T[b] = T0 + a.n_new;
+}
+
+// Bulk fills (a prefill or a resume): the survivors' pieces spread over
+// gridDim.x workgroups per request; the count is advanced afterwards by
+// ring_count_kernel, launched next on the same stream, so that no workgroup
+// can read a count another has already advanced.
+__global__ __launch_bounds__(256) void ring_fill_kernel(RingAppendArgs a) {
+  const int b = blockIdx.y;
+  int64_t T0 = a.ring_T[b];
+  if (T0 < 0) T0 = 0;
+  ring_write(a, b, T0, blockIdx.x * 256 + threadIdx.x, gridDim.x * 256);
+}
+
+__global__ __launch_bounds__(256) void ring_count_kernel(int64_t* ring_T, int B, int n_new) {
+  const int b = blockIdx.x * 256 + threadIdx.x;
+  if (b >= B) return;
+  int64_t T0 = ring_T[b];
+  if (T0 < 0) T0 = 0;
+  ring_T[b] = T0 + n_new;
 }
 
 __global__ __launch_bounds__(256) void paged_append_kernel(PagedAppendArgs a) {
@@ -88,13 +114,30 @@ __global__ __launch_bounds__(256) void paged_append_kernel(PagedAppendArgs a) {
   store_kv8(a.kc, a.vc, tile, off & 31, d0, a.D, a.k_new + src, a.v_new + src);
 }
 
+// Appends longer than this take the multi-workgroup fill.
+constexpr int kRingBulkFrom = 64;
+
 }  // namespace
 
 hipError_t launch_ring_append(const RingAppendArgs& a, hipStream_t stream) {
   RingAppendArgs arg = a;
   void* args[] = {&arg};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&ring_append_kernel), dim3(a.B), dim3(256),
-                         args, 0, stream);
+  if (a.n_new <= kRingBulkFrom) {
+    return hipLaunchKernel(reinterpret_cast<const void*>(&ring_append_kernel), dim3(a.B),
+                           dim3(256), args, 0, stream);
+  }
+  // at most C survivors per request, 8 pieces per thread
+  const long pieces = (long)(a.n_new < a.C ? a.n_new : a.C) * a.Hkv * (a.D >> 3);
+  long gx = (pieces + 2047) / 2048;
+  if (gx > 1024) gx = 1024;
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&ring_fill_kernel),
+                                 dim3((unsigned)gx, a.B), dim3(256), args, 0, stream);
+  if (e != hipSuccess) return e;
+  int64_t* ring_T = a.ring_T;
+  int B = a.B, n_new = a.n_new;
+  void* cargs[] = {&ring_T, &B, &n_new};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&ring_count_kernel), dim3((B + 255) / 256),
+                         dim3(256), cargs, 0, stream);
 }
 
 hipError_t launch_paged_append(const PagedAppendArgs& a, hipStream_t stream) {
