@@ -42,7 +42,7 @@ WORKLOAD = "ctx1m_g32x2_d256"
 # keyed by a hash of the sources that kernel is built from: a changed kernel
 # reports null until it is measured again.
 MEASURED_TRAFFIC = {
-    "b9a5ceba12f0fe9f": {"read": 2.148e9, "write": 4.211e6, "keys": 1048587},
+    "f1f786c596df34c5": {"read": 2.148e9, "write": 4.211e6, "keys": 1048587},
 }
 KERNEL_SOURCES = ("csrc/attn.hip", "csrc/attn_device.h", "csrc/common.h")
 
@@ -159,7 +159,11 @@ def main() -> int:
     l_f = torch.empty(B, Hq, device=dev)
     o_v = torch.empty(B, n_q, Hq, D, device=dev)
     l_v = torch.empty(B, n_q, Hq, device=dev)
+    o_p = torch.empty(B, Hq, D, device=dev)
+    l_p = torch.empty(B, Hq, device=dev)
     ws_w = lib.new_workspace(lib.workspace_bytes(B, Hq, Hkv, D, 1, C, ring=True), dev)
+    ws_p = lib.new_workspace(lib.workspace_bytes(B, Hq, Hkv, D, 1, n_sink + n_recent,
+                                                 paged_window=True), dev)
     ws_f = lib.new_workspace(lib.workspace_bytes(B, Hq, Hkv, D, 1, max_d, args.num_splits,
                                                  partials_only=True), dev)
     ws_v = lib.new_workspace(lib.workspace_bytes(B, Hq, Hkv, D, n_q, max_t), dev)
@@ -186,16 +190,26 @@ def main() -> int:
                                     partials_only=True, prepare=True),
                 lib.split_combine(po, pl, B, Hkv, G, 1, splits_per_group=splits_f,
                                   o=o_f.view(B, 1, Hq, D), lse=l_f.view(B, 1, Hq), prepare=True)))
+        # the pages' own windowed draft: the draft KV stays in the paged cache and the
+        # attention reads a truncated index (the appends rewrite the positions the
+        # native arm has just written, with the same values)
+        wpg = []
+        for j in range(gamma):
+            wpg.append(lib.paged_append(dkv.k, dkv.v, dkv.block_table, d_pos[k, j], kd_new[k, j],
+                                        vd_new[k, j], prepare=True))
+            wpg.append(lib.draft_attn_window_paged(qd[k, j], dkv.k, dkv.v, dkv.block_table,
+                                                   d_len[k, j], max_d, n_sink, n_recent, 1.0,
+                                                   o_p, l_p, ws_p, prepare=True))
         ver = (lib.paged_append(tkv.k, tkv.v, tkv.block_table, t_pos[k], kt_new[k], vt_new[k],
                                 prepare=True),
                lib.verify_attn(qv[k], tkv.k, tkv.v, tkv.block_table, t_len[k], max_t, 1.0, o_v,
                                l_v, ws_v, prepare=True))
-        plan.append((win, full, ver))
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5 + 2 * gamma)]
+        plan.append((win, full, wpg, ver))
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6 + 2 * gamma)]
            for _ in range(nsteps)]
 
     def step(k):
-        win, full, ver = plan[k]
+        win, full, wpg, ver = plan[k]
         e = evs[k]
         e[0].record(stream)
         for c in win:                       # windowed arm: gamma x (ring append + attention)
@@ -208,12 +222,15 @@ def main() -> int:
             e[6 + 2 * j].record(stream)
             comb()
         e[2].record(stream)
+        for c in wpg:                       # windowed arm by index truncation (no ring)
+            c()
+        e[5 + 2 * gamma].record(stream)
         ver[0]()                            # target append of the proposed positions
         e[3].record(stream)
         ver[1]()                            # verify attention
         e[4].record(stream)
-        return {"t0": e[0], "t1": e[1], "t2": e[2], "v0": e[3], "t3": e[4],
-                "attn": [(e[5 + 2 * j], e[6 + 2 * j]) for j in range(gamma)]}
+        return {"t0": e[0], "t1": e[1], "t2": e[2], "p1": e[5 + 2 * gamma], "v0": e[3],
+                "t3": e[4], "attn": [(e[5 + 2 * j], e[6 + 2 * j]) for j in range(gamma)]}
 
     if args.copy_calibration:
         src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
@@ -239,7 +256,8 @@ def main() -> int:
 
     win_chain = np.median([us(m["t0"], m["t1"]) for m in marks])
     full_chain = np.median([us(m["t1"], m["t2"]) for m in marks])
-    verify_us = np.median([us(m["t2"], m["t3"]) for m in marks])
+    wpg_chain = np.median([us(m["t2"], m["p1"]) for m in marks])
+    verify_us = np.median([us(m["p1"], m["t3"]) for m in marks])
     verify_kernel_us = np.median([us(m["v0"], m["t3"]) for m in marks])
     attn_us = np.array([us(a, b) for m in marks for (a, b) in m["attn"]])
     attn_mean = float(attn_us.mean())
@@ -281,8 +299,10 @@ def main() -> int:
                    "verify_queries": n_q},
         "draft_attn_us_per_step": {"full": round(float(full_chain / gamma), 2),
                                    "window": round(float(win_step_us), 2),
+                                   "window_paged_index": round(float(wpg_chain / gamma), 2),
                                    "full_attention_kernel": round(attn_mean, 2)},
         "decode_step_us": {"full": round(float(step_full), 2), "window": round(float(step_window), 2),
+                           "window_paged_index": round(float(verify_us + wpg_chain), 2),
                            "verify": round(float(verify_us), 2)},
         "cost_reduction": {"native_over_window_minus_1": round(float(up), 4),
                            "one_minus_window_over_native": round(float(down), 4)},

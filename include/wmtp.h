@@ -81,13 +81,15 @@ typedef enum wmtp_status {
 const char* wmtp_status_string(wmtp_status s);
 
 /* `call` argument of the two planning queries below */
-#define WMTP_CALL_PAGED 0 /* wmtp_draft_attn_full, wmtp_verify_attn */
-#define WMTP_CALL_RING 1  /* wmtp_draft_attn_window */
+#define WMTP_CALL_PAGED 0        /* wmtp_draft_attn_full, wmtp_verify_attn */
+#define WMTP_CALL_RING 1         /* wmtp_draft_attn_window */
+#define WMTP_CALL_PAGED_WINDOW 2 /* wmtp_draft_attn_window_paged */
 
 /*
  * Split plan of the attention calls.  n_q = 1 for the draft calls;
- * max_keys = min(max_seq_len, max_pages * 64) for the paged calls and C for
- * the ring call; num_splits = 0 lets the library choose.  Returns the number
+ * max_keys = min(max_seq_len, max_pages * 64) for the paged calls, C for
+ * the ring call and n_sink + n_recent for the truncated paged index (its
+ * plan then covers any max_seq_len); num_splits = 0 lets the library choose.  Returns the number
  * of key splits per (sequence, kv head) that a call with these arguments
  * will use, or -1 if the sizes are invalid.
  */
@@ -136,6 +138,28 @@ wmtp_status wmtp_draft_attn_full(const uint16_t* q, const uint16_t* k_cache,
                                  float softmax_scale, float* o, float* lse, void* workspace,
                                  size_t workspace_bytes, int num_splits, unsigned flags,
                                  void* stream);
+
+/*
+ * Windowed draft attention over the paged draft KV by index truncation: the
+ * same key set as wmtp_draft_attn_window, read straight from the paged cache
+ * instead of from a compact ring.  (Verdict page, key machinery: the draft
+ * reads a per-request KV index cut down to the attention sink plus the recent
+ * window; nothing is reclaimed, the full draft KV stays resident.)
+ * Sequence b attends over keys [0, min(n_sink, L_b)) u [max(n_sink, L_b -
+ * n_recent), L_b) of its pages, each key once.
+ *   arguments as wmtp_draft_attn_full, plus
+ *   n_sink, n_recent (host) the window: n_sink >= 0, n_recent >= 1
+ * Workspace: wmtp_workspace_bytes(WMTP_CALL_PAGED_WINDOW, ..., max_keys =
+ * n_sink + n_recent, ...).  More than 32 query rows per kv head (Hq / Hkv)
+ * give WMTP_ERR_UNSUPPORTED.
+ */
+wmtp_status wmtp_draft_attn_window_paged(const uint16_t* q, const uint16_t* k_cache,
+                                         const uint16_t* v_cache, const int32_t* block_table,
+                                         const int32_t* seq_lens, int B, int Hq, int Hkv, int D,
+                                         int num_pages, int max_pages, int max_seq_len,
+                                         int n_sink, int n_recent, float softmax_scale, float* o,
+                                         float* lse, void* workspace, size_t workspace_bytes,
+                                         int num_splits, unsigned flags, void* stream);
 
 /*
  * Windowed draft attention over a per-request ring of C slots.

@@ -25,7 +25,8 @@ FLAG_PARTIALS_ONLY = 1
 # Every symbol include/wmtp.h declares.
 EXPORTS = (
     "wmtp_status_string", "wmtp_plan_splits", "wmtp_workspace_bytes",
-    "wmtp_draft_attn_full", "wmtp_draft_attn_window", "wmtp_ring_append",
+    "wmtp_draft_attn_full", "wmtp_draft_attn_window", "wmtp_draft_attn_window_paged",
+    "wmtp_ring_append",
     "wmtp_paged_append", "wmtp_verify_attn", "wmtp_split_combine",
 )
 
@@ -55,6 +56,7 @@ _SIGS = {
     "wmtp_workspace_bytes": ([_I] * 9, _SZ),
     "wmtp_draft_attn_full": ([_P] * 5 + [_I] * 7 + [_F, _P, _P, _P, _SZ, _I, _U, _P], _I),
     "wmtp_draft_attn_window": ([_P] * 5 + [_I] * 7 + [_F, _P, _P, _P, _SZ, _I, _U, _P], _I),
+    "wmtp_draft_attn_window_paged": ([_P] * 5 + [_I] * 9 + [_F, _P, _P, _P, _SZ, _I, _U, _P], _I),
     "wmtp_ring_append": ([_P] * 6 + [_I] * 6 + [_P], _I),
     "wmtp_paged_append": ([_P] * 6 + [_I] * 6 + [_P], _I),
     "wmtp_verify_attn": ([_P] * 5 + [_I] * 8 + [_F, _P, _P, _P, _SZ, _I, _U, _P], _I),
@@ -200,10 +202,18 @@ def new_ring(B: int, C: int, Hkv: int, D: int, n_sink: int, n_recent: int, devic
 
 CALL_PAGED = 0
 CALL_RING = 1
+CALL_PAGED_WINDOW = 2
 
 
-def plan_splits(B, Hq, Hkv, D, n_q, max_keys, num_splits=0, ring=False) -> int:
-    n = load().wmtp_plan_splits(CALL_RING if ring else CALL_PAGED, B, Hq, Hkv, D, n_q, max_keys,
+def _call_kind(ring, paged_window):
+    return CALL_RING if ring else (CALL_PAGED_WINDOW if paged_window else CALL_PAGED)
+
+
+def plan_splits(B, Hq, Hkv, D, n_q, max_keys, num_splits=0, ring=False,
+                paged_window=False) -> int:
+    """Splits per (sequence, kv head); with ``paged_window`` max_keys is the window
+    n_sink + n_recent of ``draft_attn_window_paged``."""
+    n = load().wmtp_plan_splits(_call_kind(ring, paged_window), B, Hq, Hkv, D, n_q, max_keys,
                                 num_splits)
     if n < 0:
         raise WmtpError("wmtp_plan_splits", 1)
@@ -211,8 +221,8 @@ def plan_splits(B, Hq, Hkv, D, n_q, max_keys, num_splits=0, ring=False) -> int:
 
 
 def workspace_bytes(B, Hq, Hkv, D, n_q, max_keys, num_splits=0, partials_only=False,
-                    ring=False) -> int:
-    return int(load().wmtp_workspace_bytes(CALL_RING if ring else CALL_PAGED, B, Hq, Hkv, D, n_q,
+                    ring=False, paged_window=False) -> int:
+    return int(load().wmtp_workspace_bytes(_call_kind(ring, paged_window), B, Hq, Hkv, D, n_q,
                                            max_keys, num_splits, 1 if partials_only else 0))
 
 
@@ -221,11 +231,12 @@ def new_workspace(nbytes: int, device="cuda"):
     return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
 
 
-def partials_view(workspace, B, Hq, Hkv, D, n_q, max_keys, num_splits=0, ring=False):
+def partials_view(workspace, B, Hq, Hkv, D, n_q, max_keys, num_splits=0, ring=False,
+                  paged_window=False):
     """(part_o [P, R, D], part_lse [P, R]) views of a workspace left by a
     partials-only call with the same arguments."""
     torch = _torch()
-    splits = plan_splits(B, Hq, Hkv, D, n_q, max_keys, num_splits, ring)
+    splits = plan_splits(B, Hq, Hkv, D, n_q, max_keys, num_splits, ring, paged_window)
     P = B * Hkv * splits
     R = n_q * (Hq // Hkv)
     ob = P * R * D * 4
@@ -275,6 +286,37 @@ def draft_attn_full(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, sof
         B, Hq, Hkv, D, num_pages, max_pages, int(max_seq_len), float(softmax_scale),
         _ptr(o), _ptr(lse), _ptr(workspace), workspace.numel(), int(num_splits),
         FLAG_PARTIALS_ONLY if partials_only else 0, _stream(stream)), prepare)
+    if prepare:
+        return c
+    return workspace if partials_only else (o, lse)
+
+
+def draft_attn_window_paged(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, n_sink,
+                            n_recent, softmax_scale=1.0, o=None, lse=None, workspace=None,
+                            num_splits=0, partials_only=False, stream=None, prepare=False):
+    """Windowed draft attention by index truncation over the paged draft KV
+    (``wmtp_draft_attn_window_paged``): keys [0, n_sink) and the last n_recent."""
+    torch = _torch()
+    B, Hq, D = q.shape
+    num_pages, Hkv = k_cache.shape[0], k_cache.shape[1]
+    max_pages = block_table.shape[1]
+    _need(q, torch.bfloat16, None, "q")
+    _need(k_cache, torch.bfloat16, k_cache_shape(num_pages, Hkv, D), "k_cache")
+    _need(v_cache, torch.bfloat16, v_cache_shape(num_pages, Hkv, D), "v_cache")
+    _need(block_table, torch.int32, (B, max_pages), "block_table")
+    _need(seq_lens, torch.int32, (B,), "seq_lens")
+    need = workspace_bytes(B, Hq, Hkv, D, 1, int(n_sink) + int(n_recent), num_splits,
+                           partials_only, paged_window=True)
+    if workspace is None:
+        workspace = new_workspace(need, q.device)
+    _need(workspace, torch.uint8, None, "workspace")
+    if not partials_only:
+        o, lse = _outputs(o, lse, (B, Hq, D), (B, Hq), q.device)
+    c = _invoke("wmtp_draft_attn_window_paged", (
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
+        B, Hq, Hkv, D, num_pages, max_pages, int(max_seq_len), int(n_sink), int(n_recent),
+        float(softmax_scale), _ptr(o), _ptr(lse), _ptr(workspace), workspace.numel(),
+        int(num_splits), FLAG_PARTIALS_ONLY if partials_only else 0, _stream(stream)), prepare)
     if prepare:
         return c
     return workspace if partials_only else (o, lse)

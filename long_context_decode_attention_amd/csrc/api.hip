@@ -20,16 +20,26 @@ bool head_dim_ok(int D) { return D == 64 || D == 128 || D == 256; }
 
 wmtp_status from_hip(hipError_t e) { return e == hipSuccess ? WMTP_OK : WMTP_ERR_HIP; }
 
-// Common tail of the three attention calls: plan, check the workspace, launch the
-// split pass and, when there is more than one split, the combine.
-wmtp_status run_attention(AttnArgs a, bool ring, int max_keys, float* o, float* lse,
-                          void* workspace, size_t workspace_bytes, int num_splits,
+// Keys to plan a truncated paged index for (window n_sink + n_recent = w): its
+// virtual tiles number at most ceil(w / 32) + 2 (the sink part and the recent part
+// may each start or end inside a tile).
+int window_plan_keys(long w, int max_keys) {
+  const long k = 32 * ((w + 31) / 32 + 2);
+  return k < max_keys ? (int)k : max_keys;
+}
+
+// Common tail of the attention calls: plan (for plan_keys keys per sequence),
+// check the workspace, launch the split pass and, when there is more than one
+// split, the combine.
+wmtp_status run_attention(AttnArgs a, bool ring, int max_keys, int plan_keys, float* o,
+                          float* lse, void* workspace, size_t workspace_bytes, int num_splits,
                           unsigned flags, hipStream_t stream) {
   const int partials_only = (flags & WMTP_FLAG_PARTIALS_ONLY) ? 1 : 0;
   AttnPlan p;
-  if (!plan_attention(a.B, a.Hq, a.Hkv, a.D, a.n_q, max_keys, num_splits, partials_only, ring,
+  if (!plan_attention(a.B, a.Hq, a.Hkv, a.D, a.n_q, plan_keys, num_splits, partials_only, ring,
                       &p))
     return (a.n_q * (a.Hq / a.Hkv) > 256) ? WMTP_ERR_UNSUPPORTED : WMTP_ERR_INVALID_ARG;
+  if (a.win && p.shared) return WMTP_ERR_UNSUPPORTED;   // truncated index: split kernel only
   if (p.ws_bytes > 0) {
     if (!workspace || !aligned16(workspace)) return WMTP_ERR_WORKSPACE;
     if (workspace_bytes < p.ws_bytes) return WMTP_ERR_WORKSPACE;
@@ -95,7 +105,12 @@ const char* wmtp_status_string(wmtp_status s) {
 int wmtp_plan_splits(int call, int B, int Hq, int Hkv, int D, int n_q, int max_keys,
                      int num_splits) {
   AttnPlan p;
-  if (call != WMTP_CALL_PAGED && call != WMTP_CALL_RING) return -1;
+  if (call != WMTP_CALL_PAGED && call != WMTP_CALL_RING && call != WMTP_CALL_PAGED_WINDOW)
+    return -1;
+  if (call == WMTP_CALL_PAGED_WINDOW) {
+    if (max_keys < 0) return -1;
+    max_keys = window_plan_keys(max_keys, INT_MAX);
+  }
   if (!plan_attention(B, Hq, Hkv, D, n_q, max_keys, num_splits, 0, call == WMTP_CALL_RING, &p))
     return -1;
   return p.nsplit;
@@ -104,20 +119,27 @@ int wmtp_plan_splits(int call, int B, int Hq, int Hkv, int D, int n_q, int max_k
 size_t wmtp_workspace_bytes(int call, int B, int Hq, int Hkv, int D, int n_q, int max_keys,
                             int num_splits, int partials_only) {
   AttnPlan p;
-  if (call != WMTP_CALL_PAGED && call != WMTP_CALL_RING) return 0;
+  if (call != WMTP_CALL_PAGED && call != WMTP_CALL_RING && call != WMTP_CALL_PAGED_WINDOW)
+    return 0;
+  if (call == WMTP_CALL_PAGED_WINDOW) {
+    if (max_keys < 0) return 0;
+    max_keys = window_plan_keys(max_keys, INT_MAX);
+  }
   if (!plan_attention(B, Hq, Hkv, D, n_q, max_keys, num_splits, partials_only,
                       call == WMTP_CALL_RING, &p))
     return 0;
   return p.ws_bytes;
 }
 
+// win: keys [0, n_sink) and the last n_recent of each sequence only.
 static wmtp_status paged_attention(const uint16_t* q, const uint16_t* k_cache,
                                    const uint16_t* v_cache, const int32_t* block_table,
                                    const int32_t* seq_lens, int B, int n_q, int Hq, int Hkv,
                                    int D, int num_pages, int max_pages, int max_seq_len,
                                    float softmax_scale, float* o, float* lse, void* workspace,
                                    size_t workspace_bytes, int num_splits, unsigned flags,
-                                   void* stream) {
+                                   void* stream, bool win = false, int n_sink = 0,
+                                   int n_recent = 0) {
   if (!attn_dims_ok(B, Hq, Hkv, D) || n_q < 1) return WMTP_ERR_INVALID_ARG;
   if (!head_dim_ok(D)) return WMTP_ERR_UNSUPPORTED;
   if (n_q * (Hq / Hkv) > 256) return WMTP_ERR_UNSUPPORTED;
@@ -147,8 +169,16 @@ static wmtp_status paged_attention(const uint16_t* q, const uint16_t* k_cache,
   a.num_pages = num_pages;
   a.max_pages = max_pages;
   a.scale_log2 = softmax_scale * kLog2e;
-  return run_attention(a, false, max_keys, o, lse, workspace, workspace_bytes, num_splits, flags,
-                       static_cast<hipStream_t>(stream));
+  int plan_keys = max_keys;
+  if (win) {
+    if (n_sink < 0 || n_recent < 1) return WMTP_ERR_INVALID_ARG;
+    a.win = 1;
+    a.n_sink = n_sink;
+    a.n_recent = n_recent;
+    plan_keys = window_plan_keys((long)n_sink + n_recent, max_keys);
+  }
+  return run_attention(a, false, max_keys, plan_keys, o, lse, workspace, workspace_bytes,
+                       num_splits, flags, static_cast<hipStream_t>(stream));
 }
 
 wmtp_status wmtp_draft_attn_full(const uint16_t* q, const uint16_t* k_cache,
@@ -161,6 +191,18 @@ wmtp_status wmtp_draft_attn_full(const uint16_t* q, const uint16_t* k_cache,
   return paged_attention(q, k_cache, v_cache, block_table, seq_lens, B, 1, Hq, Hkv, D, num_pages,
                          max_pages, max_seq_len, softmax_scale, o, lse, workspace,
                          workspace_bytes, num_splits, flags, stream);
+}
+
+wmtp_status wmtp_draft_attn_window_paged(const uint16_t* q, const uint16_t* k_cache,
+                                         const uint16_t* v_cache, const int32_t* block_table,
+                                         const int32_t* seq_lens, int B, int Hq, int Hkv, int D,
+                                         int num_pages, int max_pages, int max_seq_len,
+                                         int n_sink, int n_recent, float softmax_scale, float* o,
+                                         float* lse, void* workspace, size_t workspace_bytes,
+                                         int num_splits, unsigned flags, void* stream) {
+  return paged_attention(q, k_cache, v_cache, block_table, seq_lens, B, 1, Hq, Hkv, D, num_pages,
+                         max_pages, max_seq_len, softmax_scale, o, lse, workspace,
+                         workspace_bytes, num_splits, flags, stream, true, n_sink, n_recent);
 }
 
 wmtp_status wmtp_verify_attn(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
@@ -212,7 +254,7 @@ wmtp_status wmtp_draft_attn_window(const uint16_t* q, const uint16_t* ring_k,
   a.n_sink = n_sink;
   a.n_recent = n_recent;
   a.scale_log2 = softmax_scale * kLog2e;
-  return run_attention(a, true, C, o, lse, workspace, workspace_bytes, num_splits, flags,
+  return run_attention(a, true, C, C, o, lse, workspace, workspace_bytes, num_splits, flags,
                        static_cast<hipStream_t>(stream));
 }
 

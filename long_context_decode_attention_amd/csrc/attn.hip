@@ -106,11 +106,13 @@ __device__ __forceinline__ void load_v(VTile<D>& t, const AttnArgs& a, size_t ti
     for (int kk = 0; kk < 2; ++kk) t.v[db][kk] = ld_bf16x8_stream(vt + v_operand_offset<D>(db, kk, m, h));
 }
 
-// Which of this lane's 16 keys exist for every row: inside the sequence length,
-// or (ring) holding a position of the current window.
+// Which of this lane's 16 keys exist for every row: inside the sequence length
+// (and, for a truncated paged index, below sink_end or from r0 on), or (ring)
+// holding a position of the current window.
 template <int D, bool RING>
 __device__ __forceinline__ uint32_t present_keys(const KTile<D, RING>& t, const AttnArgs& a,
-                                                 int kb, int L, int T, int h) {
+                                                 int kb, int L, int T, int h, int sink_end,
+                                                 int r0) {
   if constexpr (RING) {
     uint32_t keep = 0;
 #pragma unroll
@@ -121,7 +123,9 @@ __device__ __forceinline__ uint32_t present_keys(const KTile<D, RING>& t, const 
     }
     return keep;
   } else {
-    return keys_below(L - kb * 32, h);
+    uint32_t keep = keys_below(L - kb * 32, h);
+    if (a.win) keep &= keys_below(sink_end - kb * 32, h) | (~keys_below(r0 - kb * 32, h) & 0xFFFFu);
+    return keep;
   }
 }
 
@@ -195,8 +199,20 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
     L = len_raw < 0 ? 0 : (len_raw > a.max_keys ? a.max_keys : len_raw);
   }
   const int nkb = (L + 31) >> 5;
+  // Truncated paged index (win): the key set [0, sink_end) u [r0, L) as virtual
+  // tiles, the sink tiles [0, st_end) then the recent tiles from kr on; phys()
+  // maps a virtual tile to its 32-key tile of the sequence.
+  int sink_end = L, r0 = 0, st_end = 0, kr = 0, nvt = nkb;
+  if (!RING && a.win) {
+    sink_end = min(a.n_sink, L);
+    r0 = max(a.n_sink, L - a.n_recent);
+    st_end = (sink_end + 31) >> 5;
+    kr = max(r0 >> 5, st_end);
+    nvt = st_end + max(nkb - kr, 0);
+  }
+  auto phys = [&](int u) { return (!RING && a.win && u >= st_end) ? kr + (u - st_end) : u; };
   const int kb0 = s * a.kb_per_split;
-  const int kb1 = min(kb0 + a.kb_per_split, nkb);
+  const int kb1 = min(kb0 + a.kb_per_split, nvt);
   asm volatile("" ::: "memory");
   // Loop over this wave's tiles.  K registers are refilled with the next tile as
   // soon as the S^T products have consumed them, V registers as soon as the PV
@@ -211,8 +227,14 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
     // unconditional (a wave without tiles loads a valid tile it never uses), so
     // that the Q stores below wait only for the Q loads
     const int kbl = kb < kb1 ? kb : 0;
-    const size_t tile = RING ? tile_index<RING>(a, b, g, kbl, ok)
-                             : tile_of_page(a, kb < kb1 ? page_first : 0, g, kbl, ok);
+    size_t tile;
+    if (RING) {
+      tile = tile_index<RING>(a, b, g, kbl, ok);
+    } else if (a.win) {   // the page of the first tile depends on L here
+      tile = tile_index<RING>(a, b, g, phys(kbl), ok);
+    } else {
+      tile = tile_of_page(a, kb < kb1 ? page_first : 0, g, kbl, ok);
+    }
     load_k<D, RING>(kt, a, tile, b, kbl, m, h);
     load_v<D>(vt, a, tile, m, h);
   }
@@ -250,7 +272,7 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
   bool mask_v = false;
   auto next_tile = [&]() {
     kbn = kb + 4;
-    tile_n = tile_index<RING>(a, b, g, kbn, ok_n);
+    tile_n = tile_index<RING>(a, b, g, phys(kbn), ok_n);
   };
   auto advance = [&]() {
     ok = ok_n;
@@ -258,15 +280,17 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
   };
   // S^T of tile kb, refill K (when there is a next tile), masked scores.
   auto scores_of = [&](auto has_next) {
-    keep = ok ? present_keys<D, RING>(kt, a, kb, L, T, h) : 0u;
+    const int pk = phys(kb);   // the tile's place in the sequence
+    keep = ok ? present_keys<D, RING>(kt, a, pk, L, T, h, sink_end, r0) : 0u;
     bool all_vis;
     if (RING) {
       all_vis = __all(keep == 0xFFFFu);
       mask_v = !all_vis;
     } else {
       // every key present and visible to every row (smallest causal limit L - n_q + 1)
-      all_vis = ok && (kb + 1) * 32 <= L - a.n_q + 1;
-      mask_v = !ok || (kb + 1) * 32 > L;
+      const bool in_set = !a.win || pk * 32 >= r0 || (pk + 1) * 32 <= sink_end;
+      all_vis = ok && in_set && (pk + 1) * 32 <= L - a.n_q + 1;
+      mask_v = !ok || !in_set || (pk + 1) * 32 > L;
     }
     f32x16 sacc[NB];
 #pragma unroll
@@ -278,7 +302,7 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
     if constexpr (decltype(has_next)::value) load_k<D, RING>(kt, a, tile_n, b, kbn, m, h);
 #pragma unroll
     for (int rb = 0; rb < NB; ++rb) {
-      const uint32_t vis = RING ? keep : keep & keys_below(lim[rb] - kb * 32, h);
+      const uint32_t vis = RING ? keep : keep & keys_below(lim[rb] - pk * 32, h);
       mx[rb] = masked_scores(x[rb], sacc[rb], vis, all_vis, a.scale_log2);
     }
   };

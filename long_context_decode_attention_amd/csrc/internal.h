@@ -27,7 +27,8 @@ struct AttnArgs {
   int items;                    // B * Hkv * nsplit
   int nrg;                      // row groups (16 * NRB rows each)
   int direct;                   // 1: write final o/lse, 0: write partials
-  int C, n_sink, n_recent;      // ring mode
+  int C, n_sink, n_recent;      // ring mode; paged mode with win: the key set
+  int win;                      // paged mode: 1 = keys [0, n_sink) and the last n_recent only
   float scale_log2;             // softmax_scale * log2(e)
 };
 

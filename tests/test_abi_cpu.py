@@ -119,6 +119,26 @@ def test_verify_and_window_argument_checks():
     assert win(D=96) == UNSUPPORTED
 
 
+def test_paged_window_argument_checks():
+    lib = _lib()
+    P = ctypes.c_void_p
+
+    def pw(**kw):
+        a = dict(B=1, Hq=32, Hkv=2, D=256, ns=4, nr=4092, q=FAKE, ws=None, ws_bytes=0, splits=0)
+        a.update(kw)
+        return lib.wmtp_draft_attn_window_paged(P(a["q"]), P(FAKE), P(FAKE), P(FAKE), P(FAKE),
+                                                a["B"], a["Hq"], a["Hkv"], a["D"], 16, 16, 1024,
+                                                a["ns"], a["nr"], 1.0, P(FAKE), None, P(a["ws"]),
+                                                a["ws_bytes"], a["splits"], 0, None)
+    assert pw(nr=0) == INVALID
+    assert pw(ns=-1) == INVALID
+    assert pw(q=None) == INVALID
+    assert pw(D=96) == UNSUPPORTED
+    assert pw(Hq=128, Hkv=2) == UNSUPPORTED              # 64 query rows per kv head
+    # 1024 keys in 16 splits need a workspace: none given
+    assert pw(splits=16) == WORKSPACE
+
+
 def test_append_and_combine_argument_checks():
     lib = _lib()
     P = ctypes.c_void_p
@@ -161,6 +181,14 @@ def test_plan_and_workspace_consistency():
     assert lib_mod.workspace_bytes(1, 32, 2, 256, 1, 100, 1, partials_only=True) > 0
     # the ring call plans with the ring's capacity
     assert lib_mod.plan_splits(1, 32, 2, 256, 1, 4096, ring=True) >= 1
+    # the truncated paged index plans for its window (4 + 4092 keys: at most 130 tiles
+    # per sequence), whatever the context; its workspace covers every context
+    wp = lib_mod.workspace_bytes(1, 32, 2, 256, 1, 4096, paged_window=True)
+    assert wp > 0
+    assert lib_mod.plan_splits(1, 32, 2, 256, 1, 4096, paged_window=True) <= 130 // 4 + 1
+    for keys in (1, 100, 4096, 4200, L):
+        # the call plans with min(window bound, max_keys) keys: never more splits
+        assert lib_mod.workspace_bytes(1, 32, 2, 256, 1, min(keys, 32 * 130)) <= wp
     with pytest.raises(lib_mod.WmtpError):
         lib_mod.plan_splits(1, 32, 3, 256, 1, L)
 

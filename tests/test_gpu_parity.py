@@ -47,13 +47,18 @@ def _draft_chain(sc: DraftScenario, num_splits=0, check_window=True):
         o_f, l_f = lib.draft_attn_full(qt, sc.kv.k, sc.kv.v, sc.kv.block_table, dev_i32(lens),
                                        max(lens), 1.0, num_splits=num_splits)
         o_w, l_w = lib.draft_attn_window(qt, sc.ring, 1.0, num_splits=num_splits)
+        o_p, l_p = lib.draft_attn_window_paged(qt, sc.kv.k, sc.kv.v, sc.kv.block_table,
+                                               dev_i32(lens), max(lens), cfg["n_sink"],
+                                               cfg["n_recent"], 1.0, num_splits=num_splits)
         torch().cuda.synchronize()
         for b in range(sc.B):
             of, lf = OA.draft_full(q[b], sc.K[b], sc.V[b], lens[b], 1.0)
             compare(o_f[b], l_f[b], of, lf, f"full b={b} step={j} L={lens[b]}")
+            ow, lw = OA.draft_window(q[b], sc.K[b], sc.V[b], lens[b], cfg["n_sink"],
+                                     cfg["n_recent"], 1.0)
+            # the truncated paged index reads the window's keys from the paged cache
+            compare(o_p[b], l_p[b], ow, lw, f"paged window b={b} step={j} L={lens[b]}")
             if check_window:
-                ow, lw = OA.draft_window(q[b], sc.K[b], sc.V[b], lens[b], cfg["n_sink"],
-                                         cfg["n_recent"], 1.0)
                 compare(o_w[b], l_w[b], ow, lw, f"window b={b} step={j} L={lens[b]}")
         res.append((o_f, l_f, o_w, l_w))
     return res
@@ -116,6 +121,24 @@ def test_draft_peaked_and_scaled():
     compare(o[0], l[0], of, lf, "peaked full")
     ow_ref, lw_ref = OA.draft_window(q[0], sc.K[0], sc.V[0], lens[0], 4, 4092, s)
     compare(ow[0], lw[0], ow_ref, lw_ref, "peaked window")
+
+
+@pytest.mark.parametrize("num_splits", [1, 3, 64])
+def test_paged_window_split_counts(num_splits):
+    """Truncated paged index with the sink tile and the recent tiles in one split,
+    in a few, and one tile per split; window 4 + 4092 over a 40000-key context."""
+    lib = _lib()
+    cfg = CFG["ctx1m_g32x2_d256"]
+    sc = DraftScenario(cfg, 12, [40000], 1)
+    sc.append(1)
+    q = sc.q(1)
+    lens = sc.lens(1)
+    o, l = lib.draft_attn_window_paged(dev_bf16(q), sc.kv.k, sc.kv.v, sc.kv.block_table,
+                                       dev_i32(lens), lens[0], cfg["n_sink"], cfg["n_recent"],
+                                       1.0, num_splits=num_splits)
+    torch().cuda.synchronize()
+    ow, lw = OA.draft_window(q[0], sc.K[0], sc.V[0], lens[0], cfg["n_sink"], cfg["n_recent"], 1.0)
+    compare(o[0], l[0], ow, lw, f"paged window num_splits={num_splits}")
 
 
 def test_window_equals_full_when_window_covers_context():
