@@ -130,9 +130,14 @@ def main() -> int:
     dkv = sc.alloc_paged_kv([S + d_extra], Hkv, D, W.page_permutation(seed, "draft_k", npd), dev)
     tkv = sc.alloc_paged_kv([S + t_extra], Hkv, D, W.page_permutation(seed, "target_k", npt), dev)
     ring = lib.new_ring(B, C, Hkv, D, n_sink, n_recent, dev)
+    # the draft context pass over a ring needs slack for its earlier queries'
+    # windows (n_q - 1 positions): a second ring with 64 more slots
+    n_ctx = gamma + 1
+    ring_c = lib.new_ring(B, C + 64, Hkv, D, n_sink, n_recent, dev)
     sc.fill_paged(dkv, 0, 0, Kd[:S], Vd[:S])
     sc.fill_paged(tkv, 0, 0, Kt[:S], Vt[:S])
     sc.fill_ring(ring, 0, Kd[:S], Vd[:S])
+    sc.fill_ring(ring_c, 0, Kd[:S], Vd[:S])
     # per-step inputs, resident on the device
     kd_new = sc.to_device_bf16(Kd[S:S + d_extra]).view(nsteps, gamma, 1, 1, Hkv, D)
     vd_new = sc.to_device_bf16(Vd[S:S + d_extra]).view(nsteps, gamma, 1, 1, Hkv, D)
@@ -143,6 +148,14 @@ def main() -> int:
     qd = sc.to_device_bf16(qd_host).view(nsteps, gamma, B, Hq, D)
     qv = sc.to_device_bf16(np.stack([W.queries(seed, "q_verify", (B, n_q, Hq), D, step=k)
                                      for k in range(nsteps)])).view(nsteps, B, n_q, Hq, D)
+    qc = sc.to_device_bf16(np.stack([W.queries(seed, "q_ctx", (B, n_ctx, Hq), D, step=k)
+                                     for k in range(nsteps)])).view(nsteps, B, n_ctx, Hq, D)
+    # K/V the context pass appends to its ring: the step's drafts and one more
+    # position (the bonus one; its values repeat the last draft's)
+    kc_new = torch.cat([kd_new.view(nsteps, gamma, Hkv, D), kd_new.view(nsteps, gamma, Hkv, D)[:, -1:]],
+                       1).view(nsteps, 1, n_ctx, Hkv, D).contiguous()
+    vc_new = torch.cat([vd_new.view(nsteps, gamma, Hkv, D), vd_new.view(nsteps, gamma, Hkv, D)[:, -1:]],
+                       1).view(nsteps, 1, n_ctx, Hkv, D).contiguous()
     # draft step j of bench step k appends position S + k*gamma + j - 1 and reads S + k*gamma + j keys
     d_pos = torch.tensor([[S + k * gamma + j for j in range(gamma)] for k in range(nsteps)],
                          dtype=torch.int32, device=dev).view(nsteps, gamma, 1)
@@ -167,6 +180,10 @@ def main() -> int:
     ws_f = lib.new_workspace(lib.workspace_bytes(B, Hq, Hkv, D, 1, max_d, args.num_splits,
                                                  partials_only=True), dev)
     ws_v = lib.new_workspace(lib.workspace_bytes(B, Hq, Hkv, D, n_q, max_t), dev)
+    o_c = torch.empty(B, n_ctx, Hq, D, device=dev)
+    l_c = torch.empty(B, n_ctx, Hq, device=dev)
+    ws_cw = lib.new_workspace(lib.workspace_bytes(B, Hq, Hkv, D, n_ctx, C + 64, ring=True), dev)
+    ws_cn = lib.new_workspace(lib.workspace_bytes(B, Hq, Hkv, D, n_ctx, max_d), dev)
     po, pl = lib.partials_view(ws_f, B, Hq, Hkv, D, 1, max_d, args.num_splits)
     splits_f = lib.plan_splits(B, Hq, Hkv, D, 1, max_d, args.num_splits)
     stream = torch.cuda.current_stream()
@@ -204,12 +221,19 @@ def main() -> int:
                                 prepare=True),
                lib.verify_attn(qv[k], tkv.k, tkv.v, tkv.block_table, t_len[k], max_t, 1.0, o_v,
                                l_v, ws_v, prepare=True))
-        plan.append((win, full, wpg, ver))
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6 + 2 * gamma)]
+        # draft context pass over the n_ctx accepted positions (here: every draft
+        # plus the bonus position): windowed over the slack ring, natively the
+        # causal verify kernel over the whole paged draft KV
+        ctx = (lib.ring_append(ring_c, kc_new[k], vc_new[k], prepare=True),
+               lib.draft_context_window(qc[k], ring_c, 1.0, o_c, l_c, ws_cw, prepare=True),
+               lib.verify_attn(qc[k], dkv.k, dkv.v, dkv.block_table, d_len[k, gamma - 1], max_d,
+                               1.0, o_c, l_c, ws_cn, prepare=True))
+        plan.append((win, full, wpg, ver, ctx))
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(9 + 2 * gamma)]
            for _ in range(nsteps)]
 
     def step(k):
-        win, full, wpg, ver = plan[k]
+        win, full, wpg, ver, ctx = plan[k]
         e = evs[k]
         e[0].record(stream)
         for c in win:                       # windowed arm: gamma x (ring append + attention)
@@ -229,8 +253,14 @@ def main() -> int:
         e[3].record(stream)
         ver[1]()                            # verify attention
         e[4].record(stream)
+        ctx[0]()                            # context pass, windowed: append + ring attention
+        ctx[1]()
+        e[6 + 2 * gamma].record(stream)
+        ctx[2]()                            # context pass, native: over all the draft KV
+        e[7 + 2 * gamma].record(stream)
         return {"t0": e[0], "t1": e[1], "t2": e[2], "p1": e[5 + 2 * gamma], "v0": e[3],
-                "t3": e[4], "attn": [(e[5 + 2 * j], e[6 + 2 * j]) for j in range(gamma)]}
+                "t3": e[4], "c1": e[6 + 2 * gamma], "c2": e[7 + 2 * gamma],
+                "attn": [(e[5 + 2 * j], e[6 + 2 * j]) for j in range(gamma)]}
 
     if args.copy_calibration:
         src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
@@ -257,6 +287,8 @@ def main() -> int:
     win_chain = np.median([us(m["t0"], m["t1"]) for m in marks])
     full_chain = np.median([us(m["t1"], m["t2"]) for m in marks])
     wpg_chain = np.median([us(m["t2"], m["p1"]) for m in marks])
+    ctx_win = np.median([us(m["t3"], m["c1"]) for m in marks])
+    ctx_full = np.median([us(m["c1"], m["c2"]) for m in marks])
     verify_us = np.median([us(m["p1"], m["t3"]) for m in marks])
     verify_kernel_us = np.median([us(m["v0"], m["t3"]) for m in marks])
     attn_us = np.array([us(a, b) for m in marks for (a, b) in m["attn"]])
@@ -306,6 +338,10 @@ def main() -> int:
                            "verify": round(float(verify_us), 2)},
         "cost_reduction": {"native_over_window_minus_1": round(float(up), 4),
                            "one_minus_window_over_native": round(float(down), 4)},
+        "draft_context_pass_us": {"queries": n_ctx, "window": round(float(ctx_win), 2),
+                                  "full": round(float(ctx_full), 2),
+                                  "decode_step_window_with_it": round(float(step_window + ctx_win), 2),
+                                  "decode_step_full_with_it": round(float(step_full + ctx_full), 2)},
         "hbm_gbs": {"full_draft_attention": round(achieved, 1), "verify": round(verify_gbs, 1),
                     "window_draft_step": round(win_bytes / (win_step_us * 1e-6) / 1e9, 1)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,

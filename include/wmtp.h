@@ -187,6 +187,28 @@ wmtp_status wmtp_draft_attn_window(const uint16_t* q, const uint16_t* ring_k,
                                    int num_splits, unsigned flags, void* stream);
 
 /*
+ * Draft context pass over the ring: the n_q positions the draft head
+ * processes after a verify (the accepted ones), each attending causally over
+ * its own window.  (Referee major comment on App. B / Eq. 1: the per-step cost
+ * has a draft context term besides the draft forwards; its native form reads
+ * the whole draft KV, which is wmtp_verify_attn over the paged draft cache.)
+ * Query i is position ring_T[b] - n_q + i and sees the positions p <= its own
+ * with p < n_sink or p > its own - n_recent.  The ring's slack must hold the
+ * earlier queries' windows: n_q - 1 <= C - n_sink - n_recent, else
+ * WMTP_ERR_INVALID_ARG.
+ *   q     bf16 [B][n_q][Hq][D]; o fp32 [B][n_q][Hq][D]; lse fp32 [B][n_q][Hq]
+ *   other arguments as wmtp_draft_attn_window; n_q * Hq / Hkv <= 256
+ * Workspace: wmtp_workspace_bytes(WMTP_CALL_RING, B, Hq, Hkv, D, n_q, C, ...).
+ */
+wmtp_status wmtp_draft_context_window(const uint16_t* q, const uint16_t* ring_k,
+                                      const uint16_t* ring_v, const int32_t* ring_pos,
+                                      const int64_t* ring_T, int B, int n_q, int Hq, int Hkv,
+                                      int D, int C, int n_sink, int n_recent,
+                                      float softmax_scale, float* o, float* lse, void* workspace,
+                                      size_t workspace_bytes, int num_splits, unsigned flags,
+                                      void* stream);
+
+/*
  * Append n_new consecutive positions to each request's draft ring.
  * (Referee minor comment on App. A: slot = ring_base(r) + logical_pos, with
  * slack beyond the window.)  Position p of request b goes to slot

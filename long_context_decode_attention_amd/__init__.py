@@ -26,7 +26,7 @@ FLAG_PARTIALS_ONLY = 1
 EXPORTS = (
     "wmtp_status_string", "wmtp_plan_splits", "wmtp_workspace_bytes",
     "wmtp_draft_attn_full", "wmtp_draft_attn_window", "wmtp_draft_attn_window_paged",
-    "wmtp_ring_append",
+    "wmtp_draft_context_window", "wmtp_ring_append",
     "wmtp_paged_append", "wmtp_verify_attn", "wmtp_split_combine",
 )
 
@@ -57,6 +57,7 @@ _SIGS = {
     "wmtp_draft_attn_full": ([_P] * 5 + [_I] * 7 + [_F, _P, _P, _P, _SZ, _I, _U, _P], _I),
     "wmtp_draft_attn_window": ([_P] * 5 + [_I] * 7 + [_F, _P, _P, _P, _SZ, _I, _U, _P], _I),
     "wmtp_draft_attn_window_paged": ([_P] * 5 + [_I] * 9 + [_F, _P, _P, _P, _SZ, _I, _U, _P], _I),
+    "wmtp_draft_context_window": ([_P] * 5 + [_I] * 8 + [_F, _P, _P, _P, _SZ, _I, _U, _P], _I),
     "wmtp_ring_append": ([_P] * 6 + [_I] * 6 + [_P], _I),
     "wmtp_paged_append": ([_P] * 6 + [_I] * 6 + [_P], _I),
     "wmtp_verify_attn": ([_P] * 5 + [_I] * 8 + [_F, _P, _P, _P, _SZ, _I, _U, _P], _I),
@@ -372,6 +373,34 @@ def draft_attn_window(q, ring: Ring, softmax_scale=1.0, o=None, lse=None, worksp
     c = _invoke("wmtp_draft_attn_window", (
         _ptr(q), _ptr(ring.k), _ptr(ring.v), _ptr(ring.pos), _ptr(ring.T),
         B, Hq, Hkv, D, C, ring.n_sink, ring.n_recent, float(softmax_scale),
+        _ptr(o), _ptr(lse), _ptr(workspace), workspace.numel(), int(num_splits),
+        FLAG_PARTIALS_ONLY if partials_only else 0, _stream(stream)), prepare)
+    if prepare:
+        return c
+    return workspace if partials_only else (o, lse)
+
+
+def draft_context_window(q, ring: Ring, softmax_scale=1.0, o=None, lse=None, workspace=None,
+                         num_splits=0, partials_only=False, stream=None, prepare=False):
+    """Draft context pass over the rings (``wmtp_draft_context_window``): q is
+    [B, n_q, Hq, D], query i at position ring.T - n_q + i, each over its own window."""
+    torch = _torch()
+    B, n_q, Hq, D = q.shape
+    Hkv, C = ring.Hkv, ring.C
+    _need(q, torch.bfloat16, None, "q")
+    _need(ring.k, torch.bfloat16, k_cache_shape(B * C // PAGE, Hkv, D), "ring.k")
+    _need(ring.v, torch.bfloat16, v_cache_shape(B * C // PAGE, Hkv, D), "ring.v")
+    _need(ring.pos, torch.int32, (B, C), "ring.pos")
+    _need(ring.T, torch.int64, (B,), "ring.T")
+    need = workspace_bytes(B, Hq, Hkv, D, n_q, C, num_splits, partials_only, ring=True)
+    if workspace is None:
+        workspace = new_workspace(need, q.device)
+    _need(workspace, torch.uint8, None, "workspace")
+    if not partials_only:
+        o, lse = _outputs(o, lse, (B, n_q, Hq, D), (B, n_q, Hq), q.device)
+    c = _invoke("wmtp_draft_context_window", (
+        _ptr(q), _ptr(ring.k), _ptr(ring.v), _ptr(ring.pos), _ptr(ring.T),
+        B, n_q, Hq, Hkv, D, C, ring.n_sink, ring.n_recent, float(softmax_scale),
         _ptr(o), _ptr(lse), _ptr(workspace), workspace.numel(), int(num_splits),
         FLAG_PARTIALS_ONLY if partials_only else 0, _stream(stream)), prepare)
     if prepare:

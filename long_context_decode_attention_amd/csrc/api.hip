@@ -216,18 +216,22 @@ wmtp_status wmtp_verify_attn(const uint16_t* q, const uint16_t* k_cache, const u
                          workspace_bytes, num_splits, flags, stream);
 }
 
-wmtp_status wmtp_draft_attn_window(const uint16_t* q, const uint16_t* ring_k,
-                                   const uint16_t* ring_v, const int32_t* ring_pos,
-                                   const int64_t* ring_T, int B, int Hq, int Hkv, int D, int C,
-                                   int n_sink, int n_recent, float softmax_scale, float* o,
-                                   float* lse, void* workspace, size_t workspace_bytes,
-                                   int num_splits, unsigned flags, void* stream) {
-  if (!attn_dims_ok(B, Hq, Hkv, D)) return WMTP_ERR_INVALID_ARG;
+// The ring calls: n_q = 1 (a draft step) or the n_q positions of a draft
+// context pass, query i at position ring_T - n_q + i.
+static wmtp_status ring_attention(const uint16_t* q, const uint16_t* ring_k,
+                                  const uint16_t* ring_v, const int32_t* ring_pos,
+                                  const int64_t* ring_T, int B, int n_q, int Hq, int Hkv, int D,
+                                  int C, int n_sink, int n_recent, float softmax_scale, float* o,
+                                  float* lse, void* workspace, size_t workspace_bytes,
+                                  int num_splits, unsigned flags, void* stream) {
+  if (!attn_dims_ok(B, Hq, Hkv, D) || n_q < 1) return WMTP_ERR_INVALID_ARG;
   if (!head_dim_ok(D)) return WMTP_ERR_UNSUPPORTED;
-  if (Hq / Hkv > 256) return WMTP_ERR_UNSUPPORTED;
+  if ((long)n_q * (Hq / Hkv) > 256) return WMTP_ERR_UNSUPPORTED;
   if (C < 64 || C % 64 != 0 || n_sink < 0 || n_sink >= C || n_recent < 1 ||
       n_recent > C - n_sink || num_splits < 0)
     return WMTP_ERR_INVALID_ARG;
+  // the earliest query's window must still be in the ring: slack >= n_q - 1
+  if (n_q - 1 > C - n_sink - n_recent) return WMTP_ERR_INVALID_ARG;
   if ((long)B * C > (long)INT_MAX) return WMTP_ERR_INVALID_ARG;
   if ((flags & ~WMTP_FLAG_PARTIALS_ONLY) != 0) return WMTP_ERR_INVALID_ARG;
   // the kernels take row maxima of raw scores before scaling: the scale must be positive
@@ -246,7 +250,7 @@ wmtp_status wmtp_draft_attn_window(const uint16_t* q, const uint16_t* ring_k,
   a.B = B;
   a.Hq = Hq;
   a.Hkv = Hkv;
-  a.n_q = 1;
+  a.n_q = n_q;
   a.D = D;
   a.num_pages = B * (C / 64);
   a.max_pages = C / 64;
@@ -256,6 +260,29 @@ wmtp_status wmtp_draft_attn_window(const uint16_t* q, const uint16_t* ring_k,
   a.scale_log2 = softmax_scale * kLog2e;
   return run_attention(a, true, C, C, o, lse, workspace, workspace_bytes, num_splits, flags,
                        static_cast<hipStream_t>(stream));
+}
+
+wmtp_status wmtp_draft_attn_window(const uint16_t* q, const uint16_t* ring_k,
+                                   const uint16_t* ring_v, const int32_t* ring_pos,
+                                   const int64_t* ring_T, int B, int Hq, int Hkv, int D, int C,
+                                   int n_sink, int n_recent, float softmax_scale, float* o,
+                                   float* lse, void* workspace, size_t workspace_bytes,
+                                   int num_splits, unsigned flags, void* stream) {
+  return ring_attention(q, ring_k, ring_v, ring_pos, ring_T, B, 1, Hq, Hkv, D, C, n_sink,
+                        n_recent, softmax_scale, o, lse, workspace, workspace_bytes, num_splits,
+                        flags, stream);
+}
+
+wmtp_status wmtp_draft_context_window(const uint16_t* q, const uint16_t* ring_k,
+                                      const uint16_t* ring_v, const int32_t* ring_pos,
+                                      const int64_t* ring_T, int B, int n_q, int Hq, int Hkv,
+                                      int D, int C, int n_sink, int n_recent,
+                                      float softmax_scale, float* o, float* lse, void* workspace,
+                                      size_t workspace_bytes, int num_splits, unsigned flags,
+                                      void* stream) {
+  return ring_attention(q, ring_k, ring_v, ring_pos, ring_T, B, n_q, Hq, Hkv, D, C, n_sink,
+                        n_recent, softmax_scale, o, lse, workspace, workspace_bytes, num_splits,
+                        flags, stream);
 }
 
 wmtp_status wmtp_ring_append(uint16_t* ring_k, uint16_t* ring_v, int32_t* ring_pos,

@@ -118,7 +118,9 @@ __device__ __forceinline__ uint32_t present_keys(const KTile<D, RING>& t, const 
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int p = t.pos[i];
-      const bool ok = p >= 0 && p < T && (p < a.n_sink || p >= T - a.n_recent);
+      // in the window of some query: the last n_q positions T - n_q .. T - 1 each
+      // see the sink and their own last n_recent positions
+      const bool ok = p >= 0 && p < T && (p < a.n_sink || p >= T - (a.n_q - 1) - a.n_recent);
       keep |= (ok ? 1u : 0u) << i;
     }
     return keep;
@@ -251,7 +253,11 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
 #pragma unroll
   for (int rb = 0; rb < NB; ++rb) {
     const int row = row0 + rb * 32 + m;
-    lim[rb] = (row < a.R && !RING) ? L - a.n_q + row / a.G + 1 : L;
+    // paged: keys visible to the row (causal limit); ring: the row's query position
+    if (RING)
+      lim[rb] = T - a.n_q + (row < a.R ? row / a.G : a.n_q - 1);
+    else
+      lim[rb] = row < a.R ? L - a.n_q + row / a.G + 1 : L;
   }
 
   SoftmaxState<D, NB> st;
@@ -283,9 +289,26 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
     const int pk = phys(kb);   // the tile's place in the sequence
     keep = ok ? present_keys<D, RING>(kt, a, pk, L, T, h, sink_end, r0) : 0u;
     bool all_vis;
+    uint32_t rvis[NB];   // ring, several queries: the keys in each row's own window
     if (RING) {
-      all_vis = __all(keep == 0xFFFFu);
-      mask_v = !all_vis;
+      mask_v = !__all(keep == 0xFFFFu);
+      bool rows_all = true;
+#pragma unroll
+      for (int rb = 0; rb < NB; ++rb) {
+        rvis[rb] = keep;
+        if (a.n_q > 1) {
+          const int pq = lim[rb];
+          uint32_t v = 0;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int p = kt.pos[i];
+            v |= (p <= pq && (p < a.n_sink || p > pq - a.n_recent) ? 1u : 0u) << i;
+          }
+          rvis[rb] &= v;
+        }
+        rows_all = rows_all && rvis[rb] == 0xFFFFu;
+      }
+      all_vis = __all(rows_all);
     } else {
       // every key present and visible to every row (smallest causal limit L - n_q + 1)
       const bool in_set = !a.win || pk * 32 >= r0 || (pk + 1) * 32 <= sink_end;
@@ -302,7 +325,7 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
     if constexpr (decltype(has_next)::value) load_k<D, RING>(kt, a, tile_n, b, kbn, m, h);
 #pragma unroll
     for (int rb = 0; rb < NB; ++rb) {
-      const uint32_t vis = RING ? keep : keep & keys_below(lim[rb] - pk * 32, h);
+      const uint32_t vis = RING ? rvis[rb] : keep & keys_below(lim[rb] - pk * 32, h);
       mx[rb] = masked_scores(x[rb], sacc[rb], vis, all_vis, a.scale_log2);
     }
   };

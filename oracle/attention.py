@@ -34,6 +34,11 @@ Readings taken where the pages are silent (each listed in the design notes):
   keys (the position appended at that step included);
 * verify query ``i`` of ``n_q`` (0-based) sees the first ``L - n_q + i + 1``
   keys, where ``L`` already counts the ``n_q`` appended positions;
+* the draft context pass (the draft head over the accepted positions, the
+  draft-context term of the step cost in [VERDICT] referee report, major
+  comment on Eq. 1) is causal like the verify: its query ``i`` sits at position
+  ``L - n_q + i``; natively it reads every earlier draft key, windowed it reads
+  the window of its own position, ``window_positions(L - n_q + i + 1, ...)``;
 * ``lse`` is the natural-log log-sum-exp of the scaled logits.
 """
 
@@ -167,6 +172,24 @@ def verify(q, K, V, L: int, scale: float):
     lse = np.zeros(q.shape[:2])
     for i in range(n_q):
         o[i], lse[i] = draft_over(q[i], K, V, np.arange(L - n_q + i + 1), scale)
+    return o, lse
+
+
+def draft_context_window(q, K, V, L: int, n_sink: int, n_recent: int, scale: float):
+    """Windowed draft context pass: ``n_q`` causal queries over the draft KV, query
+    ``i`` (position ``L - n_q + i``) over the window of its own position.
+
+    q [n_q, Hq, D]; K, V [>= L, Hkv, D].  The native form is ``verify`` over the
+    draft KV.  Returns (o [n_q, Hq, D], lse [n_q, Hq]).
+    """
+    q = np.asarray(q)
+    n_q = q.shape[0]
+    if L < n_q:
+        raise ValueError("L must count the n_q positions of the pass")
+    o = np.zeros(q.shape[:2] + (V.shape[2],))
+    lse = np.zeros(q.shape[:2])
+    for i in range(n_q):
+        o[i], lse[i] = draft_window(q[i], K, V, L - n_q + i + 1, n_sink, n_recent, scale)
     return o, lse
 
 

@@ -141,6 +141,48 @@ def test_paged_window_split_counts(num_splits):
     compare(o[0], l[0], ow, lw, f"paged window num_splits={num_splits}")
 
 
+@pytest.mark.parametrize("cfg_name,C,n_sink,n_recent,L,n_q", [
+    ("ctx1m_g32x2_d256", 4160, 4, 4092, 6000, 8),      # 128 query rows, ring wrapped
+    ("ctx128k_g32x4_d128", 4160, 4, 4092, 3000, 4),    # ring not yet full
+    ("nope8l_1m_g64x2_d128", 128, 4, 60, 1000, 8),     # 256 rows; small window, many wraps
+])
+def test_draft_context_pass_over_the_ring(cfg_name, C, n_sink, n_recent, L, n_q):
+    """Draft context pass: n_q causal queries, each over the window of its own
+    position, read from a ring whose slack (C - n_sink - n_recent >= n_q - 1)
+    still holds the earliest query's window."""
+    lib = _lib()
+    from long_context_decode_attention_amd import scenario as scn
+    cfg = CFG[cfg_name]
+    Hq, Hkv, D = cfg["Hq"], cfg["Hkv"], cfg["D"]
+    seed = 70 + n_q
+    K = W.kv_positions(seed, "draft_k", 0, 0, L, Hkv, D)
+    V = W.kv_positions(seed, "draft_v", 0, 0, L, Hkv, D)
+    ring = lib.new_ring(1, C, Hkv, D, n_sink, n_recent)
+    scn.poison(ring.k)
+    scn.poison(ring.v)
+    scn.fill_ring(ring, 0, K, V)
+    q = W.queries(seed, "q_ctx", (1, n_q, Hq), D)
+    o, l = lib.draft_context_window(dev_bf16(q), ring, 1.0)
+    torch().cuda.synchronize()
+    ro, rl = OA.draft_context_window(q[0], K, V, L, n_sink, n_recent, 1.0)
+    compare(o[0], l[0], ro, rl, f"context pass {cfg_name} n_q={n_q}")
+    # one query is a draft step: the same as the windowed draft call
+    o1, l1 = lib.draft_context_window(dev_bf16(q[:, -1:]), ring, 1.0)
+    ow, lw = lib.draft_attn_window(dev_bf16(q[:, -1]), ring, 1.0)
+    torch().cuda.synchronize()
+    assert torch().equal(o1[:, 0], ow) and torch().equal(l1[:, 0], lw)
+
+
+def test_draft_context_pass_needs_slack():
+    """Without slack for the earlier queries' windows the call is refused."""
+    lib = _lib()
+    cfg = CFG["ctx1m_g32x2_d256"]
+    ring = lib.new_ring(1, 4096, cfg["Hkv"], cfg["D"], 4, 4092)
+    q = dev_bf16(W.queries(3, "q_ctx", (1, 2, cfg["Hq"]), cfg["D"]))
+    with pytest.raises(lib.WmtpError):
+        lib.draft_context_window(q, ring, 1.0)
+
+
 def test_window_equals_full_when_window_covers_context():
     cfg = CFG["ctx128k_g32x4_d128"]
     sc = DraftScenario(cfg, 7, [3000], 1)

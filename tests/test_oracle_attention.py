@@ -232,6 +232,53 @@ def test_verify_query_i_sees_its_causal_prefix():
     assert np.max(np.abs(ov[0] - of_all)) > 1e-6
 
 
+def test_context_window_covering_everything_is_the_causal_verify():
+    """A window that covers the whole context turns the windowed draft context
+    pass into the native one, which is the causal verify over the draft KV."""
+    rng = np.random.default_rng(11)
+    S, n_q, Hq, Hkv, D = 50, 6, 4, 2, 8
+    L = S + n_q
+    q = _bf16(rng, n_q, Hq, D)
+    K, V = _kv(rng, L, Hkv, D)
+    oc, lc = A.draft_context_window(q, K, V, L, 4, L, 0.5)
+    ov, lv = A.verify(q, K, V, L, 0.5)
+    assert np.allclose(oc, ov, rtol=0, atol=1e-13) and np.allclose(lc, lv, rtol=0, atol=1e-13)
+
+
+def test_context_window_of_one_recent_key_returns_that_key():
+    """No sink and a one-key window: query i sees only its own position, so its
+    output is that key's value and its lse that key's logit (a closed form)."""
+    rng = np.random.default_rng(12)
+    S, n_q, Hq, Hkv, D = 30, 4, 4, 2, 8
+    L = S + n_q
+    q = _bf16(rng, n_q, Hq, D)
+    K, V = _kv(rng, L, Hkv, D)
+    Kf, Vf, qf = A.widen_bf16(K), A.widen_bf16(V), A.widen_bf16(q)
+    oc, lc = A.draft_context_window(q, K, V, L, 0, 1, 0.25)
+    G = Hq // Hkv
+    for i in range(n_q):
+        p = S + i
+        for h in range(Hq):
+            assert np.array_equal(oc[i, h], Vf[p, h // G])
+            assert abs(lc[i, h] - 0.25 * float(qf[i, h] @ Kf[p, h // G])) < 1e-12
+
+
+def test_context_window_queries_have_different_windows():
+    """With sink 2 and window 5, query 0 still sees position S - 4, which the last
+    query's window has left; one dominant value there moves query 0 only."""
+    rng = np.random.default_rng(13)
+    S, n_q, Hq, Hkv, D = 40, 4, 2, 1, 8
+    L = S + n_q
+    q = _bf16(rng, n_q, Hq, D)
+    K, V = _kv(rng, L, Hkv, D)
+    base, _ = A.draft_context_window(q, K, V, L, 2, 5, 1.0)
+    V2 = A.widen_bf16(V).copy()
+    V2[S - 4] += 100.0
+    moved, _ = A.draft_context_window(q, K, V2, L, 2, 5, 1.0)
+    assert np.max(np.abs(moved[0] - base[0])) > 1e-3
+    assert np.array_equal(moved[n_q - 1], base[n_q - 1])
+
+
 @pytest.mark.parametrize("cuts", [[0, 100], [0, 1, 100], [0, 37, 38, 64, 100], [0, 50, 50, 100]])
 def test_combine_reproduces_attention_over_union(cuts):
     rng = np.random.default_rng(len(cuts))

@@ -31,7 +31,7 @@ PAGE = 64
 TENSORS = {
     "draft_k": 11, "draft_v": 12,        # the draft head's own KV (native arm reads all of it)
     "target_k": 21, "target_v": 22,      # the target's KV (verify reads all of it)
-    "q_draft": 31, "q_verify": 32,
+    "q_draft": 31, "q_verify": 32, "q_ctx": 33,   # q_ctx: the draft context pass
     "perm": 41, "lens": 42, "misc": 51,
 }
 
