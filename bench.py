@@ -42,7 +42,7 @@ WORKLOAD = "ctx1m_g32x2_d256"
 # keyed by a hash of the sources that kernel is built from: a changed kernel
 # reports null until it is measured again.
 MEASURED_TRAFFIC = {
-    "f1f786c596df34c5": {"read": 2.148e9, "write": 4.211e6, "keys": 1048587},
+    "e1bd98330e62fb57": {"read": 2.148e9, "write": 4.211e6, "keys": 1048587},
 }
 KERNEL_SOURCES = ("csrc/attn.hip", "csrc/attn_device.h", "csrc/common.h")
 
@@ -184,6 +184,18 @@ def main() -> int:
     l_c = torch.empty(B, n_ctx, Hq, device=dev)
     ws_cw = lib.new_workspace(lib.workspace_bytes(B, Hq, Hkv, D, n_ctx, C + 64, ring=True), dev)
     ws_cn = lib.new_workspace(lib.workspace_bytes(B, Hq, Hkv, D, n_ctx, max_d), dev)
+    # tree-shaped proposals of the same size for the tree verify: a binary tree
+    # (node i's parent (i - 1) // 2), mask bit a = node a is an ancestor or itself
+    tree = []
+    for i in range(n_q):
+        mk, j = 0, i
+        while True:
+            mk |= 1 << j
+            if j == 0:
+                break
+            j = (j - 1) // 2
+        tree.append(mk)
+    tree_mask = torch.tensor([tree] * B, dtype=torch.int64, device=dev)
     po, pl = lib.partials_view(ws_f, B, Hq, Hkv, D, 1, max_d, args.num_splits)
     splits_f = lib.plan_splits(B, Hq, Hkv, D, 1, max_d, args.num_splits)
     stream = torch.cuda.current_stream()
@@ -227,9 +239,11 @@ def main() -> int:
         ctx = (lib.ring_append(ring_c, kc_new[k], vc_new[k], prepare=True),
                lib.draft_context_window(qc[k], ring_c, 1.0, o_c, l_c, ws_cw, prepare=True),
                lib.verify_attn(qc[k], dkv.k, dkv.v, dkv.block_table, d_len[k, gamma - 1], max_d,
-                               1.0, o_c, l_c, ws_cn, prepare=True))
+                               1.0, o_c, l_c, ws_cn, prepare=True),
+               lib.verify_attn_tree(qv[k], tkv.k, tkv.v, tkv.block_table, t_len[k], tree_mask,
+                                    max_t, 1.0, o_v, l_v, ws_v, prepare=True))
         plan.append((win, full, wpg, ver, ctx))
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(9 + 2 * gamma)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(10 + 2 * gamma)]
            for _ in range(nsteps)]
 
     def step(k):
@@ -258,8 +272,11 @@ def main() -> int:
         e[6 + 2 * gamma].record(stream)
         ctx[2]()                            # context pass, native: over all the draft KV
         e[7 + 2 * gamma].record(stream)
+        ctx[3]()                            # the verify for a tree of proposals
+        e[8 + 2 * gamma].record(stream)
         return {"t0": e[0], "t1": e[1], "t2": e[2], "p1": e[5 + 2 * gamma], "v0": e[3],
                 "t3": e[4], "c1": e[6 + 2 * gamma], "c2": e[7 + 2 * gamma],
+                "c3": e[8 + 2 * gamma],
                 "attn": [(e[5 + 2 * j], e[6 + 2 * j]) for j in range(gamma)]}
 
     if args.copy_calibration:
@@ -289,6 +306,7 @@ def main() -> int:
     wpg_chain = np.median([us(m["t2"], m["p1"]) for m in marks])
     ctx_win = np.median([us(m["t3"], m["c1"]) for m in marks])
     ctx_full = np.median([us(m["c1"], m["c2"]) for m in marks])
+    tree_us = np.median([us(m["c2"], m["c3"]) for m in marks])
     verify_us = np.median([us(m["p1"], m["t3"]) for m in marks])
     verify_kernel_us = np.median([us(m["v0"], m["t3"]) for m in marks])
     attn_us = np.array([us(a, b) for m in marks for (a, b) in m["attn"]])
@@ -335,7 +353,9 @@ def main() -> int:
                                    "full_attention_kernel": round(attn_mean, 2)},
         "decode_step_us": {"full": round(float(step_full), 2), "window": round(float(step_window), 2),
                            "window_paged_index": round(float(verify_us + wpg_chain), 2),
-                           "verify": round(float(verify_us), 2)},
+                           "verify": round(float(verify_us), 2),
+                           "verify_kernel": round(float(verify_kernel_us), 2),
+                           "verify_tree_kernel": round(float(tree_us), 2)},
         "cost_reduction": {"native_over_window_minus_1": round(float(up), 4),
                            "one_minus_window_over_native": round(float(down), 4)},
         "draft_context_pass_us": {"queries": n_ctx, "window": round(float(ctx_win), 2),

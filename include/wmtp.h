@@ -140,6 +140,26 @@ wmtp_status wmtp_draft_attn_full(const uint16_t* q, const uint16_t* k_cache,
                                  void* stream);
 
 /*
+ * Verify of a tree of proposals: as wmtp_verify_attn, but the n_q appended
+ * positions form a tree instead of a chain.  (Verdict page, forward
+ * implications: the window composes with tree-shaped speculation.)  Query i
+ * sees every key before the appended positions and the appended position
+ * L_b - n_q + a exactly when bit a of tree_mask[b * n_q + i] is set (its
+ * ancestors and itself; the causal verify is mask_i = 2^(i+1) - 1).
+ *   tree_mask  uint64 [B][n_q] (device, 8-byte aligned); bits >= n_q ignored
+ *   n_q        1 .. 64
+ *   other arguments and the workspace as wmtp_verify_attn
+ * A query that sees no key gets o = 0 and lse = -inf.
+ */
+wmtp_status wmtp_verify_attn_tree(const uint16_t* q, const uint16_t* k_cache,
+                                  const uint16_t* v_cache, const int32_t* block_table,
+                                  const int32_t* seq_lens, const uint64_t* tree_mask, int B,
+                                  int n_q, int Hq, int Hkv, int D, int num_pages, int max_pages,
+                                  int max_seq_len, float softmax_scale, float* o, float* lse,
+                                  void* workspace, size_t workspace_bytes, int num_splits,
+                                  unsigned flags, void* stream);
+
+/*
  * Windowed draft attention over the paged draft KV by index truncation: the
  * same key set as wmtp_draft_attn_window, read straight from the paged cache
  * instead of from a compact ring.  (Verdict page, key machinery: the draft

@@ -26,7 +26,7 @@ FLAG_PARTIALS_ONLY = 1
 EXPORTS = (
     "wmtp_status_string", "wmtp_plan_splits", "wmtp_workspace_bytes",
     "wmtp_draft_attn_full", "wmtp_draft_attn_window", "wmtp_draft_attn_window_paged",
-    "wmtp_draft_context_window", "wmtp_ring_append",
+    "wmtp_draft_context_window", "wmtp_verify_attn_tree", "wmtp_ring_append",
     "wmtp_paged_append", "wmtp_verify_attn", "wmtp_split_combine",
 )
 
@@ -58,6 +58,7 @@ _SIGS = {
     "wmtp_draft_attn_window": ([_P] * 5 + [_I] * 7 + [_F, _P, _P, _P, _SZ, _I, _U, _P], _I),
     "wmtp_draft_attn_window_paged": ([_P] * 5 + [_I] * 9 + [_F, _P, _P, _P, _SZ, _I, _U, _P], _I),
     "wmtp_draft_context_window": ([_P] * 5 + [_I] * 8 + [_F, _P, _P, _P, _SZ, _I, _U, _P], _I),
+    "wmtp_verify_attn_tree": ([_P] * 6 + [_I] * 8 + [_F, _P, _P, _P, _SZ, _I, _U, _P], _I),
     "wmtp_ring_append": ([_P] * 6 + [_I] * 6 + [_P], _I),
     "wmtp_paged_append": ([_P] * 6 + [_I] * 6 + [_P], _I),
     "wmtp_verify_attn": ([_P] * 5 + [_I] * 8 + [_F, _P, _P, _P, _SZ, _I, _U, _P], _I),
@@ -285,6 +286,38 @@ def draft_attn_full(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, sof
     c = _invoke("wmtp_draft_attn_full", (
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
         B, Hq, Hkv, D, num_pages, max_pages, int(max_seq_len), float(softmax_scale),
+        _ptr(o), _ptr(lse), _ptr(workspace), workspace.numel(), int(num_splits),
+        FLAG_PARTIALS_ONLY if partials_only else 0, _stream(stream)), prepare)
+    if prepare:
+        return c
+    return workspace if partials_only else (o, lse)
+
+
+def verify_attn_tree(q, k_cache, v_cache, block_table, seq_lens, tree_mask, max_seq_len,
+                     softmax_scale=1.0, o=None, lse=None, workspace=None, num_splits=0,
+                     partials_only=False, stream=None, prepare=False):
+    """Verify of a tree of proposals (``wmtp_verify_attn_tree``): q is [B, n_q, Hq, D];
+    tree_mask int64 [B, n_q], bit a of row i set when query i sees appended position a."""
+    torch = _torch()
+    B, n_q, Hq, D = q.shape
+    num_pages, Hkv = k_cache.shape[0], k_cache.shape[1]
+    max_pages = block_table.shape[1]
+    _need(q, torch.bfloat16, None, "q")
+    _need(k_cache, torch.bfloat16, k_cache_shape(num_pages, Hkv, D), "k_cache")
+    _need(v_cache, torch.bfloat16, v_cache_shape(num_pages, Hkv, D), "v_cache")
+    _need(block_table, torch.int32, (B, max_pages), "block_table")
+    _need(seq_lens, torch.int32, (B,), "seq_lens")
+    _need(tree_mask, torch.int64, (B, n_q), "tree_mask")
+    max_keys = min(int(max_seq_len), max_pages * PAGE)
+    need = workspace_bytes(B, Hq, Hkv, D, n_q, max_keys, num_splits, partials_only)
+    if workspace is None:
+        workspace = new_workspace(need, q.device)
+    _need(workspace, torch.uint8, None, "workspace")
+    if not partials_only:
+        o, lse = _outputs(o, lse, (B, n_q, Hq, D), (B, n_q, Hq), q.device)
+    c = _invoke("wmtp_verify_attn_tree", (
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens), _ptr(tree_mask),
+        B, n_q, Hq, Hkv, D, num_pages, max_pages, int(max_seq_len), float(softmax_scale),
         _ptr(o), _ptr(lse), _ptr(workspace), workspace.numel(), int(num_splits),
         FLAG_PARTIALS_ONLY if partials_only else 0, _stream(stream)), prepare)
     if prepare:

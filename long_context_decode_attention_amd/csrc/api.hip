@@ -139,7 +139,7 @@ static wmtp_status paged_attention(const uint16_t* q, const uint16_t* k_cache,
                                    float softmax_scale, float* o, float* lse, void* workspace,
                                    size_t workspace_bytes, int num_splits, unsigned flags,
                                    void* stream, bool win = false, int n_sink = 0,
-                                   int n_recent = 0) {
+                                   int n_recent = 0, const uint64_t* tree_mask = nullptr) {
   if (!attn_dims_ok(B, Hq, Hkv, D) || n_q < 1) return WMTP_ERR_INVALID_ARG;
   if (!head_dim_ok(D)) return WMTP_ERR_UNSUPPORTED;
   if (n_q * (Hq / Hkv) > 256) return WMTP_ERR_UNSUPPORTED;
@@ -169,6 +169,7 @@ static wmtp_status paged_attention(const uint16_t* q, const uint16_t* k_cache,
   a.num_pages = num_pages;
   a.max_pages = max_pages;
   a.scale_log2 = softmax_scale * kLog2e;
+  a.tree_mask = tree_mask;
   int plan_keys = max_keys;
   if (win) {
     if (n_sink < 0 || n_recent < 1) return WMTP_ERR_INVALID_ARG;
@@ -260,6 +261,19 @@ static wmtp_status ring_attention(const uint16_t* q, const uint16_t* ring_k,
   a.scale_log2 = softmax_scale * kLog2e;
   return run_attention(a, true, C, C, o, lse, workspace, workspace_bytes, num_splits, flags,
                        static_cast<hipStream_t>(stream));
+}
+
+wmtp_status wmtp_verify_attn_tree(const uint16_t* q, const uint16_t* k_cache,
+                                  const uint16_t* v_cache, const int32_t* block_table,
+                                  const int32_t* seq_lens, const uint64_t* tree_mask, int B,
+                                  int n_q, int Hq, int Hkv, int D, int num_pages, int max_pages,
+                                  int max_seq_len, float softmax_scale, float* o, float* lse,
+                                  void* workspace, size_t workspace_bytes, int num_splits,
+                                  unsigned flags, void* stream) {
+  if (!tree_mask || !aligned8(tree_mask) || n_q < 1 || n_q > 64) return WMTP_ERR_INVALID_ARG;
+  return paged_attention(q, k_cache, v_cache, block_table, seq_lens, B, n_q, Hq, Hkv, D,
+                         num_pages, max_pages, max_seq_len, softmax_scale, o, lse, workspace,
+                         workspace_bytes, num_splits, flags, stream, false, 0, 0, tree_mask);
 }
 
 wmtp_status wmtp_draft_attn_window(const uint16_t* q, const uint16_t* ring_k,

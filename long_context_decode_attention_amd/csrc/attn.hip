@@ -259,6 +259,13 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
     else
       lim[rb] = row < a.R ? L - a.n_q + row / a.G + 1 : L;
   }
+  // tree verify: each row's ancestor mask over the appended positions
+  uint64_t tmask[NB];
+#pragma unroll
+  for (int rb = 0; rb < NB; ++rb) {
+    const int row = row0 + rb * 32 + m;
+    tmask[rb] = (!RING && a.tree_mask && row < a.R) ? a.tree_mask[(size_t)b * a.n_q + row / a.G] : 0;
+  }
 
   SoftmaxState<D, NB> st;
 #pragma unroll
@@ -312,7 +319,8 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
     } else {
       // every key present and visible to every row (smallest causal limit L - n_q + 1)
       const bool in_set = !a.win || pk * 32 >= r0 || (pk + 1) * 32 <= sink_end;
-      all_vis = ok && in_set && (pk + 1) * 32 <= L - a.n_q + 1;
+      // (a tree's first appended position need not be visible to every row)
+      all_vis = ok && in_set && (pk + 1) * 32 <= L - a.n_q + (a.tree_mask ? 0 : 1);
       mask_v = !ok || !in_set || (pk + 1) * 32 > L;
     }
     f32x16 sacc[NB];
@@ -325,7 +333,14 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
     if constexpr (decltype(has_next)::value) load_k<D, RING>(kt, a, tile_n, b, kbn, m, h);
 #pragma unroll
     for (int rb = 0; rb < NB; ++rb) {
-      const uint32_t vis = RING ? rvis[rb] : keep & keys_below(lim[rb] - pk * 32, h);
+      uint32_t vis;
+      if (RING)
+        vis = rvis[rb];
+      else if (a.tree_mask)
+        vis = keep & (keys_below(L - a.n_q - pk * 32, h) |
+                      tree_keys(tmask[rb], pk * 32 - (L - a.n_q), h));
+      else
+        vis = keep & keys_below(lim[rb] - pk * 32, h);
       mx[rb] = masked_scores(x[rb], sacc[rb], vis, all_vis, a.scale_log2);
     }
   };

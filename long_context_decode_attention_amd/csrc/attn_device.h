@@ -71,6 +71,21 @@ __device__ __forceinline__ uint32_t keys_below(int count, int h) {
 __device__ __forceinline__ float max_over_row(float v) { return fmaxf(v, __shfl_xor(v, 32)); }
 __device__ __forceinline__ float sum_over_row(float v) { return v + __shfl_xor(v, 32); }
 
+// Verify under a tree of proposals: of this lane's 16 keys, which are appended
+// positions that `mask` marks (bit a: the appended position a, 0 <= a < 64).
+// rel0 is the appended index of the tile's key 0 (negative when the tile starts
+// before the appended positions).
+__device__ __forceinline__ uint32_t tree_keys(uint64_t mask, int rel0, int h) {
+  uint32_t bits = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int a = rel0 + (i < 8 ? 8 * h + i : 16 + 8 * h + (i - 8));
+    const bool on = a >= 0 && a < 64 && ((mask >> (a & 63)) & 1u);
+    bits |= (on ? 1u : 0u) << i;
+  }
+  return bits;
+}
+
 // Online softmax in log2 units: scores x = s * c with c = scale * log2(e) > 0,
 // weights p = exp2(x - m).  The running maximum m of a row (the same on its two
 // lanes) is raised lazily, only when a score exceeds it by more than kLazyMax.

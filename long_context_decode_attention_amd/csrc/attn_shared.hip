@@ -262,7 +262,8 @@ __device__ __forceinline__ void fast_tile(SoftmaxState<D, RBW>& st, f32x16 (&s_a
         st.acc[rb][db] = mfma32x32x16(vop[2 * db + kk], p_hi[rb][kk], st.acc[rb][db]);
 }
 
-template <int D, int RBW, int NW>
+// TREE: the appended positions form a tree (a.tree_mask), else a causal chain.
+template <int D, int RBW, int NW, bool TREE>
 __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
@@ -301,11 +302,15 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
   const int kb0 = s * a.kb_per_split;
   const int kb1 = min(kb0 + a.kb_per_split, nkb);
   const int ntile = kb1 > kb0 ? kb1 - kb0 : 0;
+  // keys below vis_end are visible to every row: the causal limit of the first
+  // query, or (tree) the start of the appended positions
+  const int vis_end = L - a.n_q + (TREE ? 0 : 1);
 
   // Q^T operands of this wave's rows: lane (m, h) holds row row0 + 32*rb + m,
   // dims 16*ks + 8*h .. +7.
   bf16x8 qop[RBW][KS];
   int lim[RBW];
+  uint64_t tmask[TREE ? RBW : 1];   // tree: the row's ancestor mask over the appended positions
 #pragma unroll
   for (int rb = 0; rb < RBW; ++rb) {
     const int row = row0 + rb * 32 + m;
@@ -316,10 +321,12 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) qop[rb][ks] = ld_bf16x8(qp + ks * 16);
       lim[rb] = L - a.n_q + qi + 1;
+      if constexpr (TREE) tmask[rb] = a.tree_mask[(size_t)b * a.n_q + qi];
     } else {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) qop[rb][ks] = zero_bf16x8();
       lim[rb] = L;
+      if constexpr (TREE) tmask[rb] = 0;
     }
   }
   const bool any_row = row0 < a.R;   // wave-uniform: does this wave own a real row?
@@ -450,12 +457,17 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
     const int kb = kb0 + t;
     // every key of the tile is present and visible to every row (the smallest
     // causal limit of any row is L - n_q + 1)
-    const bool all_vis = (kb + 1) * 32 <= L - a.n_q + 1;
+    const bool all_vis = (kb + 1) * 32 <= vis_end;
     keep = keys_below(L - kb * 32, h);
     mask_v = (kb + 1) * 32 > L;
 #pragma unroll
     for (int rb = 0; rb < RBW; ++rb) {
-      mx[rb] = masked_scores(x[rb], s_acc[rb], keys_below(lim[rb] - kb * 32, h), all_vis,
+      uint32_t vis;
+      if constexpr (TREE)
+        vis = keys_below(L - a.n_q - kb * 32, h) | tree_keys(tmask[rb], kb * 32 - (L - a.n_q), h);
+      else
+        vis = keys_below(lim[rb] - kb * 32, h);
+      mx[rb] = masked_scores(x[rb], s_acc[rb], vis, all_vis,
                              a.scale_log2);
 #pragma unroll
       for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(x[rb][i]));
@@ -488,7 +500,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
       for (; t + kSlots < ntile; ++t) {
         publish(t);
         const int kb = kb0 + t;
-        bool slow = !tile_ok(t) || (kb + 1) * 32 > L - a.n_q + 1;
+        bool slow = !tile_ok(t) || (kb + 1) * 32 > vis_end;
 #pragma unroll
         for (int rb = 0; rb < RBW; ++rb) {
 #pragma unroll
@@ -578,8 +590,10 @@ template <int D, int RBW>
 hipError_t launch_shared_one(const AttnArgs& a, int grid, hipStream_t stream) {
   AttnArgs arg = a;
   void* args[] = {&arg};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_shared_kernel<D, RBW, kWaves>),
-                         dim3(grid), dim3(64 * kWaves), args, 0, stream);
+  const void* k = a.tree_mask
+                      ? reinterpret_cast<const void*>(&attn_shared_kernel<D, RBW, kWaves, true>)
+                      : reinterpret_cast<const void*>(&attn_shared_kernel<D, RBW, kWaves, false>);
+  return hipLaunchKernel(k, dim3(grid), dim3(64 * kWaves), args, 0, stream);
 }
 
 }  // namespace

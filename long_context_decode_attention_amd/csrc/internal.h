@@ -16,6 +16,7 @@ struct AttnArgs {
   const int32_t* seq_lens;      // paged mode: [B]
   const int32_t* ring_pos;      // ring mode: [B][C]
   const int64_t* ring_T;        // ring mode: [B]
+  const uint64_t* tree_mask;    // paged verify: [B][n_q] ancestor masks, or null (causal)
   float* out_o;                 // partials (split mode) or final o (direct mode)
   float* out_lse;               // partials or final lse (may be null in direct mode)
   int B, Hq, Hkv, G, n_q, R, D;

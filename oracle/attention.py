@@ -175,6 +175,30 @@ def verify(q, K, V, L: int, scale: float):
     return o, lse
 
 
+def verify_tree(q, K, V, L: int, masks, scale: float):
+    """Verify of a tree of ``n_q`` proposals ([VERDICT] forward implications: the
+    window composes with tree-shaped speculation).
+
+    q [n_q, Hq, D]; K, V [>= L, Hkv, D]; ``L`` counts the ``n_q`` appended positions;
+    ``masks[i]`` (an int) has bit ``a`` set when query ``i`` sees the appended
+    position ``L - n_q + a`` (its ancestors and itself).  Every query sees all keys
+    before the appended ones.  Returns (o [n_q, Hq, D], lse [n_q, Hq]); a query
+    with no key gets o = 0, lse = -inf.
+    """
+    q = np.asarray(q)
+    n_q = q.shape[0]
+    if L < n_q:
+        raise ValueError("L must count the n_q appended positions")
+    base = L - n_q
+    o = np.zeros(q.shape[:2] + (V.shape[2],))
+    lse = np.zeros(q.shape[:2])
+    for i in range(n_q):
+        seen = [base + a for a in range(n_q) if (int(masks[i]) >> a) & 1]
+        o[i], lse[i] = draft_over(q[i], K, V, np.concatenate([np.arange(base), seen]).astype(np.int64),
+                                  scale)
+    return o, lse
+
+
 def draft_context_window(q, K, V, L: int, n_sink: int, n_recent: int, scale: float):
     """Windowed draft context pass: ``n_q`` causal queries over the draft KV, query
     ``i`` (position ``L - n_q + i``) over the window of its own position.

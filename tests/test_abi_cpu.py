@@ -118,6 +118,16 @@ def test_verify_and_window_argument_checks():
     assert win(pos=None) == INVALID
     assert win(D=96) == UNSUPPORTED
 
+    def tree(**kw):
+        a = dict(mask=FAKE, n_q=8)
+        a.update(kw)
+        return lib.wmtp_verify_attn_tree(P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(a["mask"]),
+                                         1, a["n_q"], 32, 2, 256, 16, 16, 1024, 1.0, P(FAKE), None,
+                                         None, 0, 0, 0, None)
+    assert tree(mask=None) == INVALID
+    assert tree(mask=FAKE + 4) == INVALID             # misaligned
+    assert tree(n_q=65) == INVALID                    # more proposals than mask bits
+
 
 def test_paged_window_argument_checks():
     lib = _lib()

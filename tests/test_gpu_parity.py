@@ -434,6 +434,46 @@ def test_verify_long_splits(cfg_name, S, n_q, num_splits, peak):
           f"max|o err| {err:.2e} (max|o| {float(np.max(np.abs(ro))):.2e}), max|lse err| {lerr:.2e}")
 
 
+def _tree_masks(n_q, kind):
+    if kind == "binary":      # node i's parent is (i - 1) // 2
+        masks = []
+        for i in range(n_q):
+            mk, j = 0, i
+            while True:
+                mk |= 1 << j
+                if j == 0:
+                    break
+                j = (j - 1) // 2
+            masks.append(mk)
+        return masks
+    if kind == "star":        # every node a child of the root
+        return [1] + [1 | (1 << i) for i in range(1, n_q)]
+    return [(1 << (i + 1)) - 1 for i in range(n_q)]   # chain
+
+
+@pytest.mark.parametrize("cfg_name,S,n_q,kind,num_splits", [
+    ("ctx1m_g32x2_d256", 20000, 8, "binary", 2),       # shared kernel, 128 rows, long splits
+    ("ctx1m_g32x2_d256", 3000, 8, "star", 0),
+    ("ctx128k_g32x4_d128", 9000, 4, "binary", 0),      # split kernel, 32 rows
+    ("nope8l_1m_g64x2_d128", 6000, 8, "star", 1),      # shared kernel, two row blocks
+    ("ctx1m_g32x2_d256", 5000, 8, "chain", 3),
+])
+def test_verify_tree(cfg_name, S, n_q, kind, num_splits):
+    """Verify of a tree of proposals: query i sees the prefix and its ancestors."""
+    lib = _lib()
+    cfg = CFG[cfg_name]
+    vs = VerifyScenario(cfg, 80 + n_q, [S], n_q)
+    vs.append_proposed()
+    masks = _tree_masks(n_q, kind)
+    tm = torch().tensor([masks], dtype=torch().int64, device="cuda")
+    L = S + n_q
+    o, l = lib.verify_attn_tree(dev_bf16(vs.q), vs.kv.k, vs.kv.v, vs.kv.block_table, dev_i32([L]),
+                                tm, L, 1.0, num_splits=num_splits)
+    torch().cuda.synchronize()
+    ro, rl = OA.verify_tree(vs.q[0], vs.K[0], vs.V[0], L, masks, 1.0)
+    compare(o[0], l[0], ro, rl, f"tree verify {cfg_name} {kind}")
+
+
 def test_verify_same_in_both_arms():
     """The verify call reads only the target KV: repeated calls (one per arm) agree bitwise."""
     lib = _lib()

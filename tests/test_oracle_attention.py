@@ -232,6 +232,55 @@ def test_verify_query_i_sees_its_causal_prefix():
     assert np.max(np.abs(ov[0] - of_all)) > 1e-6
 
 
+def test_tree_verify_with_chain_masks_is_the_causal_verify():
+    rng = np.random.default_rng(14)
+    S, n_q, Hq, Hkv, D = 33, 5, 4, 2, 8
+    L = S + n_q
+    q = _bf16(rng, n_q, Hq, D)
+    K, V = _kv(rng, L, Hkv, D)
+    ot, lt = A.verify_tree(q, K, V, L, [(1 << (i + 1)) - 1 for i in range(n_q)], 0.5)
+    ov, lv = A.verify(q, K, V, L, 0.5)
+    assert np.array_equal(ot, ov) and np.array_equal(lt, lv)
+
+
+def test_tree_verify_bruteforce_on_a_small_tree():
+    """Root 0 with children 1 and 2, node 3 under 1: each query against pure-Python
+    attention over the prefix plus its ancestors."""
+    rng = np.random.default_rng(15)
+    S, Hq, Hkv, D = 9, 2, 1, 4
+    masks = [0b0001, 0b0011, 0b0101, 0b1011]
+    n_q = len(masks)
+    L = S + n_q
+    q = _bf16(rng, n_q, Hq, D)
+    K, V = _kv(rng, L, Hkv, D)
+    o, lse = A.verify_tree(q, K, V, L, masks, 0.7)
+    Kf, Vf, qf = bf16_to_f32(K), bf16_to_f32(V), bf16_to_f32(q)
+    for i, mk in enumerate(masks):
+        rows = list(range(S)) + [S + a for a in range(n_q) if (mk >> a) & 1]
+        for h in range(Hq):
+            bo, bl = _brute(qf[i, h], [Kf[r, 0] for r in rows], [Vf[r, 0] for r in rows], 0.7)
+            assert np.max(np.abs(o[i, h] - np.array(bo))) < 1e-12
+            assert abs(lse[i, h] - bl) < 1e-12
+
+
+def test_tree_verify_ignores_non_ancestors_and_empty_masks_read_the_prefix():
+    rng = np.random.default_rng(16)
+    S, Hq, Hkv, D = 20, 2, 1, 8
+    masks = [0b001, 0b011, 0b101]
+    n_q = 3
+    L = S + n_q
+    q = _bf16(rng, n_q, Hq, D)
+    K, V = _kv(rng, L, Hkv, D)
+    base, _ = A.verify_tree(q, K, V, L, masks, 1.0)
+    V2 = A.widen_bf16(V).copy()
+    V2[S + 1] += 50.0                           # appended position 1: not an ancestor of query 2
+    moved, _ = A.verify_tree(q, K, V2, L, masks, 1.0)
+    assert np.array_equal(moved[2], base[2]) and np.max(np.abs(moved[1] - base[1])) > 1e-3
+    o0, l0 = A.verify_tree(q, K, V, L, [0, 0, 0], 1.0)
+    of, lf = A.draft_full(q[1], K, V, S, 1.0)
+    assert np.allclose(o0[1], of, rtol=0, atol=1e-14) and np.allclose(l0[1], lf, rtol=0, atol=1e-14)
+
+
 def test_context_window_covering_everything_is_the_causal_verify():
     """A window that covers the whole context turns the windowed draft context
     pass into the native one, which is the causal verify over the draft KV."""
