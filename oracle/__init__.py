@@ -23,6 +23,8 @@ Modules
                 split combine.
 ``ring``        the draft-KV ring buffer slot mapping and its state after
                 any sequence of appends (pure Python).
+``fp8``         OCP e4m3 storage of the draft KV: the quantizer and the values
+                of the 8-bit codes.
 ``accounting``  the per-step cost identity (Eq. 1), the two readings of the
                 cost reduction, the dropped-entry and reclaimed-KV fractions.
 
