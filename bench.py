@@ -138,6 +138,13 @@ def main() -> int:
     sc.fill_paged(tkv, 0, 0, Kt[:S], Vt[:S])
     sc.fill_ring(ring, 0, Kd[:S], Vd[:S])
     sc.fill_ring(ring_c, 0, Kd[:S], Vd[:S])
+    # the same draft KV as fp8 e4m3 codes (scales 1: N(0, 1) values fit), same pages
+    k8, v8 = lib.new_paged_cache_fp8(dkv.num_pages, Hkv, D, dev)
+    for lo in range(0, S, 1 << 16):
+        hi = min(S, lo + (1 << 16))
+        lib.paged_append_fp8(k8, v8, dkv.block_table, torch.tensor([lo], dtype=torch.int32, device=dev),
+                             sc.to_device_bf16(Kd[lo:hi]).unsqueeze(0),
+                             sc.to_device_bf16(Vd[lo:hi]).unsqueeze(0))
     # per-step inputs, resident on the device
     kd_new = sc.to_device_bf16(Kd[S:S + d_extra]).view(nsteps, gamma, 1, 1, Hkv, D)
     vd_new = sc.to_device_bf16(Vd[S:S + d_extra]).view(nsteps, gamma, 1, 1, Hkv, D)
@@ -179,6 +186,10 @@ def main() -> int:
                                                  paged_window=True), dev)
     ws_f = lib.new_workspace(lib.workspace_bytes(B, Hq, Hkv, D, 1, max_d, args.num_splits,
                                                  partials_only=True), dev)
+    ws_8 = lib.new_workspace(lib.workspace_bytes(B, Hq, Hkv, D, 1, max_d, args.num_splits,
+                                                 partials_only=True), dev)
+    o_8 = torch.empty(B, Hq, D, device=dev)
+    l_8 = torch.empty(B, Hq, device=dev)
     ws_v = lib.new_workspace(lib.workspace_bytes(B, Hq, Hkv, D, n_q, max_t), dev)
     o_c = torch.empty(B, n_ctx, Hq, D, device=dev)
     l_c = torch.empty(B, n_ctx, Hq, device=dev)
@@ -242,12 +253,24 @@ def main() -> int:
                                1.0, o_c, l_c, ws_cn, prepare=True),
                lib.verify_attn_tree(qv[k], tkv.k, tkv.v, tkv.block_table, t_len[k], tree_mask,
                                     max_t, 1.0, o_v, l_v, ws_v, prepare=True))
-        plan.append((win, full, wpg, ver, ctx))
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(10 + 2 * gamma)]
+        # native arm over the fp8 draft KV: quantizing append, split pass, combine
+        full8 = []
+        for j in range(gamma):
+            full8.append((
+                lib.paged_append_fp8(k8, v8, dkv.block_table, d_pos[k, j], kd_new[k, j],
+                                     vd_new[k, j], prepare=True),
+                lib.draft_attn_full_fp8(qd[k, j], k8, v8, dkv.block_table, d_len[k, j], max_d,
+                                        workspace=ws_8, num_splits=args.num_splits,
+                                        partials_only=True, prepare=True),
+                lib.split_combine(*lib.partials_view(ws_8, B, Hq, Hkv, D, 1, max_d, args.num_splits),
+                                  B, Hkv, G, 1, splits_per_group=splits_f,
+                                  o=o_8.view(B, 1, Hq, D), lse=l_8.view(B, 1, Hq), prepare=True)))
+        plan.append((win, full, wpg, ver, ctx, full8))
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(11 + 4 * gamma)]
            for _ in range(nsteps)]
 
     def step(k):
-        win, full, wpg, ver, ctx = plan[k]
+        win, full, wpg, ver, ctx, full8 = plan[k]
         e = evs[k]
         e[0].record(stream)
         for c in win:                       # windowed arm: gamma x (ring append + attention)
@@ -274,9 +297,17 @@ def main() -> int:
         e[7 + 2 * gamma].record(stream)
         ctx[3]()                            # the verify for a tree of proposals
         e[8 + 2 * gamma].record(stream)
+        for j, (app, attn, comb) in enumerate(full8):  # native arm, fp8 draft KV
+            app()
+            e[10 + 2 * gamma + 2 * j].record(stream)
+            attn()
+            e[11 + 2 * gamma + 2 * j].record(stream)
+            comb()
+        e[9 + 2 * gamma].record(stream)
         return {"t0": e[0], "t1": e[1], "t2": e[2], "p1": e[5 + 2 * gamma], "v0": e[3],
                 "t3": e[4], "c1": e[6 + 2 * gamma], "c2": e[7 + 2 * gamma],
-                "c3": e[8 + 2 * gamma],
+                "c3": e[8 + 2 * gamma], "f8": e[9 + 2 * gamma],
+                "attn8": [(e[10 + 2 * gamma + 2 * j], e[11 + 2 * gamma + 2 * j]) for j in range(gamma)],
                 "attn": [(e[5 + 2 * j], e[6 + 2 * j]) for j in range(gamma)]}
 
     if args.copy_calibration:
@@ -307,6 +338,8 @@ def main() -> int:
     ctx_win = np.median([us(m["t3"], m["c1"]) for m in marks])
     ctx_full = np.median([us(m["c1"], m["c2"]) for m in marks])
     tree_us = np.median([us(m["c2"], m["c3"]) for m in marks])
+    full8_chain = np.median([us(m["c3"], m["f8"]) for m in marks])
+    attn8_mean = float(np.array([us(a, b) for m in marks for (a, b) in m["attn8"]]).mean())
     verify_us = np.median([us(m["p1"], m["t3"]) for m in marks])
     verify_kernel_us = np.median([us(m["v0"], m["t3"]) for m in marks])
     attn_us = np.array([us(a, b) for m in marks for (a, b) in m["attn"]])
@@ -316,6 +349,7 @@ def main() -> int:
     # mean keys read by the timed draft steps (step k, draft j reads S + k*gamma + j keys)
     L_avg = S + gamma * (args.warmup + nsteps - 1) / 2.0 + (gamma + 1) / 2.0
     kv_bytes = 2 * Hkv * D * 2                             # K + V bytes per position
+    attn8_bytes = kv_bytes / 2 * L_avg + B * Hq * D * 2        # fp8 K + V of the keys + q
     attn_bytes = kv_bytes * L_avg + B * Hq * D * 2         # keys' K/V + q (algorithmic)
     verify_bytes = kv_bytes * (S + n_q * (args.warmup + nsteps) / 2.0) + B * n_q * Hq * (D * 2 + D * 4 + 4)
     win_bytes = kv_bytes * (n_sink + n_recent) + B * Hq * D * 2
@@ -348,10 +382,13 @@ def main() -> int:
                    "draft_depth": gamma, "window": f"{n_sink}+{n_recent}", "ring_slots": C,
                    "verify_queries": n_q},
         "draft_attn_us_per_step": {"full": round(float(full_chain / gamma), 2),
+                                   "full_fp8_kv": round(float(full8_chain / gamma), 2),
+                                   "full_fp8_kv_attention_kernel": round(attn8_mean, 2),
                                    "window": round(float(win_step_us), 2),
                                    "window_paged_index": round(float(wpg_chain / gamma), 2),
                                    "full_attention_kernel": round(attn_mean, 2)},
         "decode_step_us": {"full": round(float(step_full), 2), "window": round(float(step_window), 2),
+                           "full_fp8_kv": round(float(verify_us + full8_chain), 2),
                            "window_paged_index": round(float(verify_us + wpg_chain), 2),
                            "verify": round(float(verify_us), 2),
                            "verify_kernel": round(float(verify_kernel_us), 2),
@@ -370,6 +407,11 @@ def main() -> int:
                      "bytes_per_launch": int(attn_bytes)},
         "roofline_verify": {"bound": "hbm", "achieved": round(verify_gbs, 1), "peak": HBM_PEAK_GBS,
                             "unit": "GB/s", "frac": round(verify_gbs / HBM_PEAK_GBS, 4)},
+        "roofline_full_fp8_kv": {
+            "bound": "hbm", "achieved": round(attn8_bytes / (attn8_mean * 1e-6) / 1e9, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(attn8_bytes / (attn8_mean * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "bytes_per_launch": int(attn8_bytes)},
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle, one kv head of one native draft step)")

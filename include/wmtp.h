@@ -140,6 +140,46 @@ wmtp_status wmtp_draft_attn_full(const uint16_t* q, const uint16_t* k_cache,
                                  void* stream);
 
 /*
+ * fp8 draft KV.  (Verdict page, forward implications: the window composes with
+ * KV quantization to fp8.)  The format is OCP fp8 E4M3 (1 sign, 4 exponent
+ * bits of bias 7, 3 mantissa bits; no infinity, largest magnitude 448).  An fp8
+ * cache has the tile layout of the bf16 caches with one byte per element: a
+ * page of 64 positions is Hkv * 2 tiles of 32 * D bytes for K and the same
+ * for V.  A bf16 value x is stored as the code nearest to x / scale (the
+ * product with the float32 inverse of the scale, clamped to +-448, rounded to
+ * nearest with ties to the even code); its value is code value * scale.  One
+ * scale per cache (k_scale, v_scale: finite, > 0).
+ *
+ * wmtp_paged_append_fp8: as wmtp_paged_append, quantizing into fp8 caches.
+ * wmtp_draft_attn_full_fp8 / wmtp_draft_attn_window_paged_fp8: as the bf16
+ * calls, reading fp8 caches: the attention over the dequantized keys and
+ * values (every e4m3 value is a bf16 value, so the MFMA operands are exact);
+ * k_scale folds into the logit scale, v_scale into the output.  At most 32
+ * query rows per kv head (Hq / Hkv), else WMTP_ERR_UNSUPPORTED.  Workspace and
+ * plan as the bf16 calls.
+ */
+wmtp_status wmtp_paged_append_fp8(uint8_t* k_cache, uint8_t* v_cache, const int32_t* block_table,
+                                  const int32_t* start_pos, const uint16_t* k_new,
+                                  const uint16_t* v_new, int B, int n_new, int Hkv, int D,
+                                  int num_pages, int max_pages, float k_scale, float v_scale,
+                                  void* stream);
+
+wmtp_status wmtp_draft_attn_full_fp8(const uint16_t* q, const uint8_t* k_cache,
+                                     const uint8_t* v_cache, const int32_t* block_table,
+                                     const int32_t* seq_lens, int B, int Hq, int Hkv, int D,
+                                     int num_pages, int max_pages, int max_seq_len, float k_scale,
+                                     float v_scale, float softmax_scale, float* o, float* lse,
+                                     void* workspace, size_t workspace_bytes, int num_splits,
+                                     unsigned flags, void* stream);
+
+wmtp_status wmtp_draft_attn_window_paged_fp8(
+    const uint16_t* q, const uint8_t* k_cache, const uint8_t* v_cache, const int32_t* block_table,
+    const int32_t* seq_lens, int B, int Hq, int Hkv, int D, int num_pages, int max_pages,
+    int max_seq_len, int n_sink, int n_recent, float k_scale, float v_scale, float softmax_scale,
+    float* o, float* lse, void* workspace, size_t workspace_bytes, int num_splits, unsigned flags,
+    void* stream);
+
+/*
  * Verify of a tree of proposals: as wmtp_verify_attn, but the n_q appended
  * positions form a tree instead of a chain.  (Verdict page, forward
  * implications: the window composes with tree-shaped speculation.)  Query i

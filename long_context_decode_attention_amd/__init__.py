@@ -26,7 +26,8 @@ FLAG_PARTIALS_ONLY = 1
 EXPORTS = (
     "wmtp_status_string", "wmtp_plan_splits", "wmtp_workspace_bytes",
     "wmtp_draft_attn_full", "wmtp_draft_attn_window", "wmtp_draft_attn_window_paged",
-    "wmtp_draft_context_window", "wmtp_verify_attn_tree", "wmtp_ring_append",
+    "wmtp_draft_context_window", "wmtp_verify_attn_tree", "wmtp_paged_append_fp8",
+    "wmtp_draft_attn_full_fp8", "wmtp_draft_attn_window_paged_fp8", "wmtp_ring_append",
     "wmtp_paged_append", "wmtp_verify_attn", "wmtp_split_combine",
 )
 
@@ -59,6 +60,10 @@ _SIGS = {
     "wmtp_draft_attn_window_paged": ([_P] * 5 + [_I] * 9 + [_F, _P, _P, _P, _SZ, _I, _U, _P], _I),
     "wmtp_draft_context_window": ([_P] * 5 + [_I] * 8 + [_F, _P, _P, _P, _SZ, _I, _U, _P], _I),
     "wmtp_verify_attn_tree": ([_P] * 6 + [_I] * 8 + [_F, _P, _P, _P, _SZ, _I, _U, _P], _I),
+    "wmtp_paged_append_fp8": ([_P] * 6 + [_I] * 6 + [_F, _F, _P], _I),
+    "wmtp_draft_attn_full_fp8": ([_P] * 5 + [_I] * 7 + [_F, _F, _F, _P, _P, _P, _SZ, _I, _U, _P], _I),
+    "wmtp_draft_attn_window_paged_fp8": ([_P] * 5 + [_I] * 9 + [_F, _F, _F, _P, _P, _P, _SZ, _I, _U, _P],
+                                         _I),
     "wmtp_ring_append": ([_P] * 6 + [_I] * 6 + [_P], _I),
     "wmtp_paged_append": ([_P] * 6 + [_I] * 6 + [_P], _I),
     "wmtp_verify_attn": ([_P] * 5 + [_I] * 8 + [_F, _P, _P, _P, _SZ, _I, _U, _P], _I),
@@ -160,6 +165,15 @@ def new_paged_cache(num_pages: int, Hkv: int, D: int, device="cuda"):
     torch = _torch()
     k = torch.empty(k_cache_shape(num_pages, Hkv, D), dtype=torch.bfloat16, device=device)
     v = torch.empty(v_cache_shape(num_pages, Hkv, D), dtype=torch.bfloat16, device=device)
+    return k, v
+
+
+def new_paged_cache_fp8(num_pages: int, Hkv: int, D: int, device="cuda"):
+    """Uninitialised fp8 (e4m3 codes, uint8) K and V caches: the bf16 tile layout,
+    one byte per element."""
+    torch = _torch()
+    k = torch.empty(k_cache_shape(num_pages, Hkv, D), dtype=torch.uint8, device=device)
+    v = torch.empty(v_cache_shape(num_pages, Hkv, D), dtype=torch.uint8, device=device)
     return k, v
 
 
@@ -455,6 +469,68 @@ def ring_append(ring: Ring, k_new, v_new, stream=None, prepare=False):
     return _invoke("wmtp_ring_append", (_ptr(ring.k), _ptr(ring.v), _ptr(ring.pos), _ptr(ring.T),
                                         _ptr(k_new), _ptr(v_new), B, n_new, Hkv, D, ring.C,
                                         ring.n_sink, _stream(stream)), prepare)
+
+
+def paged_append_fp8(k_cache, v_cache, block_table, start_pos, k_new, v_new, k_scale=1.0,
+                     v_scale=1.0, stream=None, prepare=False):
+    """Quantize ``n_new`` bf16 positions per sequence into fp8 caches
+    (``wmtp_paged_append_fp8``)."""
+    torch = _torch()
+    B, n_new, Hkv, D = k_new.shape
+    num_pages = k_cache.shape[0]
+    max_pages = block_table.shape[1]
+    _need(k_cache, torch.uint8, k_cache_shape(num_pages, Hkv, D), "k_cache")
+    _need(v_cache, torch.uint8, v_cache_shape(num_pages, Hkv, D), "v_cache")
+    _need(block_table, torch.int32, (B, max_pages), "block_table")
+    _need(start_pos, torch.int32, (B,), "start_pos")
+    _need(k_new, torch.bfloat16, (B, n_new, Hkv, D), "k_new")
+    _need(v_new, torch.bfloat16, (B, n_new, Hkv, D), "v_new")
+    return _invoke("wmtp_paged_append_fp8", (
+        _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(start_pos), _ptr(k_new),
+        _ptr(v_new), B, n_new, Hkv, D, num_pages, max_pages, float(k_scale), float(v_scale),
+        _stream(stream)), prepare)
+
+
+def draft_attn_full_fp8(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, k_scale=1.0,
+                        v_scale=1.0, softmax_scale=1.0, o=None, lse=None, workspace=None,
+                        num_splits=0, partials_only=False, stream=None, prepare=False,
+                        window=None):
+    """Native draft attention over fp8 caches (``wmtp_draft_attn_full_fp8``); with
+    ``window=(n_sink, n_recent)`` the truncated paged index
+    (``wmtp_draft_attn_window_paged_fp8``)."""
+    torch = _torch()
+    B, Hq, D = q.shape
+    num_pages, Hkv = k_cache.shape[0], k_cache.shape[1]
+    max_pages = block_table.shape[1]
+    _need(q, torch.bfloat16, None, "q")
+    _need(k_cache, torch.uint8, k_cache_shape(num_pages, Hkv, D), "k_cache")
+    _need(v_cache, torch.uint8, v_cache_shape(num_pages, Hkv, D), "v_cache")
+    _need(block_table, torch.int32, (B, max_pages), "block_table")
+    _need(seq_lens, torch.int32, (B,), "seq_lens")
+    if window is None:
+        need = workspace_bytes(B, Hq, Hkv, D, 1, min(int(max_seq_len), max_pages * PAGE),
+                               num_splits, partials_only)
+    else:
+        need = workspace_bytes(B, Hq, Hkv, D, 1, int(window[0]) + int(window[1]), num_splits,
+                               partials_only, paged_window=True)
+    if workspace is None:
+        workspace = new_workspace(need, q.device)
+    _need(workspace, torch.uint8, None, "workspace")
+    if not partials_only:
+        o, lse = _outputs(o, lse, (B, Hq, D), (B, Hq), q.device)
+    head = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
+            B, Hq, Hkv, D, num_pages, max_pages, int(max_seq_len))
+    tail = (float(k_scale), float(v_scale), float(softmax_scale), _ptr(o), _ptr(lse),
+            _ptr(workspace), workspace.numel(), int(num_splits),
+            FLAG_PARTIALS_ONLY if partials_only else 0, _stream(stream))
+    if window is None:
+        c = _invoke("wmtp_draft_attn_full_fp8", head + tail, prepare)
+    else:
+        c = _invoke("wmtp_draft_attn_window_paged_fp8",
+                    head + (int(window[0]), int(window[1])) + tail, prepare)
+    if prepare:
+        return c
+    return workspace if partials_only else (o, lse)
 
 
 def paged_append(k_cache, v_cache, block_table, start_pos, k_new, v_new, stream=None,

@@ -40,6 +40,7 @@ wmtp_status run_attention(AttnArgs a, bool ring, int max_keys, int plan_keys, fl
                       &p))
     return (a.n_q * (a.Hq / a.Hkv) > 256) ? WMTP_ERR_UNSUPPORTED : WMTP_ERR_INVALID_ARG;
   if (a.win && p.shared) return WMTP_ERR_UNSUPPORTED;   // truncated index: split kernel only
+  if (a.kv8 && p.shared) return WMTP_ERR_UNSUPPORTED;   // fp8 caches: split kernel only
   if (p.ws_bytes > 0) {
     if (!workspace || !aligned16(workspace)) return WMTP_ERR_WORKSPACE;
     if (workspace_bytes < p.ws_bytes) return WMTP_ERR_WORKSPACE;
@@ -139,7 +140,8 @@ static wmtp_status paged_attention(const uint16_t* q, const uint16_t* k_cache,
                                    float softmax_scale, float* o, float* lse, void* workspace,
                                    size_t workspace_bytes, int num_splits, unsigned flags,
                                    void* stream, bool win = false, int n_sink = 0,
-                                   int n_recent = 0, const uint64_t* tree_mask = nullptr) {
+                                   int n_recent = 0, const uint64_t* tree_mask = nullptr,
+                                   bool kv8 = false, float k_scale = 1.f, float v_scale = 1.f) {
   if (!attn_dims_ok(B, Hq, Hkv, D) || n_q < 1) return WMTP_ERR_INVALID_ARG;
   if (!head_dim_ok(D)) return WMTP_ERR_UNSUPPORTED;
   if (n_q * (Hq / Hkv) > 256) return WMTP_ERR_UNSUPPORTED;
@@ -170,6 +172,16 @@ static wmtp_status paged_attention(const uint16_t* q, const uint16_t* k_cache,
   a.max_pages = max_pages;
   a.scale_log2 = softmax_scale * kLog2e;
   a.tree_mask = tree_mask;
+  if (kv8) {
+    if (!std::isfinite(k_scale) || !(k_scale > 0.f) || !std::isfinite(v_scale) ||
+        !(v_scale > 0.f))
+      return WMTP_ERR_INVALID_ARG;
+    // fp8 caches: the split kernel only (up to 32 query rows per kv head)
+    if (n_q * (Hq / Hkv) > 32) return WMTP_ERR_UNSUPPORTED;
+    a.kv8 = 1;
+    a.scale_log2 = softmax_scale * k_scale * kLog2e;   // logits of the K codes
+    a.v_scale = v_scale;
+  }
   int plan_keys = max_keys;
   if (win) {
     if (n_sink < 0 || n_recent < 1) return WMTP_ERR_INVALID_ARG;
@@ -263,6 +275,33 @@ static wmtp_status ring_attention(const uint16_t* q, const uint16_t* ring_k,
                        static_cast<hipStream_t>(stream));
 }
 
+wmtp_status wmtp_draft_attn_full_fp8(const uint16_t* q, const uint8_t* k_cache,
+                                     const uint8_t* v_cache, const int32_t* block_table,
+                                     const int32_t* seq_lens, int B, int Hq, int Hkv, int D,
+                                     int num_pages, int max_pages, int max_seq_len, float k_scale,
+                                     float v_scale, float softmax_scale, float* o, float* lse,
+                                     void* workspace, size_t workspace_bytes, int num_splits,
+                                     unsigned flags, void* stream) {
+  return paged_attention(q, reinterpret_cast<const uint16_t*>(k_cache),
+                         reinterpret_cast<const uint16_t*>(v_cache), block_table, seq_lens, B, 1,
+                         Hq, Hkv, D, num_pages, max_pages, max_seq_len, softmax_scale, o, lse,
+                         workspace, workspace_bytes, num_splits, flags, stream, false, 0, 0,
+                         nullptr, true, k_scale, v_scale);
+}
+
+wmtp_status wmtp_draft_attn_window_paged_fp8(
+    const uint16_t* q, const uint8_t* k_cache, const uint8_t* v_cache, const int32_t* block_table,
+    const int32_t* seq_lens, int B, int Hq, int Hkv, int D, int num_pages, int max_pages,
+    int max_seq_len, int n_sink, int n_recent, float k_scale, float v_scale, float softmax_scale,
+    float* o, float* lse, void* workspace, size_t workspace_bytes, int num_splits, unsigned flags,
+    void* stream) {
+  return paged_attention(q, reinterpret_cast<const uint16_t*>(k_cache),
+                         reinterpret_cast<const uint16_t*>(v_cache), block_table, seq_lens, B, 1,
+                         Hq, Hkv, D, num_pages, max_pages, max_seq_len, softmax_scale, o, lse,
+                         workspace, workspace_bytes, num_splits, flags, stream, true, n_sink,
+                         n_recent, nullptr, true, k_scale, v_scale);
+}
+
 wmtp_status wmtp_verify_attn_tree(const uint16_t* q, const uint16_t* k_cache,
                                   const uint16_t* v_cache, const int32_t* block_table,
                                   const int32_t* seq_lens, const uint64_t* tree_mask, int B,
@@ -328,10 +367,12 @@ wmtp_status wmtp_ring_append(uint16_t* ring_k, uint16_t* ring_v, int32_t* ring_p
   return from_hip(launch_ring_append(a, static_cast<hipStream_t>(stream)));
 }
 
-wmtp_status wmtp_paged_append(uint16_t* k_cache, uint16_t* v_cache, const int32_t* block_table,
-                              const int32_t* start_pos, const uint16_t* k_new,
-                              const uint16_t* v_new, int B, int n_new, int Hkv, int D,
-                              int num_pages, int max_pages, void* stream) {
+// kv8: quantize to fp8 e4m3 with the scales (k_scale, v_scale > 0, finite).
+static wmtp_status paged_append(void* k_cache, void* v_cache, const int32_t* block_table,
+                                const int32_t* start_pos, const uint16_t* k_new,
+                                const uint16_t* v_new, int B, int n_new, int Hkv, int D,
+                                int num_pages, int max_pages, void* stream, bool kv8,
+                                float k_scale, float v_scale) {
   if (B < 1 || B > 65535 || Hkv < 1 || n_new < 0 || num_pages < 1 || max_pages < 1)
     return WMTP_ERR_INVALID_ARG;
   if (!head_dim_ok(D)) return WMTP_ERR_UNSUPPORTED;
@@ -340,11 +381,14 @@ wmtp_status wmtp_paged_append(uint16_t* k_cache, uint16_t* v_cache, const int32_
   if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned4(block_table) ||
       !aligned4(start_pos) || (k_new && !aligned16(k_new)) || (v_new && !aligned16(v_new)))
     return WMTP_ERR_INVALID_ARG;
+  if (kv8 && (!std::isfinite(k_scale) || !(k_scale > 0.f) || !std::isfinite(v_scale) ||
+              !(v_scale > 0.f)))
+    return WMTP_ERR_INVALID_ARG;
   if ((long)n_new * Hkv * (D / 8) / 256 + 1 > (long)INT_MAX) return WMTP_ERR_INVALID_ARG;
   if (n_new == 0) return WMTP_OK;
-  PagedAppendArgs a;
-  a.kc = k_cache;
-  a.vc = v_cache;
+  PagedAppendArgs a = {};
+  a.kc = static_cast<uint16_t*>(k_cache);
+  a.vc = static_cast<uint16_t*>(v_cache);
   a.block_table = block_table;
   a.start_pos = start_pos;
   a.k_new = k_new;
@@ -355,7 +399,27 @@ wmtp_status wmtp_paged_append(uint16_t* k_cache, uint16_t* v_cache, const int32_
   a.D = D;
   a.num_pages = num_pages;
   a.max_pages = max_pages;
+  a.kv8 = kv8 ? 1 : 0;
+  a.k_inv = kv8 ? 1.0f / k_scale : 1.0f;
+  a.v_inv = kv8 ? 1.0f / v_scale : 1.0f;
   return from_hip(launch_paged_append(a, static_cast<hipStream_t>(stream)));
+}
+
+wmtp_status wmtp_paged_append(uint16_t* k_cache, uint16_t* v_cache, const int32_t* block_table,
+                              const int32_t* start_pos, const uint16_t* k_new,
+                              const uint16_t* v_new, int B, int n_new, int Hkv, int D,
+                              int num_pages, int max_pages, void* stream) {
+  return paged_append(k_cache, v_cache, block_table, start_pos, k_new, v_new, B, n_new, Hkv, D,
+                      num_pages, max_pages, stream, false, 1.f, 1.f);
+}
+
+wmtp_status wmtp_paged_append_fp8(uint8_t* k_cache, uint8_t* v_cache, const int32_t* block_table,
+                                  const int32_t* start_pos, const uint16_t* k_new,
+                                  const uint16_t* v_new, int B, int n_new, int Hkv, int D,
+                                  int num_pages, int max_pages, float k_scale, float v_scale,
+                                  void* stream) {
+  return paged_append(k_cache, v_cache, block_table, start_pos, k_new, v_new, B, n_new, Hkv, D,
+                      num_pages, max_pages, stream, true, k_scale, v_scale);
 }
 
 wmtp_status wmtp_split_combine(const float* part_o, const float* part_lse, int n_parts,

@@ -28,6 +28,40 @@ __device__ __forceinline__ void store_kv8(uint16_t* kc, uint16_t* vc, size_t til
   }
 }
 
+// fp8 e4m3 form of 8 bf16 values: code(clamp(x * inv, +-448)), round to nearest
+// even (the conversion instruction's rounding); byte j holds element j.
+__device__ __forceinline__ u32x2 bf16x8_to_fp8(const uint16_t* src, float inv) {
+  const u32x4 w = *reinterpret_cast<const u32x4*>(src);
+  float f[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __builtin_bit_cast(float, w[i] << 16) * inv;
+    f[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xFFFF0000u) * inv;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] = fminf(fmaxf(f[i], -448.f), 448.f);
+  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], lo, true);
+  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], hi, true);
+  return u32x2{(uint32_t)lo, (uint32_t)hi};
+}
+
+// The same store as store_kv8 into fp8 tiles (one byte per element, the bf16
+// tiles' element order).
+__device__ __forceinline__ void store_kv8_fp8(uint8_t* kc, uint8_t* vc, size_t tile, int tok,
+                                              int d0, int D, const uint16_t* ksrc,
+                                              const uint16_t* vsrc, float k_inv, float v_inv) {
+  const u32x2 kq = bf16x8_to_fp8(ksrc, k_inv);
+  const u32x2 vq = bf16x8_to_fp8(vsrc, v_inv);
+  uint8_t* kt = kc + tile * (size_t)(32 * D);
+  uint8_t* vt = vc + tile * (size_t)(32 * D);
+  *reinterpret_cast<u32x2*>(kt + (d0 >> 4) * 512 + tok * 16 + (d0 & 15)) = kq;
+  uint8_t* vp = vt + (tok >> 4) * (16 * D) + (tok & 15);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) vp[(d0 + i) * 16] = (uint8_t)(vq[i >> 2] >> (8 * (i & 3)));
+}
+
 // Of the appended positions [T0, T0 + n_new), a sink position keeps its slot for
 // good, and a later position survives iff no later appended position shares its
 // slot, i.e. iff p >= T1 - M.  Only survivors are written: items
@@ -111,7 +145,11 @@ __global__ __launch_bounds__(256) void paged_append_kernel(PagedAppendArgs a) {
   const size_t src = (((size_t)b * a.n_new + t_in) * a.Hkv + g) * a.D + d0;
   const int off = (int)(pos & 63);
   const size_t tile = ((size_t)ppage * a.Hkv + g) * 2 + (off >> 5);
-  store_kv8(a.kc, a.vc, tile, off & 31, d0, a.D, a.k_new + src, a.v_new + src);
+  if (a.kv8)
+    store_kv8_fp8(reinterpret_cast<uint8_t*>(a.kc), reinterpret_cast<uint8_t*>(a.vc), tile,
+                  off & 31, d0, a.D, a.k_new + src, a.v_new + src, a.k_inv, a.v_inv);
+  else
+    store_kv8(a.kc, a.vc, tile, off & 31, d0, a.D, a.k_new + src, a.v_new + src);
 }
 
 // Appends longer than this take the multi-workgroup fill.

@@ -35,15 +35,16 @@ namespace wmtp {
 
 namespace {
 
-template <int D, bool RING>
+// KV8: the operands stay as loaded (8 fp8 bytes) until their MFMA.
+template <int D, bool RING, bool KV8>
 struct KTile {
-  bf16x8 k[D / 16];             // K operands, head-dim step ks
+  std::conditional_t<KV8, u32x2, bf16x8> k[D / 16];   // K operands, head-dim step ks
   int32_t pos[RING ? 16 : 1];   // ring mode: positions held by this lane's 16 slots
 };
 
-template <int D>
+template <int D, bool KV8>
 struct VTile {
-  bf16x8 v[D / 32][2];          // V^T operands, head-dim block db, key step kk
+  std::conditional_t<KV8, u32x2, bf16x8> v[D / 32][2];   // V^T operands (db, kk)
 };
 
 // Physical 32-key tile index of tile kb of (b, g); ok = false when the page id
@@ -77,12 +78,20 @@ __device__ __forceinline__ size_t tile_of_page(const AttnArgs& a, int ppage, int
   return ((size_t)ppage * a.Hkv + g) * 2 + (kb & 1);
 }
 
-template <int D, bool RING>
-__device__ __forceinline__ void load_k(KTile<D, RING>& t, const AttnArgs& a, size_t tile, int b,
-                                       int kb, int m, int h) {
-  const uint16_t* kt = a.kc + tile * (size_t)(32 * D);
+// The fp8 tiles keep the bf16 tiles' element order at one byte per element, so
+// the operand offsets are the same numbers in bytes.
+template <int D, bool RING, bool KV8>
+__device__ __forceinline__ void load_k(KTile<D, RING, KV8>& t, const AttnArgs& a, size_t tile,
+                                       int b, int kb, int m, int h) {
+  if constexpr (KV8) {
+    const uint8_t* kt = reinterpret_cast<const uint8_t*>(a.kc) + tile * (size_t)(32 * D);
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) t.k[ks] = ld_bf16x8_stream(kt + k_operand_offset(ks, m, h));
+    for (int ks = 0; ks < D / 16; ++ks) t.k[ks] = ld_u32x2_stream(kt + k_operand_offset(ks, m, h));
+  } else {
+    const uint16_t* kt = a.kc + tile * (size_t)(32 * D);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) t.k[ks] = ld_bf16x8_stream(kt + k_operand_offset(ks, m, h));
+  }
   if constexpr (RING) {
     // slots 8h..8h+7 and 16+8h..16+8h+7 of the tile
     const int32_t* rp = a.ring_pos + (size_t)b * a.C + kb * 32 + 8 * h;
@@ -97,20 +106,29 @@ __device__ __forceinline__ void load_k(KTile<D, RING>& t, const AttnArgs& a, siz
   }
 }
 
-template <int D>
-__device__ __forceinline__ void load_v(VTile<D>& t, const AttnArgs& a, size_t tile, int m, int h) {
-  const uint16_t* vt = a.vc + tile * (size_t)(32 * D);
+template <int D, bool KV8>
+__device__ __forceinline__ void load_v(VTile<D, KV8>& t, const AttnArgs& a, size_t tile, int m,
+                                       int h) {
+  if constexpr (KV8) {
+    const uint8_t* vt = reinterpret_cast<const uint8_t*>(a.vc) + tile * (size_t)(32 * D);
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+    for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) t.v[db][kk] = ld_bf16x8_stream(vt + v_operand_offset<D>(db, kk, m, h));
+      for (int kk = 0; kk < 2; ++kk) t.v[db][kk] = ld_u32x2_stream(vt + v_operand_offset<D>(db, kk, m, h));
+  } else {
+    const uint16_t* vt = a.vc + tile * (size_t)(32 * D);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) t.v[db][kk] = ld_bf16x8_stream(vt + v_operand_offset<D>(db, kk, m, h));
+  }
 }
 
 // Which of this lane's 16 keys exist for every row: inside the sequence length
 // (and, for a truncated paged index, below sink_end or from r0 on), or (ring)
 // holding a position of the current window.
-template <int D, bool RING>
-__device__ __forceinline__ uint32_t present_keys(const KTile<D, RING>& t, const AttnArgs& a,
+template <int D, bool RING, bool KV8>
+__device__ __forceinline__ uint32_t present_keys(const KTile<D, RING, KV8>& t, const AttnArgs& a,
                                                  int kb, int L, int T, int h, int sink_end,
                                                  int r0) {
   if constexpr (RING) {
@@ -131,7 +149,7 @@ __device__ __forceinline__ uint32_t present_keys(const KTile<D, RING>& t, const 
   }
 }
 
-template <int D, int NB, bool RING>
+template <int D, int NB, bool RING, bool KV8>
 __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
@@ -221,8 +239,8 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
   // products have: one tile of each is always in flight.  Loads are
   // unconditional (a tile with a bad page id is loaded from page 0 and then
   // masked), so the loop carries the tile registers without copies.
-  KTile<D, RING> kt;
-  VTile<D> vt;
+  KTile<D, RING, KV8> kt;
+  VTile<D, KV8> vt;
   int kb = kb0 + wave;
   bool ok = false;
   {
@@ -237,8 +255,8 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
     } else {
       tile = tile_of_page(a, kb < kb1 ? page_first : 0, g, kbl, ok);
     }
-    load_k<D, RING>(kt, a, tile, b, kbl, m, h);
-    load_v<D>(vt, a, tile, m, h);
+    load_k<D, RING, KV8>(kt, a, tile, b, kbl, m, h);
+    load_v<D, KV8>(vt, a, tile, m, h);
   }
   asm volatile("" ::: "memory");
 #pragma unroll
@@ -294,7 +312,7 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
   // S^T of tile kb, refill K (when there is a next tile), masked scores.
   auto scores_of = [&](auto has_next) {
     const int pk = phys(kb);   // the tile's place in the sequence
-    keep = ok ? present_keys<D, RING>(kt, a, pk, L, T, h, sink_end, r0) : 0u;
+    keep = ok ? present_keys<D, RING, KV8>(kt, a, pk, L, T, h, sink_end, r0) : 0u;
     bool all_vis;
     uint32_t rvis[NB];   // ring, several queries: the keys in each row's own window
     if (RING) {
@@ -328,9 +346,10 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
     for (int rb = 0; rb < NB; ++rb) {
       sacc[rb] = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) sacc[rb] = mfma32x32x16(kt.k[ks], sm_q[rb][ks][lane], sacc[rb]);
+      for (int ks = 0; ks < KS; ++ks)
+        sacc[rb] = mfma32x32x16(as_operand(kt.k[ks]), sm_q[rb][ks][lane], sacc[rb]);
     }
-    if constexpr (decltype(has_next)::value) load_k<D, RING>(kt, a, tile_n, b, kbn, m, h);
+    if constexpr (decltype(has_next)::value) load_k<D, RING, KV8>(kt, a, tile_n, b, kbn, m, h);
 #pragma unroll
     for (int rb = 0; rb < NB; ++rb) {
       uint32_t vis;
@@ -349,16 +368,29 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
     bf16x8 p_hi[NB][2], p_lo[NB][2];
 #pragma unroll
     for (int rb = 0; rb < NB; ++rb) weights<D, NB>(st, rb, x[rb], a.scale_log2, p_hi[rb], p_lo[rb]);
-    if (mask_v) {
-      // Absent keys may hold any bits (even NaN): zero their values so that
-      // 0-weight * value stays 0 in the PV product.
+    if constexpr (KV8) {
+      bf16x8 vv[DB][2];
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) vt.v[db][kk] = mask8(vt.v[db][kk], (keep >> (8 * kk)) & 0xFFu);
+        for (int kk = 0; kk < 2; ++kk) {
+          vv[db][kk] = fp8x8_to_bf16(vt.v[db][kk]);
+          // absent keys may hold any bits (an fp8 NaN too): zero them
+          if (mask_v) vv[db][kk] = mask8(vv[db][kk], (keep >> (8 * kk)) & 0xFFu);
+        }
+      pv<D, NB>(st, vv, p_hi, p_lo);
+    } else {
+      if (mask_v) {
+        // Absent keys may hold any bits (even NaN): zero their values so that
+        // 0-weight * value stays 0 in the PV product.
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) vt.v[db][kk] = mask8(vt.v[db][kk], (keep >> (8 * kk)) & 0xFFu);
+      }
+      pv<D, NB>(st, vt.v, p_hi, p_lo);
     }
-    pv<D, NB>(st, vt.v, p_hi, p_lo);
-    if constexpr (decltype(has_next)::value) load_v<D>(vt, a, tile_n, m, h);
+    if constexpr (decltype(has_next)::value) load_v<D, KV8>(vt, a, tile_n, m, h);
   };
   const std::true_type more;
   const std::false_type last;
@@ -433,7 +465,7 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
     __syncthreads();
     const int row = row0 + rb * 32 + m;
     if (row < a.R) {
-      const float inv = Ltot > 0.f ? 1.f / Ltot : 0.f;
+      const float inv = (Ltot > 0.f ? 1.f / Ltot : 0.f) * (KV8 ? a.v_scale : 1.f);
       float* op;
       float* lp;
       if (a.direct) {
@@ -458,18 +490,20 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
   }
 }
 
-template <int D, int NB, bool RING>
+template <int D, int NB, bool RING, bool KV8>
 hipError_t launch_one(const AttnArgs& a, int grid, hipStream_t stream) {
   AttnArgs arg = a;
   void* args[] = {&arg};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_split_kernel<D, NB, RING>),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_split_kernel<D, NB, RING, KV8>),
                          dim3(grid), dim3(256), args, 0, stream);
 }
 
 template <int D>
 hipError_t launch_d(const AttnArgs& a, const AttnPlan& p, bool ring, hipStream_t stream) {
   if (p.nrb != 1) return hipErrorInvalidValue;
-  return ring ? launch_one<D, 1, true>(a, p.grid, stream) : launch_one<D, 1, false>(a, p.grid, stream);
+  if (ring) return launch_one<D, 1, true, false>(a, p.grid, stream);
+  return a.kv8 ? launch_one<D, 1, false, true>(a, p.grid, stream)
+               : launch_one<D, 1, false, false>(a, p.grid, stream);
 }
 
 }  // namespace

@@ -71,6 +71,20 @@ __device__ __forceinline__ uint32_t keys_below(int count, int h) {
 __device__ __forceinline__ float max_over_row(float v) { return fmaxf(v, __shfl_xor(v, 32)); }
 __device__ __forceinline__ float sum_over_row(float v) { return v + __shfl_xor(v, 32); }
 
+// Eight fp8 e4m3 values (bytes 0..7 of r, element j = byte j) as the bf16 MFMA
+// operand of the same element order.  Every e4m3 value is a bf16 value, so the
+// conversion (hardware fp8 -> fp32, then the high halves) is exact.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(u32x2 r) {
+  const auto f0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)r.x, false);
+  const auto f1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)r.x, true);
+  const auto f2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)r.y, false);
+  const auto f3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)r.y, true);
+  return __builtin_bit_cast(bf16x8, u32x4{pack_bf16x2(f0[0], f0[1]), pack_bf16x2(f1[0], f1[1]),
+                                          pack_bf16x2(f2[0], f2[1]), pack_bf16x2(f3[0], f3[1])});
+}
+__device__ __forceinline__ bf16x8 as_operand(bf16x8 v) { return v; }
+__device__ __forceinline__ bf16x8 as_operand(u32x2 r) { return fp8x8_to_bf16(r); }
+
 // Verify under a tree of proposals: of this lane's 16 keys, which are appended
 // positions that `mask` marks (bit a: the appended position a, 0 <= a < 64).
 // rel0 is the appended index of the tile's key 0 (negative when the tile starts

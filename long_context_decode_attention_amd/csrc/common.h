@@ -14,6 +14,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // 16-byte global load as 8 bf16 lanes.
 __device__ __forceinline__ bf16x8 ld_bf16x8(const uint16_t* p) {
@@ -27,6 +28,11 @@ __device__ __forceinline__ bf16x8 ld_bf16x8(const uint16_t* p) {
 __device__ __forceinline__ bf16x8 ld_bf16x8_stream(const uint16_t* p) {
   u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   return __builtin_bit_cast(bf16x8, v);
+}
+
+// 8-byte non-temporal load (8 fp8 values of a streamed K/V tile).
+__device__ __forceinline__ u32x2 ld_u32x2_stream(const uint8_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
 }
 
 __device__ __forceinline__ bf16x8 zero_bf16x8() {

@@ -30,6 +30,9 @@ struct AttnArgs {
   int direct;                   // 1: write final o/lse, 0: write partials
   int C, n_sink, n_recent;      // ring mode; paged mode with win: the key set
   int win;                      // paged mode: 1 = keys [0, n_sink) and the last n_recent only
+  int kv8;                      // paged mode: kc/vc hold fp8 e4m3 tiles (1 byte per element)
+  float v_scale;                // kv8: value of a V code = code value * v_scale (K's scale is
+                                // folded into scale_log2)
   float scale_log2;             // softmax_scale * log2(e)
 };
 
@@ -82,6 +85,8 @@ struct PagedAppendArgs {
   const uint16_t* k_new;
   const uint16_t* v_new;
   int B, n_new, Hkv, D, num_pages, max_pages;
+  int kv8;                      // kc/vc hold fp8 e4m3 tiles: store code(x * k_inv) etc.
+  float k_inv, v_inv;
 };
 
 hipError_t launch_paged_append(const PagedAppendArgs& a, hipStream_t stream);

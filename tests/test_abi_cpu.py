@@ -128,6 +128,19 @@ def test_verify_and_window_argument_checks():
     assert tree(mask=FAKE + 4) == INVALID             # misaligned
     assert tree(n_q=65) == INVALID                    # more proposals than mask bits
 
+    def f8(**kw):
+        a = dict(Hq=32, Hkv=2, ks=1.0, vs=1.0)
+        a.update(kw)
+        return lib.wmtp_draft_attn_full_fp8(P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), 1, a["Hq"],
+                                            a["Hkv"], 256, 16, 16, 1024, a["ks"], a["vs"], 1.0,
+                                            P(FAKE), None, None, 0, 0, 0, None)
+    assert f8(ks=0.0) == INVALID
+    assert f8(vs=float("nan")) == INVALID
+    assert f8(Hq=128) == UNSUPPORTED                  # 64 query rows per kv head
+    st = lib.wmtp_paged_append_fp8(P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), 1, 4, 2,
+                                   256, 16, 16, -1.0, 1.0, None)
+    assert st == INVALID
+
 
 def test_paged_window_argument_checks():
     lib = _lib()

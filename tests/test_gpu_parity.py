@@ -611,3 +611,75 @@ def test_error_codes():
         lib.draft_attn_full(q, sc.kv.k, sc.kv.v, sc.kv.block_table, lens, 1 << 20, workspace=small,
                             num_splits=4)
     assert e.value.status == 3
+
+
+# ------------------------------------------------------------------ fp8 draft KV
+
+def _fp8_case(cfg_name, seed, S, k_scale, v_scale, perm=True):
+    """A paged fp8 draft cache holding positions 0 .. S-1 of the seeded draft K/V,
+    written by the fp8 append in a few calls; returns what the tests need."""
+    from oracle import fp8 as F
+    from long_context_decode_attention_amd import scenario as scn
+    lib = _lib()
+    cfg = CFG[cfg_name]
+    Hkv, D = cfg["Hkv"], cfg["D"]
+    K = W.kv_positions(seed, "draft_k", 0, 0, S, Hkv, D)
+    V = W.kv_positions(seed, "draft_v", 0, 0, S, Hkv, D)
+    n_pages = (S + 63) // 64 + 1
+    table = W.page_permutation(seed, "draft_k", n_pages) if perm else np.arange(n_pages, dtype=np.int32)
+    k8, v8 = lib.new_paged_cache_fp8(n_pages, Hkv, D)
+    k8.fill_(0x7F)                  # NaN codes wherever nothing was written
+    v8.fill_(0x7F)
+    bt = torch().tensor(table.reshape(1, -1), dtype=torch().int32, device="cuda")
+    cuts = [0, S // 3, S // 3 + 1, S]
+    for lo, hi in zip(cuts[:-1], cuts[1:]):
+        if hi > lo:
+            lib.paged_append_fp8(k8, v8, bt, dev_i32([lo]), dev_bf16(K[lo:hi][None]),
+                                 dev_bf16(V[lo:hi][None]), k_scale, v_scale)
+    torch().cuda.synchronize()
+    inv_k = np.float32(1.0) / np.float32(k_scale)
+    inv_v = np.float32(1.0) / np.float32(v_scale)
+    Kc, Vc = F.bf16_to_e4m3(K, inv_k), F.bf16_to_e4m3(V, inv_v)
+    Kq, Vq = F.dequantize_e4m3(Kc, k_scale), F.dequantize_e4m3(Vc, v_scale)
+    return dict(cfg=cfg, k8=k8, v8=v8, bt=bt, table=table, Kc=Kc, Vc=Vc, Kq=Kq, Vq=Vq)
+
+
+@pytest.mark.parametrize("k_scale,v_scale", [(1.0, 1.0), (0.5, 2.0), (0.01, 0.003)])
+def test_fp8_append_codes_bitexact(k_scale, v_scale):
+    """The fp8 append stores exactly the oracle quantizer's codes, in the tile layout."""
+    c = _fp8_case("ctx1m_g32x2_d256", 90, 1000, k_scale, v_scale)
+    D = c["cfg"]["D"]
+    Kp = c["k8"].cpu().numpy().reshape(-1, c["cfg"]["Hkv"], 2, D // 16, 32, 16)
+    Kp = Kp.transpose(0, 1, 2, 4, 3, 5).reshape(Kp.shape[0], c["cfg"]["Hkv"], 64, D)
+    Vp = c["v8"].cpu().numpy().reshape(-1, c["cfg"]["Hkv"], 2, 2, D, 16)
+    Vp = Vp.transpose(0, 1, 2, 3, 5, 4).reshape(Vp.shape[0], c["cfg"]["Hkv"], 64, D)
+    for p in range(1000):
+        page = c["table"][p // 64]
+        assert np.array_equal(Kp[page, :, p % 64], c["Kc"][p]), p
+        assert np.array_equal(Vp[page, :, p % 64], c["Vc"][p]), p
+
+
+@pytest.mark.parametrize("cfg_name,S,k_scale,v_scale,num_splits", [
+    ("ctx1m_g32x2_d256", 40000, 1.0, 1.0, 0),
+    ("ctx1m_g32x2_d256", 9000, 0.5, 2.0, 1),
+    ("ctx128k_g32x4_d128", 20011, 0.25, 0.5, 0),
+    ("nope8l_1m_g64x2_d128", 3000, 1.0, 1.0, 3),     # 32 rows per kv head
+    ("ctx8k_g16x2_d128", 65, 1.0, 1.0, 0),
+])
+def test_fp8_draft_full_and_window(cfg_name, S, k_scale, v_scale, num_splits):
+    """Native draft and truncated-index window over fp8 caches against the oracle
+    over the dequantized keys and values."""
+    lib = _lib()
+    c = _fp8_case(cfg_name, 91 + S % 7, S, k_scale, v_scale)
+    cfg = c["cfg"]
+    q = W.queries(92, "q_draft", (1, cfg["Hq"]), cfg["D"])
+    o, l = lib.draft_attn_full_fp8(dev_bf16(q), c["k8"], c["v8"], c["bt"], dev_i32([S]), S,
+                                   k_scale, v_scale, 1.0, num_splits=num_splits)
+    ow, lw = lib.draft_attn_full_fp8(dev_bf16(q), c["k8"], c["v8"], c["bt"], dev_i32([S]), S,
+                                     k_scale, v_scale, 1.0, num_splits=num_splits,
+                                     window=(cfg["n_sink"], cfg["n_recent"]))
+    torch().cuda.synchronize()
+    ro, rl = OA.draft_full(q[0], c["Kq"], c["Vq"], S, 1.0)
+    compare(o[0], l[0], ro, rl, f"fp8 full {cfg_name} S={S}")
+    rwo, rwl = OA.draft_window(q[0], c["Kq"], c["Vq"], S, cfg["n_sink"], cfg["n_recent"], 1.0)
+    compare(ow[0], lw[0], rwo, rwl, f"fp8 window {cfg_name} S={S}")
