@@ -64,3 +64,77 @@ def test_ctx1m_draft_chain_and_verify_full_size():
         ro, rl = OA.draft_full(qg, Kg, Vg, S + i + 1, 1.0)
         compare(o[0, i, :G], l[0, i, :G], ro, rl, f"verify 1M query {i}")
         _say(f"verify query {i} matches")
+
+
+def test_ctx1m_next_rows_full_size():
+    """The widened rows at 1M: the truncated paged index, the fp8 draft KV, the
+    draft context pass over a ring with slack and the tree verify, each in its
+    automatic split plan, checked on kv head 1's rows."""
+    import long_context_decode_attention_amd as lib
+    from long_context_decode_attention_amd import scenario as scn
+    from oracle import fp8 as F
+    cfg = W.CONFIGS["ctx1m_g32x2_d256"]
+    S, n_q, Hkv, D = cfg["S"], cfg["n_q"], cfg["Hkv"], cfg["D"]
+    ns, nr = cfg["n_sink"], cfg["n_recent"]
+    G = cfg["Hq"] // Hkv
+    _say("building draft state (1M positions, permuted pages)")
+    sc = DraftScenario(cfg, 102, [S], 1, poison=False)
+    sc.append(1)
+    q = sc.q(1)
+    qt = dev_bf16(q)
+    L = S + 1
+    op, lp = lib.draft_attn_window_paged(qt, sc.kv.k, sc.kv.v, sc.kv.block_table, dev_i32([L]), L,
+                                         ns, nr)
+    # the same draft KV as fp8 codes, on the same pages
+    k8, v8 = lib.new_paged_cache_fp8(sc.kv.k.shape[0], Hkv, D)
+    for lo in range(0, L, 1 << 16):
+        hi = min(L, lo + (1 << 16))
+        lib.paged_append_fp8(k8, v8, sc.kv.block_table, dev_i32([lo]), dev_bf16(sc.K[0][lo:hi][None]),
+                             dev_bf16(sc.V[0][lo:hi][None]))
+    o8, l8 = lib.draft_attn_full_fp8(qt, k8, v8, sc.kv.block_table, dev_i32([L]), L)
+    # the context pass: a ring with 64 slots of slack, the last 8 positions as queries
+    ring = lib.new_ring(1, cfg["C"] + 64, Hkv, D, ns, nr)
+    scn.fill_ring(ring, 0, sc.K[0][:L], sc.V[0][:L])
+    qc = W.queries(103, "q_ctx", (1, n_q, cfg["Hq"]), D)
+    oc, lc = lib.draft_context_window(dev_bf16(qc), ring)
+    torch().cuda.synchronize()
+    _say("oracle on kv head 1")
+    qg, Kg, Vg = _group(q[0], sc.K[0], sc.V[0], 1, G)
+    ro, rl = OA.draft_window(qg, Kg, Vg, L, ns, nr, 1.0)
+    compare(op[0, G:2 * G], lp[0, G:2 * G], ro, rl, "paged window 1M")
+    _say("truncated paged index matches")
+    Kq = F.dequantize_e4m3(F.bf16_to_e4m3(Kg[:L]))
+    Vq = F.dequantize_e4m3(F.bf16_to_e4m3(Vg[:L]))
+    ro, rl = OA.draft_full(qg, Kq, Vq, L, 1.0)
+    compare(o8[0, G:2 * G], l8[0, G:2 * G], ro, rl, "fp8 full 1M")
+    del Kq, Vq
+    _say("fp8 native draft matches")
+    qcg = qc[0][:, G:2 * G]
+    ro, rl = OA.draft_context_window(qcg, Kg, Vg, L, ns, nr, 1.0)
+    compare(oc[0, :, G:2 * G], lc[0, :, G:2 * G], ro, rl, "context pass 1M")
+    _say("context pass matches")
+    del sc, ring, k8, v8
+    _say("building target state (1M + 8 positions)")
+    vs = VerifyScenario(cfg, 104, [S], n_q, poison=False)
+    vs.append_proposed()
+    Lt = S + n_q
+    masks = []
+    for i in range(n_q):          # binary tree: node i's parent (i - 1) // 2
+        mk, j = 0, i
+        while True:
+            mk |= 1 << j
+            if j == 0:
+                break
+            j = (j - 1) // 2
+        masks.append(mk)
+    tm = torch().tensor([masks], dtype=torch().int64, device="cuda")
+    o, l = lib.verify_attn_tree(dev_bf16(vs.q), vs.kv.k, vs.kv.v, vs.kv.block_table, dev_i32([Lt]),
+                                tm, Lt)
+    torch().cuda.synchronize()
+    # each sampled query over the prefix plus its ancestors
+    for i in (0, n_q - 1):
+        rows = np.concatenate([np.arange(S), [S + a for a in range(n_q) if (masks[i] >> a) & 1]])
+        qg, Kg, Vg = _group(vs.q[0, i], vs.K[0], vs.V[0], 0, G)
+        ro, rl = OA.draft_over(qg, Kg, Vg, rows.astype(np.int64), 1.0)
+        compare(o[0, i, :G], l[0, i, :G], ro, rl, f"tree verify 1M query {i}")
+        _say(f"tree verify query {i} matches")
