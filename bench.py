@@ -51,22 +51,22 @@ def log(msg: str) -> None:
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
-def cpu_baseline(K, V, q, L, G, g=1):
-    """The float64 oracle on a bounded sample: one kv head's G query rows of one
-    native draft step over L keys; scaled to the whole step (all kv heads)."""
+def cpu_baseline(K, V, qs, S, G, Hkv):
+    """The float64 oracle on a bounded sample of the workload: the native draft
+    attention of the first decode step's gamma draft steps (step j over S + j keys),
+    every kv head; returns the mean seconds per draft step and the threads used."""
     from oracle import attention as OA
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover - threadpoolctl is optional
         threads = len(os.sched_getaffinity(0))
-    qg = q[g * G:(g + 1) * G]
-    Kg = K[:, g:g + 1, :]
-    Vg = V[:, g:g + 1, :]
     t0 = time.perf_counter()
-    OA.draft_full(qg, Kg, Vg, L, 1.0)
+    for j, q in enumerate(qs, start=1):
+        for g in range(Hkv):
+            OA.draft_full(q[g * G:(g + 1) * G], K[:, g:g + 1, :], V[:, g:g + 1, :], S + j, 1.0)
     dt = time.perf_counter() - t0
-    return dt, threads
+    return dt / len(qs), threads
 
 
 def kernel_source_hash() -> str:
@@ -414,13 +414,14 @@ def main() -> int:
             "bytes_per_launch": int(attn8_bytes)},
     }
     if not args.no_cpu_baseline:
-        log("cpu baseline (oracle, one kv head of one native draft step)")
-        q0 = qd_host[0][0]
-        dt, threads = cpu_baseline(Kd, Vd, q0, S + 1, G)
+        log("cpu baseline (oracle, the native draft steps of one decode step)")
+        qs = [qd_host[j][0] for j in range(gamma)]
+        dt, threads = cpu_baseline(Kd, Vd, qs, S, G, Hkv)
         out["cpu_baseline"] = {
-            "value": round(dt * Hkv * 1e6, 1), "unit": "us/step", "cores": threads, "kind": "oracle",
-            "sample": f"float64 oracle, native draft attention of kv head 1 ({G} query rows) over "
-                      f"{S + 1} keys, timed once and scaled x{Hkv} to one draft step",
+            "value": round(dt * 1e6, 1), "unit": "us/step", "cores": threads, "kind": "oracle",
+            "sample": f"float64 oracle, native draft attention of the {gamma} draft steps of one "
+                      f"decode step ({S + 1}..{S + gamma} keys, all {Hkv} kv heads, {Hq} query "
+                      f"rows), mean per draft step",
         }
     print(json.dumps(out), flush=True)
     return 0
