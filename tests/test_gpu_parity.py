@@ -683,3 +683,47 @@ def test_fp8_draft_full_and_window(cfg_name, S, k_scale, v_scale, num_splits):
     compare(o[0], l[0], ro, rl, f"fp8 full {cfg_name} S={S}")
     rwo, rwl = OA.draft_window(q[0], c["Kq"], c["Vq"], S, cfg["n_sink"], cfg["n_recent"], 1.0)
     compare(ow[0], lw[0], rwo, rwl, f"fp8 window {cfg_name} S={S}")
+
+
+def test_draft_context_pass_batch_of_two():
+    """Two rings at different lengths (one not yet full): each request's queries
+    sit at its own ring_T - n_q + i."""
+    lib = _lib()
+    from long_context_decode_attention_amd import scenario as scn
+    cfg = CFG["ctx128k_g32x4_d128"]
+    Hq, Hkv, D = cfg["Hq"], cfg["Hkv"], cfg["D"]
+    C, ns, nr, n_q = 1088, 4, 1020, 8
+    lens = [5000, 700]
+    ring = lib.new_ring(2, C, Hkv, D, ns, nr)
+    scn.poison(ring.k)
+    scn.poison(ring.v)
+    KV = []
+    for b, L in enumerate(lens):
+        K = W.kv_positions(140 + b, "draft_k", b, 0, L, Hkv, D)
+        V = W.kv_positions(140 + b, "draft_v", b, 0, L, Hkv, D)
+        scn.fill_ring(ring, b, K, V)
+        KV.append((K, V))
+    q = W.queries(141, "q_ctx", (2, n_q, Hq), D)
+    o, l = lib.draft_context_window(dev_bf16(q), ring, 1.0)
+    torch().cuda.synchronize()
+    for b, L in enumerate(lens):
+        ro, rl = OA.draft_context_window(q[b], KV[b][0], KV[b][1], L, ns, nr, 1.0)
+        compare(o[b], l[b], ro, rl, f"context pass b={b} L={L}")
+
+
+def test_verify_tree_ragged_batch():
+    """Two sequences of different lengths, each with its own tree."""
+    lib = _lib()
+    cfg = CFG["ctx1m_g32x2_d256"]
+    n_q = 8
+    vs = VerifyScenario(cfg, 150, [3000, 7777], n_q)
+    vs.append_proposed()
+    masks = [_tree_masks(n_q, "binary"), _tree_masks(n_q, "star")]
+    tm = torch().tensor(masks, dtype=torch().int64, device="cuda")
+    lens = vs.lens()
+    o, l = lib.verify_attn_tree(dev_bf16(vs.q), vs.kv.k, vs.kv.v, vs.kv.block_table, dev_i32(lens),
+                                tm, max(lens), 1.0)
+    torch().cuda.synchronize()
+    for b in range(2):
+        ro, rl = OA.verify_tree(vs.q[b], vs.K[b], vs.V[b], lens[b], masks[b], 1.0)
+        compare(o[b], l[b], ro, rl, f"tree verify b={b}")
