@@ -4,7 +4,8 @@ One benchmark step is one pass of the whole hot path over the 1M-context
 workload (batch 1, 32 query / 2 kv heads, head_dim 256, 64-token pages in a
 seeded permutation, draft depth 7, window 4 + 4092, verify of 8 causal queries):
 
-  windowed arm   7 x (ring append + windowed draft attention)
+  windowed arm   7 x (windowed draft step: the window over the ring plus the new
+                 position in one launch, then the merge and the ring append in a second)
   native arm     7 x (paged append + full draft attention split pass + combine)
   verify         paged append of the 8 proposed positions + verify attention
 
@@ -14,6 +15,11 @@ inputs are generated and uploaded before the timed region.  HIP events on the
 launch stream time every phase; the per-step cost of each arm is assembled as
 in the per-step cost identity: t_step = t_verify + sum of the arm's draft steps
 (append + attention).
+
+Also timed beside them: the windowed arm as ring append + windowed attention
+(three launches per draft step), the windowed draft through a truncated index of
+the paged draft KV, the draft context pass, the verify of a tree of proposals and
+the native arm over fp8 draft KV.
 
 Prints one JSON line.  ``value`` is the windowed arm's decode-step time (us).
 """
@@ -130,6 +136,7 @@ def main() -> int:
     dkv = sc.alloc_paged_kv([S + d_extra], Hkv, D, W.page_permutation(seed, "draft_k", npd), dev)
     tkv = sc.alloc_paged_kv([S + t_extra], Hkv, D, W.page_permutation(seed, "target_k", npt), dev)
     ring = lib.new_ring(B, C, Hkv, D, n_sink, n_recent, dev)
+    ring_s = lib.new_ring(B, C, Hkv, D, n_sink, n_recent, dev)   # the windowed arm's ring
     # the draft context pass over a ring needs slack for its earlier queries'
     # windows (n_q - 1 positions): a second ring with 64 more slots
     n_ctx = gamma + 1
@@ -137,6 +144,7 @@ def main() -> int:
     sc.fill_paged(dkv, 0, 0, Kd[:S], Vd[:S])
     sc.fill_paged(tkv, 0, 0, Kt[:S], Vt[:S])
     sc.fill_ring(ring, 0, Kd[:S], Vd[:S])
+    sc.fill_ring(ring_s, 0, Kd[:S], Vd[:S])
     sc.fill_ring(ring_c, 0, Kd[:S], Vd[:S])
     # the same draft KV as fp8 e4m3 codes (scales 1: N(0, 1) values fit), same pages
     k8, v8 = lib.new_paged_cache_fp8(dkv.num_pages, Hkv, D, dev)
@@ -182,6 +190,9 @@ def main() -> int:
     o_p = torch.empty(B, Hq, D, device=dev)
     l_p = torch.empty(B, Hq, device=dev)
     ws_w = lib.new_workspace(lib.workspace_bytes(B, Hq, Hkv, D, 1, C, ring=True), dev)
+    ws_s = lib.new_workspace(lib.step_workspace_bytes(B, Hq, Hkv, D, C), dev)
+    o_s = torch.empty(B, Hq, D, device=dev)
+    l_s = torch.empty(B, Hq, device=dev)
     ws_p = lib.new_workspace(lib.workspace_bytes(B, Hq, Hkv, D, 1, n_sink + n_recent,
                                                  paged_window=True), dev)
     ws_f = lib.new_workspace(lib.workspace_bytes(B, Hq, Hkv, D, 1, max_d, args.num_splits,
@@ -220,6 +231,10 @@ def main() -> int:
         for j in range(gamma):
             win.append(lib.ring_append(ring, kd_new[k, j], vd_new[k, j], prepare=True))
             win.append(lib.draft_attn_window(qd[k, j], ring, 1.0, o_w, l_w, ws_w, prepare=True))
+        # the windowed arm's draft steps: window attention over the ring plus the
+        # new position in one launch, the merge and the ring append in a second
+        fused = [lib.draft_step_window(qd[k, j], ring_s, kd_new[k, j], vd_new[k, j], 1.0, o_s, l_s,
+                                       ws_s, prepare=True) for j in range(gamma)]
         full = []
         for j in range(gamma):
             full.append((
@@ -265,15 +280,19 @@ def main() -> int:
                 lib.split_combine(*lib.partials_view(ws_8, B, Hq, Hkv, D, 1, max_d, args.num_splits),
                                   B, Hkv, G, 1, splits_per_group=splits_f,
                                   o=o_8.view(B, 1, Hq, D), lse=l_8.view(B, 1, Hq), prepare=True)))
-        plan.append((win, full, wpg, ver, ctx, full8))
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(11 + 4 * gamma)]
+        plan.append((win, full, wpg, ver, ctx, full8, fused))
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(13 + 4 * gamma)]
            for _ in range(nsteps)]
 
     def step(k):
-        win, full, wpg, ver, ctx, full8 = plan[k]
+        win, full, wpg, ver, ctx, full8, fused = plan[k]
         e = evs[k]
+        e[11 + 4 * gamma].record(stream)
+        for c in fused:                     # windowed arm: gamma x fused draft step
+            c()
+        e[12 + 4 * gamma].record(stream)
         e[0].record(stream)
-        for c in win:                       # windowed arm: gamma x (ring append + attention)
+        for c in win:                       # the same as ring append + window attention
             c()
         e[1].record(stream)
         for j, (app, attn, comb) in enumerate(full):   # native arm
@@ -304,7 +323,8 @@ def main() -> int:
             e[11 + 2 * gamma + 2 * j].record(stream)
             comb()
         e[9 + 2 * gamma].record(stream)
-        return {"t0": e[0], "t1": e[1], "t2": e[2], "p1": e[5 + 2 * gamma], "v0": e[3],
+        return {"s0": e[11 + 4 * gamma], "s1": e[12 + 4 * gamma],
+                "t0": e[0], "t1": e[1], "t2": e[2], "p1": e[5 + 2 * gamma], "v0": e[3],
                 "t3": e[4], "c1": e[6 + 2 * gamma], "c2": e[7 + 2 * gamma],
                 "c3": e[8 + 2 * gamma], "f8": e[9 + 2 * gamma],
                 "attn8": [(e[10 + 2 * gamma + 2 * j], e[11 + 2 * gamma + 2 * j]) for j in range(gamma)],
@@ -332,7 +352,8 @@ def main() -> int:
     def us(a, b):
         return a.elapsed_time(b) * 1000.0
 
-    win_chain = np.median([us(m["t0"], m["t1"]) for m in marks])
+    win3_chain = np.median([us(m["t0"], m["t1"]) for m in marks])   # append, then window
+    win_chain = np.median([us(m["s0"], m["s1"]) for m in marks])    # the fused step
     full_chain = np.median([us(m["t1"], m["t2"]) for m in marks])
     wpg_chain = np.median([us(m["t2"], m["p1"]) for m in marks])
     ctx_win = np.median([us(m["t3"], m["c1"]) for m in marks])
@@ -385,11 +406,13 @@ def main() -> int:
                                    "full_fp8_kv": round(float(full8_chain / gamma), 2),
                                    "full_fp8_kv_attention_kernel": round(attn8_mean, 2),
                                    "window": round(float(win_step_us), 2),
+                                   "window_append_then_attend": round(float(win3_chain / gamma), 2),
                                    "window_paged_index": round(float(wpg_chain / gamma), 2),
                                    "full_attention_kernel": round(attn_mean, 2)},
         "decode_step_us": {"full": round(float(step_full), 2), "window": round(float(step_window), 2),
                            "full_fp8_kv": round(float(verify_us + full8_chain), 2),
                            "window_paged_index": round(float(verify_us + wpg_chain), 2),
+                           "window_append_then_attend": round(float(verify_us + win3_chain), 2),
                            "verify": round(float(verify_us), 2),
                            "verify_kernel": round(float(verify_kernel_us), 2),
                            "verify_tree_kernel": round(float(tree_us), 2)},

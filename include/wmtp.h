@@ -84,6 +84,7 @@ const char* wmtp_status_string(wmtp_status s);
 #define WMTP_CALL_PAGED 0        /* wmtp_draft_attn_full, wmtp_verify_attn */
 #define WMTP_CALL_RING 1         /* wmtp_draft_attn_window */
 #define WMTP_CALL_PAGED_WINDOW 2 /* wmtp_draft_attn_window_paged */
+#define WMTP_CALL_RING_STEP 3    /* wmtp_draft_step_window (n_q = 1, max_keys = C) */
 
 /*
  * Split plan of the attention calls.  n_q = 1 for the draft calls;
@@ -267,6 +268,45 @@ wmtp_status wmtp_draft_context_window(const uint16_t* q, const uint16_t* ring_k,
                                       float softmax_scale, float* o, float* lse, void* workspace,
                                       size_t workspace_bytes, int num_splits, unsigned flags,
                                       void* stream);
+
+/*
+ * One windowed draft step: append n_new positions to each request's ring and
+ * attend over the window that ends with them, in two launches instead of the
+ * three of wmtp_ring_append + wmtp_draft_attn_window.  (Verdict page, key
+ * machinery: per draft step the draft appends its new K/V and reads only the
+ * sink plus the recent window; referee minor comment on App. A: the draft KV
+ * lives in the ring.)  The result and the ring afterwards are those of
+ * wmtp_ring_append(k_new, v_new) followed by wmtp_draft_attn_window with the
+ * same arguments: the query attends over positions p < L = ring_T[b] + n_new
+ * with p < n_sink or p >= L - n_recent, the new positions included.
+ * How: the first launch reads the ring as it stands with the window ending at
+ * L (the slots the new positions will take hold positions outside that
+ * window) and, in one more workgroup per (request, kv head), the new positions
+ * straight from k_new / v_new; the second merges the partial results and
+ * appends the new positions to the rings.
+ *   q                bf16 [B][Hq][D]; Hq / Hkv <= 32 (else WMTP_ERR_UNSUPPORTED)
+ *   ring_k, ring_v   bf16 tiled pages (in/out), B * C / 64 pages
+ *   ring_pos         int32 [B][C] (in/out)
+ *   ring_T           int64 [B] (in/out); negative values count as 0, values
+ *                    must stay below 2^31 - 64
+ *   k_new, v_new     bf16 [B][n_new][Hkv][D], row-major; 1 <= n_new <= 32
+ *   B, n_new, Hq, Hkv, D, C, n_sink, n_recent   (host) as wmtp_draft_attn_window
+ *   softmax_scale, o, lse, stream   as in wmtp_draft_attn_full (o is required)
+ *   workspace, workspace_bytes      wmtp_workspace_bytes(WMTP_CALL_RING_STEP, B,
+ *                    Hq, Hkv, D, 1, C, num_splits, 0) bytes: the partials of
+ *                    B * Hkv * (splits + 1) workgroups, in the layout described
+ *                    there with splits + 1 partials per group (the last one
+ *                    holds the new positions)
+ *   num_splits       ring splits per (request, kv head); 0 = as the windowed
+ *                    draft plans them
+ * Errors as wmtp_draft_attn_window; the workspace is checked as there.
+ */
+wmtp_status wmtp_draft_step_window(const uint16_t* q, uint16_t* ring_k, uint16_t* ring_v,
+                                   int32_t* ring_pos, int64_t* ring_T, const uint16_t* k_new,
+                                   const uint16_t* v_new, int B, int n_new, int Hq, int Hkv, int D,
+                                   int C, int n_sink, int n_recent, float softmax_scale, float* o,
+                                   float* lse, void* workspace, size_t workspace_bytes,
+                                   int num_splits, void* stream);
 
 /*
  * Append n_new consecutive positions to each request's draft ring.

@@ -28,7 +28,7 @@ EXPORTS = (
     "wmtp_draft_attn_full", "wmtp_draft_attn_window", "wmtp_draft_attn_window_paged",
     "wmtp_draft_context_window", "wmtp_verify_attn_tree", "wmtp_paged_append_fp8",
     "wmtp_draft_attn_full_fp8", "wmtp_draft_attn_window_paged_fp8", "wmtp_ring_append",
-    "wmtp_paged_append", "wmtp_verify_attn", "wmtp_split_combine",
+    "wmtp_paged_append", "wmtp_verify_attn", "wmtp_split_combine", "wmtp_draft_step_window",
 )
 
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration",
@@ -65,6 +65,7 @@ _SIGS = {
     "wmtp_draft_attn_window_paged_fp8": ([_P] * 5 + [_I] * 9 + [_F, _F, _F, _P, _P, _P, _SZ, _I, _U, _P],
                                          _I),
     "wmtp_ring_append": ([_P] * 6 + [_I] * 6 + [_P], _I),
+    "wmtp_draft_step_window": ([_P] * 7 + [_I] * 8 + [_F, _P, _P, _P, _SZ, _I, _P], _I),
     "wmtp_paged_append": ([_P] * 6 + [_I] * 6 + [_P], _I),
     "wmtp_verify_attn": ([_P] * 5 + [_I] * 8 + [_F, _P, _P, _P, _SZ, _I, _U, _P], _I),
     "wmtp_split_combine": ([_P, _P, _I, _P] + [_I] * 6 + [_P, _P, _P], _I),
@@ -219,6 +220,7 @@ def new_ring(B: int, C: int, Hkv: int, D: int, n_sink: int, n_recent: int, devic
 CALL_PAGED = 0
 CALL_RING = 1
 CALL_PAGED_WINDOW = 2
+CALL_RING_STEP = 3
 
 
 def _call_kind(ring, paged_window):
@@ -240,6 +242,19 @@ def workspace_bytes(B, Hq, Hkv, D, n_q, max_keys, num_splits=0, partials_only=Fa
                     ring=False, paged_window=False) -> int:
     return int(load().wmtp_workspace_bytes(_call_kind(ring, paged_window), B, Hq, Hkv, D, n_q,
                                            max_keys, num_splits, 1 if partials_only else 0))
+
+
+def step_splits(B, Hq, Hkv, D, C, num_splits=0) -> int:
+    """Ring splits per (request, kv head) of ``draft_step_window`` (each group then
+    has that many plus one partials)."""
+    n = load().wmtp_plan_splits(CALL_RING_STEP, B, Hq, Hkv, D, 1, C, num_splits)
+    if n < 0:
+        raise WmtpError("wmtp_plan_splits", 1)
+    return n
+
+
+def step_workspace_bytes(B, Hq, Hkv, D, C, num_splits=0) -> int:
+    return int(load().wmtp_workspace_bytes(CALL_RING_STEP, B, Hq, Hkv, D, 1, C, num_splits, 0))
 
 
 def new_workspace(nbytes: int, device="cuda"):
@@ -453,6 +468,35 @@ def draft_context_window(q, ring: Ring, softmax_scale=1.0, o=None, lse=None, wor
     if prepare:
         return c
     return workspace if partials_only else (o, lse)
+
+
+def draft_step_window(q, ring: Ring, k_new, v_new, softmax_scale=1.0, o=None, lse=None,
+                      workspace=None, num_splits=0, stream=None, prepare=False):
+    """One windowed draft step in two launches (``wmtp_draft_step_window``): append
+    k_new, v_new (bf16 [B, n_new, Hkv, D]) to the rings and attend over the
+    window ending with them; q is [B, Hq, D]."""
+    torch = _torch()
+    B, Hq, D = q.shape
+    n_new = k_new.shape[1]
+    Hkv, C = ring.Hkv, ring.C
+    _need(q, torch.bfloat16, None, "q")
+    _need(ring.k, torch.bfloat16, k_cache_shape(B * C // PAGE, Hkv, D), "ring.k")
+    _need(ring.v, torch.bfloat16, v_cache_shape(B * C // PAGE, Hkv, D), "ring.v")
+    _need(ring.pos, torch.int32, (B, C), "ring.pos")
+    _need(ring.T, torch.int64, (B,), "ring.T")
+    _need(k_new, torch.bfloat16, (B, n_new, Hkv, D), "k_new")
+    _need(v_new, torch.bfloat16, (B, n_new, Hkv, D), "v_new")
+    if workspace is None:
+        workspace = new_workspace(step_workspace_bytes(B, Hq, Hkv, D, C, num_splits), q.device)
+    _need(workspace, torch.uint8, None, "workspace")
+    o, lse = _outputs(o, lse, (B, Hq, D), (B, Hq), q.device)
+    c = _invoke("wmtp_draft_step_window", (
+        _ptr(q), _ptr(ring.k), _ptr(ring.v), _ptr(ring.pos), _ptr(ring.T), _ptr(k_new), _ptr(v_new), B, n_new, Hq, Hkv, D, C, ring.n_sink, ring.n_recent,
+        float(softmax_scale), _ptr(o), _ptr(lse), _ptr(workspace), workspace.numel(),
+        int(num_splits), _stream(stream)), prepare)
+    if prepare:
+        return c
+    return o, lse
 
 
 def ring_append(ring: Ring, k_new, v_new, stream=None, prepare=False):

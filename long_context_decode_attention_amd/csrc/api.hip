@@ -67,7 +67,7 @@ wmtp_status run_attention(AttnArgs a, bool ring, int max_keys, int plan_keys, fl
   hipError_t e = launch_attention(a, p, ring, stream);
   if (e != hipSuccess) return WMTP_ERR_HIP;
   if (p.direct || partials_only) return WMTP_OK;
-  CombineArgs c;
+  CombineArgs c = {};
   c.part_o = part_o;
   c.part_lse = part_lse;
   c.indptr = nullptr;
@@ -106,6 +106,10 @@ const char* wmtp_status_string(wmtp_status s) {
 int wmtp_plan_splits(int call, int B, int Hq, int Hkv, int D, int n_q, int max_keys,
                      int num_splits) {
   AttnPlan p;
+  if (call == WMTP_CALL_RING_STEP) {
+    if (n_q != 1 || !plan_window_step(B, Hq, Hkv, D, max_keys, num_splits, &p)) return -1;
+    return p.nsplit;
+  }
   if (call != WMTP_CALL_PAGED && call != WMTP_CALL_RING && call != WMTP_CALL_PAGED_WINDOW)
     return -1;
   if (call == WMTP_CALL_PAGED_WINDOW) {
@@ -120,6 +124,10 @@ int wmtp_plan_splits(int call, int B, int Hq, int Hkv, int D, int n_q, int max_k
 size_t wmtp_workspace_bytes(int call, int B, int Hq, int Hkv, int D, int n_q, int max_keys,
                             int num_splits, int partials_only) {
   AttnPlan p;
+  if (call == WMTP_CALL_RING_STEP) {
+    if (n_q != 1 || !plan_window_step(B, Hq, Hkv, D, max_keys, num_splits, &p)) return 0;
+    return p.ws_bytes;
+  }
   if (call != WMTP_CALL_PAGED && call != WMTP_CALL_RING && call != WMTP_CALL_PAGED_WINDOW)
     return 0;
   if (call == WMTP_CALL_PAGED_WINDOW) {
@@ -338,6 +346,98 @@ wmtp_status wmtp_draft_context_window(const uint16_t* q, const uint16_t* ring_k,
                         flags, stream);
 }
 
+wmtp_status wmtp_draft_step_window(const uint16_t* q, uint16_t* ring_k, uint16_t* ring_v,
+                                   int32_t* ring_pos, int64_t* ring_T, const uint16_t* k_new,
+                                   const uint16_t* v_new, int B, int n_new, int Hq, int Hkv, int D,
+                                   int C, int n_sink, int n_recent, float softmax_scale, float* o,
+                                   float* lse, void* workspace, size_t workspace_bytes,
+                                   int num_splits, void* stream) {
+  if (!attn_dims_ok(B, Hq, Hkv, D)) return WMTP_ERR_INVALID_ARG;
+  if (!head_dim_ok(D)) return WMTP_ERR_UNSUPPORTED;
+  if (Hq / Hkv > 32) return WMTP_ERR_UNSUPPORTED;
+  if (n_new < 1 || n_new > 32 || num_splits < 0) return WMTP_ERR_INVALID_ARG;
+  if (C < 64 || C % 64 != 0 || n_sink < 0 || n_sink >= C || n_recent < 1 ||
+      n_recent > C - n_sink)
+    return WMTP_ERR_INVALID_ARG;
+  if ((long)B * C > (long)INT_MAX) return WMTP_ERR_INVALID_ARG;
+  // the kernels take row maxima of raw scores before scaling: the scale must be positive
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return WMTP_ERR_INVALID_ARG;
+  if (!q || !ring_k || !ring_v || !ring_pos || !ring_T || !k_new || !v_new || !o)
+    return WMTP_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(ring_k) || !aligned16(ring_v) || !aligned16(ring_pos) ||
+      !aligned8(ring_T) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(o) ||
+      (lse && !aligned4(lse)))
+    return WMTP_ERR_INVALID_ARG;
+  AttnPlan p;
+  if (!plan_window_step(B, Hq, Hkv, D, C, num_splits, &p)) return WMTP_ERR_INVALID_ARG;
+  if (!workspace || !aligned16(workspace) || workspace_bytes < p.ws_bytes)
+    return WMTP_ERR_WORKSPACE;
+  RingAppendArgs app;
+  app.kc = ring_k;
+  app.vc = ring_v;
+  app.ring_pos = ring_pos;
+  app.ring_T = ring_T;
+  app.k_new = k_new;
+  app.v_new = v_new;
+  app.B = B;
+  app.n_new = n_new;
+  app.Hkv = Hkv;
+  app.D = D;
+  app.C = C;
+  app.n_sink = n_sink;
+  // launch 1: the window over the ring as it stands, ending after the new
+  // positions, plus one workgroup per group over the new positions themselves
+  AttnArgs a = {};
+  a.q = q;
+  a.kc = ring_k;
+  a.vc = ring_v;
+  a.ring_pos = ring_pos;
+  a.ring_T = ring_T;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.n_q = 1;
+  a.D = D;
+  a.G = p.G;
+  a.R = p.R;
+  a.num_pages = B * (C / 64);
+  a.max_pages = C / 64;
+  a.max_keys = C;
+  a.C = C;
+  a.n_sink = n_sink;
+  a.n_recent = n_recent;
+  a.scale_log2 = softmax_scale * kLog2e;
+  a.nsplit = p.nsplit;
+  a.kb_per_split = p.kb_per_split;
+  a.items = p.items;
+  a.nrg = 1;
+  a.direct = 0;
+  a.out_o = static_cast<float*>(workspace);
+  a.out_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.lse_offset);
+  a.app = app;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (launch_window_step(a, p, st) != hipSuccess) return WMTP_ERR_HIP;
+  // launch 2: merge the nsplit + 1 partials of each group, and append the new
+  // positions to the rings (every read of the rings has finished by then)
+  CombineArgs c = {};
+  c.part_o = a.out_o;
+  c.part_lse = a.out_lse;
+  c.indptr = nullptr;
+  c.n_parts = p.items;
+  c.splits_per_group = p.nsplit + 1;
+  c.B = B;
+  c.Hkv = Hkv;
+  c.G = p.G;
+  c.n_q = 1;
+  c.D = D;
+  c.R = p.R;
+  c.o = o;
+  c.lse = lse;
+  c.append = 1;
+  c.app = app;
+  return from_hip(launch_combine(c, st));
+}
+
 wmtp_status wmtp_ring_append(uint16_t* ring_k, uint16_t* ring_v, int32_t* ring_pos,
                              int64_t* ring_T, const uint16_t* k_new, const uint16_t* v_new,
                              int B, int n_new, int Hkv, int D, int C, int n_sink, void* stream) {
@@ -434,7 +534,7 @@ wmtp_status wmtp_split_combine(const float* part_o, const float* part_lse, int n
   if (!aligned16(part_o) || !aligned4(part_lse) || !aligned16(o) || (lse && !aligned4(lse)) ||
       (split_indptr && !aligned4(split_indptr)))
     return WMTP_ERR_INVALID_ARG;
-  CombineArgs c;
+  CombineArgs c = {};
   c.part_o = part_o;
   c.part_lse = part_lse;
   c.indptr = split_indptr;

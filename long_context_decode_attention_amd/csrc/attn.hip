@@ -17,6 +17,7 @@
 // products have consumed the current ones, V likewise after PV, so one tile of
 // each is always in flight.
 #include "attn_device.h"
+#include "ring_device.h"
 
 #include <type_traits>
 
@@ -34,6 +35,7 @@
 namespace wmtp {
 
 namespace {
+
 
 // KV8: the operands stay as loaded (8 fp8 bytes) until their MFMA.
 template <int D, bool RING, bool KV8>
@@ -62,11 +64,6 @@ __device__ __forceinline__ size_t tile_index(const AttnArgs& a, int b, int g, in
   ok = (unsigned)ppage < (unsigned)a.num_pages;
   if (!ok) ppage = 0;   // still loaded (so that every load is unconditional), then ignored
   return ((size_t)ppage * a.Hkv + g) * 2 + (kb & 1);
-}
-
-// First 32-key tile of the split of workgroup item `item`.
-__device__ __forceinline__ int kb0_of(const AttnArgs& a, int item) {
-  return (item % a.nsplit) * a.kb_per_split;
 }
 
 // Tile index of tile kb of kv head g on physical page `ppage` (paged caches), with
@@ -124,6 +121,53 @@ __device__ __forceinline__ void load_v(VTile<D, KV8>& t, const AttnArgs& a, size
   }
 }
 
+// Fused draft step: K operands of the tile of new positions (key j = position
+// T0 + j of app.k_new, j < n_new; the other keys load key 0 and are marked
+// absent), with the positions the window test reads.
+template <int D>
+__device__ __forceinline__ void load_k_new(KTile<D, true, false>& t, const AttnArgs& a, int b, int g,
+                                           int T0, int m, int h) {
+  const int key = s_row_key(m);
+  const int kk = key < a.app.n_new ? key : 0;
+  const uint16_t* src = a.app.k_new + (((size_t)b * a.app.n_new + kk) * a.Hkv + g) * D + 8 * h;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) t.k[ks] = ld_bf16x8(src + 16 * ks);
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int j = 16 * r + 8 * h + i;
+      t.pos[8 * r + i] = j < a.app.n_new ? T0 + j : -1;
+    }
+}
+
+// V^T of the new positions, staged in LDS as [D][32 keys] bf16 (keys >= n_new
+// left as they are: the window test marks them absent and PV zeroes them).
+template <int D>
+__device__ __forceinline__ void stage_v_new(uint16_t* sm_vt, const AttnArgs& a, int b, int g) {
+  const int pieces = a.app.n_new * (D / 8);
+  for (int idx = threadIdx.x; idx < pieces; idx += 256) {
+    const int j = idx / (D / 8);
+    const int d0 = (idx - j * (D / 8)) * 8;
+    const u32x4 w = *reinterpret_cast<const u32x4*>(
+        a.app.v_new + (((size_t)b * a.app.n_new + j) * a.Hkv + g) * D + d0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sm_vt[(d0 + 2 * e) * 32 + j] = (uint16_t)(w[e] & 0xFFFFu);
+      sm_vt[(d0 + 2 * e + 1) * 32 + j] = (uint16_t)(w[e] >> 16);
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void load_v_new(VTile<D, false>& t, const uint16_t* sm_vt, int m, int h) {
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+      t.v[db][kk] = *reinterpret_cast<const bf16x8*>(sm_vt + (32 * db + m) * 32 + 16 * kk + 8 * h);
+}
+
 // Which of this lane's 16 keys exist for every row: inside the sequence length
 // (and, for a truncated paged index, below sink_end or from r0 on), or (ring)
 // holding a position of the current window.
@@ -149,8 +193,9 @@ __device__ __forceinline__ uint32_t present_keys(const KTile<D, RING, KV8>& t, c
   }
 }
 
-template <int D, int NB, bool RING, bool KV8>
+template <int D, int NB, bool RING, bool KV8, bool STEP = false>
 __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
+  static_assert(!STEP || (RING && !KV8 && NB == 1), "the fused step reads a bf16 ring");
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
   const int lane = threadIdx.x & 63;
@@ -173,8 +218,12 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
     item = (k / a.nrg) * 8 + (w & 7);
   }
   if (item >= a.items) return;
-  const int s = item % a.nsplit;
-  const int bg = item / a.nsplit;
+  // fused step: each group has a.nsplit ring splits and then one workgroup that
+  // reads the new positions (split index a.nsplit)
+  const int nparts = STEP ? a.nsplit + 1 : a.nsplit;
+  const int s = item % nparts;
+  const int bg = item / nparts;
+  const bool newk = STEP && s == a.nsplit;
   const int g = bg % a.Hkv;
   const int b = bg / a.Hkv;
   const int row0 = rg * 32 * NB;
@@ -186,13 +235,18 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
   // loads go out first, then the wave's first tile, and only then are the Q
   // values stored and published, so that the two memory latencies overlap.
   __shared__ bf16x8 sm_q[NB][KS][64];
+  // the four waves' O^T chunks for the final merge (fused step: first the V^T
+  // staging of the new positions, which is consumed before the merge starts)
+  constexpr int U = DB * 4;
+  __shared__ f32x4 sm_acc[4][U][64];
+  static_assert(sizeof(sm_acc) >= D * 32 * sizeof(uint16_t), "V^T staging fits the merge buffer");
   constexpr int kQPer = NB * KS * 64 / 256;   // Q operands per thread
   static_assert(kQPer * 256 == NB * KS * 64, "Q operands split evenly over the threads");
   // The sequence length and the wave's first page id are read first: the tile
   // loads depend on them.
   const int len_raw = RING ? 0 : a.seq_lens[b];
   const int64_t t64 = RING ? a.ring_T[b] : 0;
-  const int kb_first = kb0_of(a, item) + wave;
+  const int kb_first = s * a.kb_per_split + wave;
   const int page_first =
       RING ? 0 : a.block_table[(size_t)b * a.max_pages + min(kb_first >> 1, a.max_pages - 1)];
   bf16x8 qv[kQPer];
@@ -211,10 +265,15 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
     qv[r] = ld_bf16x8(a.q + ((size_t)(b * a.n_q + qi) * a.Hq + g * a.G + hl) * D + ks * 16 +
                       (ln >> 5) * 8);
   }
-  int L, T = 0;
+  int L, T = 0, T0 = 0;
   if (RING) {
     L = a.C;
-    T = t64 < 0 ? 0 : (t64 > (int64_t)INT_MAX ? INT_MAX : (int)t64);
+    const int64_t t_max = STEP ? INT_MAX - 64 : INT_MAX;   // step: room for the new positions
+    T = t64 < 0 ? 0 : (t64 > t_max ? (int)t_max : (int)t64);
+    // fused step: the window ends after the new positions; the slots they will
+    // overwrite hold positions outside it, so the window test skips them
+    T0 = T;
+    if (STEP) T += a.app.n_new;
   } else {
     L = len_raw < 0 ? 0 : (len_raw > a.max_keys ? a.max_keys : len_raw);
   }
@@ -231,8 +290,8 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
     nvt = st_end + max(nkb - kr, 0);
   }
   auto phys = [&](int u) { return (!RING && a.win && u >= st_end) ? kr + (u - st_end) : u; };
-  const int kb0 = s * a.kb_per_split;
-  const int kb1 = min(kb0 + a.kb_per_split, nvt);
+  const int kb0 = newk ? 0 : s * a.kb_per_split;
+  const int kb1 = newk ? 1 : min(kb0 + a.kb_per_split, nvt);   // new positions: one tile
   asm volatile("" ::: "memory");
   // Loop over this wave's tiles.  K registers are refilled with the next tile as
   // soon as the S^T products have consumed them, V registers as soon as the PV
@@ -248,15 +307,28 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
     // that the Q stores below wait only for the Q loads
     const int kbl = kb < kb1 ? kb : 0;
     size_t tile;
-    if (RING) {
+    if (newk) {
+      tile = 0;
+    } else if (RING) {
       tile = tile_index<RING>(a, b, g, kbl, ok);
     } else if (a.win) {   // the page of the first tile depends on L here
       tile = tile_index<RING>(a, b, g, phys(kbl), ok);
     } else {
       tile = tile_of_page(a, kb < kb1 ? page_first : 0, g, kbl, ok);
     }
-    load_k<D, RING, KV8>(kt, a, tile, b, kbl, m, h);
-    load_v<D, KV8>(vt, a, tile, m, h);
+    if constexpr (STEP) {
+      if (newk) {
+        load_k_new<D>(kt, a, b, g, T0, m, h);
+        ok = true;
+        stage_v_new<D>(reinterpret_cast<uint16_t*>(&sm_acc[0][0][0]), a, b, g);
+      } else {
+        load_k<D, RING, KV8>(kt, a, tile, b, kbl, m, h);
+        load_v<D, KV8>(vt, a, tile, m, h);
+      }
+    } else {
+      load_k<D, RING, KV8>(kt, a, tile, b, kbl, m, h);
+      load_v<D, KV8>(vt, a, tile, m, h);
+    }
   }
   asm volatile("" ::: "memory");
 #pragma unroll
@@ -267,6 +339,9 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
   // publish the staged Q: wait for this wave's LDS stores only, so the tile
   // loads stay in flight across the barrier
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if constexpr (STEP) {
+    if (newk) load_v_new<D>(vt, reinterpret_cast<const uint16_t*>(&sm_acc[0][0][0]), m, h);
+  }
   int lim[NB];
 #pragma unroll
   for (int rb = 0; rb < NB; ++rb) {
@@ -432,10 +507,8 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
   // Every wave stores its rescaled O^T chunks (chunk u = 4*db + c: dims
   // 32*db + 8*c + 4*h .. +3 of row m), then wave w sums and writes chunks
   // [w*U/4, (w+1)*U/4) of all four waves.
-  constexpr int U = DB * 4;
   __shared__ float sm_m[4][32];
   __shared__ float sm_l[4][32];
-  __shared__ f32x4 sm_acc[4][U][64];
 
 #pragma unroll
   for (int rb = 0; rb < NB; ++rb) {
@@ -506,7 +579,59 @@ hipError_t launch_d(const AttnArgs& a, const AttnPlan& p, bool ring, hipStream_t
                : launch_one<D, 1, false, false>(a, p.grid, stream);
 }
 
+template <int D>
+hipError_t launch_step_d(const AttnArgs& a, int grid, hipStream_t stream) {
+  AttnArgs arg = a;
+  void* args[] = {&arg};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_split_kernel<D, 1, true, false, true>),
+                         dim3(grid), dim3(256), args, 0, stream);
+}
+
 }  // namespace
+
+bool plan_window_step(int B, int Hq, int Hkv, int D, int C, int num_splits, AttnPlan* p) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || num_splits < 0 || C < 64 || C % 64 != 0)
+    return false;
+  if (D != 64 && D != 128 && D != 256) return false;
+  p->G = Hq / Hkv;
+  p->R = p->G;
+  if (p->R > 32) return false;
+  p->shared = 0;
+  p->nrb = 1;
+  p->nrg = 1;
+  p->nkb = C / 32;
+  // default: the windowed draft's plan (one workgroup per CU, at least four
+  // tiles, one per wave, per split)
+  int kbps;
+  if (num_splits > 0) {
+    kbps = (p->nkb + num_splits - 1) / num_splits;
+  } else {
+    const long units = (long)B * Hkv;
+    const long per_unit = units < WMTP_TARGET_WG_SPLIT ? WMTP_TARGET_WG_SPLIT / units : 1;
+    const long per = ((long)p->nkb + per_unit - 1) / per_unit;
+    kbps = (int)(per < 4 ? 4 : per);
+  }
+  p->kb_per_split = kbps;
+  p->nsplit = (p->nkb + kbps - 1) / kbps;
+  p->direct = 0;
+  const long items = (long)B * Hkv * (p->nsplit + 1);
+  if (items > INT_MAX / 16) return false;
+  p->items = (int)items;
+  p->grid = p->items;
+  p->part_o_bytes = (size_t)items * p->R * D * sizeof(float);
+  p->lse_offset = ((p->part_o_bytes + 255) / 256) * 256;
+  p->ws_bytes = p->lse_offset + (size_t)items * p->R * sizeof(float);
+  return true;
+}
+
+hipError_t launch_window_step(const AttnArgs& a, const AttnPlan& p, hipStream_t stream) {
+  switch (a.D) {
+    case 64: return launch_step_d<64>(a, p.grid, stream);
+    case 128: return launch_step_d<128>(a, p.grid, stream);
+    case 256: return launch_step_d<256>(a, p.grid, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 bool plan_attention(int B, int Hq, int Hkv, int D, int n_q, int max_keys, int num_splits,
                     int partials_only, bool ring, AttnPlan* p) {

@@ -15,6 +15,7 @@
 // does not depend on timing.
 #include "common.h"
 #include "internal.h"
+#include "ring_device.h"
 
 #include <cmath>
 
@@ -128,6 +129,14 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs c) {
   const int sl = t % SL;
   const int cl = t / SL;
   const int nblk = c.D / (4 * CL);            // column-chunk blocks per row
+  if (c.append) {
+    // fused draft step: the workgroups after the combine's append to the rings
+    const int merge_blocks = c.B * c.Hkv * c.R * nblk;
+    if ((int)blockIdx.x >= merge_blocks) {
+      ring_append_block(c.app, blockIdx.x - merge_blocks);
+      return;
+    }
+  }
   const int blk = blockIdx.x % nblk;
   const int rest = blockIdx.x / nblk;
   const int row = rest % c.R;
@@ -196,7 +205,7 @@ hipError_t launch_sl(const CombineArgs& c, hipStream_t stream) {
   constexpr int CL = 256 / SL;
   CombineArgs arg = c;
   void* args[] = {&arg};
-  const long grid = (long)c.B * c.Hkv * c.R * (c.D / (4 * CL));
+  const long grid = (long)c.B * c.Hkv * c.R * (c.D / (4 * CL)) + (c.append ? c.app.B : 0);
   return hipLaunchKernel(reinterpret_cast<const void*>(&combine_kernel<SL>), dim3((unsigned)grid),
                          dim3(256), args, 0, stream);
 }
@@ -204,6 +213,7 @@ hipError_t launch_sl(const CombineArgs& c, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_combine(const CombineArgs& c, hipStream_t stream) {
+  if (c.append && c.R >= 64) return hipErrorInvalidValue;   // the append rides the few-row kernel
   if (c.R >= 64) {
     // CL: a power of two dividing D / 4, the widest that gives about 512 workgroups.
     const long pairs = (long)c.B * c.Hkv * c.R;

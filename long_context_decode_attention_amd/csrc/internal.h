@@ -7,6 +7,16 @@
 
 namespace wmtp {
 
+struct RingAppendArgs {
+  uint16_t* kc;
+  uint16_t* vc;
+  int32_t* ring_pos;
+  int64_t* ring_T;
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  int B, n_new, Hkv, D, C, n_sink;
+};
+
 // Arguments of the split-KV attention kernel (draft full, draft window, verify).
 struct AttnArgs {
   const uint16_t* q;            // bf16 [B][n_q][Hq][D]
@@ -34,6 +44,11 @@ struct AttnArgs {
   float v_scale;                // kv8: value of a V code = code value * v_scale (K's scale is
                                 // folded into scale_log2)
   float scale_log2;             // softmax_scale * log2(e)
+  // Fused windowed draft step (ring mode): the n_new positions ring_T ..
+  // ring_T + n_new - 1 come from app.k_new / app.v_new, read by one more
+  // workgroup per group (split index nsplit); the ring itself is read as it
+  // stands and written afterwards by the combine launch.
+  RingAppendArgs app;
 };
 
 struct AttnPlan {
@@ -48,6 +63,12 @@ bool plan_attention(int B, int Hq, int Hkv, int D, int n_q, int max_keys, int nu
                     int partials_only, bool ring, AttnPlan* p);
 
 hipError_t launch_attention(const AttnArgs& a, const AttnPlan& p, bool ring, hipStream_t stream);
+
+// Fused windowed draft step: ring splits as the windowed draft plans them, plus
+// one workgroup per group for the new positions; items = B * Hkv * (nsplit + 1)
+// partials of R = Hq / Hkv <= 32 rows.
+bool plan_window_step(int B, int Hq, int Hkv, int D, int C, int num_splits, AttnPlan* p);
+hipError_t launch_window_step(const AttnArgs& a, const AttnPlan& p, hipStream_t stream);
 hipError_t launch_attention_shared(const AttnArgs& a, const AttnPlan& p, hipStream_t stream);
 int shared_kernel_waves();
 int shared_kernel_max_tiles();   // most 32-key tiles one split of the shared kernel covers
@@ -61,19 +82,14 @@ struct CombineArgs {
   int B, Hkv, G, n_q, D, R;
   float* o;
   float* lse;              // may be null
+  // Fused windowed draft step: after the combine's workgroups, app.B more append
+  // app.n_new positions to the rings (one workgroup per request, as
+  // wmtp_ring_append does).  Only with R < 64.
+  int append;
+  RingAppendArgs app;
 };
 
 hipError_t launch_combine(const CombineArgs& c, hipStream_t stream);
-
-struct RingAppendArgs {
-  uint16_t* kc;
-  uint16_t* vc;
-  int32_t* ring_pos;
-  int64_t* ring_T;
-  const uint16_t* k_new;
-  const uint16_t* v_new;
-  int B, n_new, Hkv, D, C, n_sink;
-};
 
 hipError_t launch_ring_append(const RingAppendArgs& a, hipStream_t stream);
 

@@ -216,6 +216,41 @@ def test_plan_and_workspace_consistency():
         lib_mod.plan_splits(1, 32, 3, 256, 1, L)
 
 
+def test_fused_step_argument_checks_and_plan():
+    """wmtp_draft_step_window: host checks (nothing launched) and its plan: the
+    windowed draft's ring splits plus one partial per group for the new positions."""
+    lib = _lib()
+    P = ctypes.c_void_p
+
+    def step(**kw):
+        a = dict(B=1, n_new=1, Hq=32, Hkv=2, D=256, C=4096, ns=4, nr=4092, ws=None, wsb=0,
+                 scale=1.0, o=FAKE, kn=FAKE)
+        a.update(kw)
+        return lib.wmtp_draft_step_window(P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(a["kn"]),
+                                          P(FAKE), a["B"], a["n_new"], a["Hq"], a["Hkv"], a["D"],
+                                          a["C"], a["ns"], a["nr"], a["scale"], P(a["o"]), None,
+                                          P(a["ws"]) if a["ws"] else None, a["wsb"], 0, None)
+    assert step(n_new=0) == INVALID
+    assert step(n_new=33) == INVALID
+    assert step(kn=None) == INVALID
+    assert step(kn=FAKE + 8) == INVALID                # misaligned new K
+    assert step(o=None) == INVALID
+    assert step(scale=0.0) == INVALID
+    assert step(C=4100) == INVALID
+    assert step(nr=4093) == INVALID
+    assert step(Hq=128) == UNSUPPORTED                 # 64 query rows per kv head
+    assert step(D=96) == UNSUPPORTED
+    assert step() == WORKSPACE                         # no workspace
+    need = lib_mod.step_workspace_bytes(1, 32, 2, 256, 4096)
+    assert step(ws=FAKE, wsb=need - 1) == WORKSPACE
+    n = lib_mod.step_splits(1, 32, 2, 256, 4096)
+    assert n == lib_mod.plan_splits(1, 32, 2, 256, 1, 4096, ring=True)
+    parts = 2 * (n + 1)
+    assert need == (parts * 16 * 256 * 4 + 255) // 256 * 256 + parts * 16 * 4
+    assert lib_mod.step_splits(1, 32, 2, 256, 4096, 1) == 1
+    assert lib_mod.step_splits(1, 32, 2, 256, 4096, 1000) == 4096 // 32
+
+
 def _imports(path):
     names = set()
     for dirpath, _, files in os.walk(path):
