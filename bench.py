@@ -48,7 +48,7 @@ WORKLOAD = "ctx1m_g32x2_d256"
 # keyed by a hash of the sources that kernel is built from: a changed kernel
 # reports null until it is measured again.
 MEASURED_TRAFFIC = {
-    "5d798e59b091536a": {"read": 2.148e9, "write": 4.211e6, "keys": 1048587},
+    "dd441f4ae9bb37fd": {"read": 2.148e+09, "write": 4.211e+06, "keys": 1048587},
 }
 KERNEL_SOURCES = ("csrc/attn.hip", "csrc/attn_device.h", "csrc/common.h")
 

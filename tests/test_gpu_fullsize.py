@@ -32,6 +32,11 @@ def test_ctx1m_draft_chain_and_verify_full_size():
     G = cfg["Hq"] // cfg["Hkv"]
     _say("building draft state (1M positions, permuted pages, ring)")
     sc = DraftScenario(cfg, 100, [S], gamma, poison=False)
+    # the windowed arm as the benchmark runs it: the fused draft step on a second
+    # ring holding the same 1M positions
+    from long_context_decode_attention_amd import scenario as scn
+    ring2 = lib.new_ring(1, cfg["C"], cfg["Hkv"], cfg["D"], cfg["n_sink"], cfg["n_recent"])
+    scn.fill_ring(ring2, 0, sc.K[0][:S], sc.V[0][:S])
     outs = {}
     for j in range(1, gamma + 1):
         sc.append(j)
@@ -40,17 +45,25 @@ def test_ctx1m_draft_chain_and_verify_full_size():
         lens = sc.lens(j)
         of, lf = lib.draft_attn_full(qt, sc.kv.k, sc.kv.v, sc.kv.block_table, dev_i32(lens), lens[0])
         ow, lw = lib.draft_attn_window(qt, sc.ring)
-        outs[j] = (q, of, lf, ow, lw)
+        kn = dev_bf16(sc.K[0][S + j - 1][None, None])
+        vn = dev_bf16(sc.V[0][S + j - 1][None, None])
+        os_, ls_ = lib.draft_step_window(qt, ring2, kn, vn)
+        outs[j] = (q, of, lf, ow, lw, os_, ls_)
     torch().cuda.synchronize()
-    _say("draft chain done; oracle on kv head 1, steps 1 and 7")
+    t = torch()
+    assert t.equal(ring2.T, sc.ring.T) and t.equal(ring2.pos, sc.ring.pos)
+    assert t.equal(ring2.k.view(t.int16), sc.ring.k.view(t.int16))
+    assert t.equal(ring2.v.view(t.int16), sc.ring.v.view(t.int16))
+    _say("draft chain done (fused-step ring equals the appended ring); oracle on kv head 1, steps 1 and 7")
     for j in (1, gamma):
-        q, of, lf, ow, lw = outs[j]
+        q, of, lf, ow, lw, os_, ls_ = outs[j]
         L = S + j
         qg, Kg, Vg = _group(q[0], sc.K[0], sc.V[0], 1, G)
         ro, rl = OA.draft_full(qg, Kg, Vg, L, 1.0)
         compare(of[0, G:2 * G], lf[0, G:2 * G], ro, rl, f"full 1M step {j}")
         ro, rl = OA.draft_window(qg, Kg, Vg, L, cfg["n_sink"], cfg["n_recent"], 1.0)
         compare(ow[0, G:2 * G], lw[0, G:2 * G], ro, rl, f"window 1M step {j}")
+        compare(os_[0, G:2 * G], ls_[0, G:2 * G], ro, rl, f"fused window step 1M step {j}")
         _say(f"step {j} matches")
     del sc, outs
     _say("building target state (1M + 8 positions)")
