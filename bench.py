@@ -137,6 +137,7 @@ def main() -> int:
     tkv = sc.alloc_paged_kv([S + t_extra], Hkv, D, W.page_permutation(seed, "target_k", npt), dev)
     ring = lib.new_ring(B, C, Hkv, D, n_sink, n_recent, dev)
     ring_s = lib.new_ring(B, C, Hkv, D, n_sink, n_recent, dev)   # the windowed arm's ring
+    ring_g = lib.new_ring(B, C, Hkv, D, n_sink, n_recent, dev)   # the same, replayed from graphs
     # the draft context pass over a ring needs slack for its earlier queries'
     # windows (n_q - 1 positions): a second ring with 64 more slots
     n_ctx = gamma + 1
@@ -145,6 +146,7 @@ def main() -> int:
     sc.fill_paged(tkv, 0, 0, Kt[:S], Vt[:S])
     sc.fill_ring(ring, 0, Kd[:S], Vd[:S])
     sc.fill_ring(ring_s, 0, Kd[:S], Vd[:S])
+    sc.fill_ring(ring_g, 0, Kd[:S], Vd[:S])
     sc.fill_ring(ring_c, 0, Kd[:S], Vd[:S])
     # the same draft KV as fp8 e4m3 codes (scales 1: N(0, 1) values fit), same pages
     k8, v8 = lib.new_paged_cache_fp8(dkv.num_pages, Hkv, D, dev)
@@ -281,7 +283,22 @@ def main() -> int:
                                   B, Hkv, G, 1, splits_per_group=splits_f,
                                   o=o_8.view(B, 1, Hq, D), lse=l_8.view(B, 1, Hq), prepare=True)))
         plan.append((win, full, wpg, ver, ctx, full8, fused))
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(13 + 4 * gamma)]
+    # The windowed arm's draft steps once more, each bench step's seven recorded in a
+    # HIP graph (14 launches) and replayed: the launches without per-call host work.
+    ws_g = lib.new_workspace(lib.step_workspace_bytes(B, Hq, Hkv, D, C), dev)
+    o_g = torch.empty(B, Hq, D, device=dev)
+    l_g = torch.empty(B, Hq, device=dev)
+    graphs = []
+    torch.cuda.synchronize()
+    for k in range(nsteps):
+        gk = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gk):
+            for j in range(gamma):
+                lib.draft_step_window(qd[k, j], ring_g, kd_new[k, j], vd_new[k, j], 1.0, o_g, l_g,
+                                      ws_g)
+        graphs.append(gk)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(15 + 4 * gamma)]
            for _ in range(nsteps)]
 
     def step(k):
@@ -291,6 +308,8 @@ def main() -> int:
         for c in fused:                     # windowed arm: gamma x fused draft step
             c()
         e[12 + 4 * gamma].record(stream)
+        graphs[k].replay()                  # the same steps replayed from a graph
+        e[14 + 4 * gamma].record(stream)
         e[0].record(stream)
         for c in win:                       # the same as ring append + window attention
             c()
@@ -323,7 +342,7 @@ def main() -> int:
             e[11 + 2 * gamma + 2 * j].record(stream)
             comb()
         e[9 + 2 * gamma].record(stream)
-        return {"s0": e[11 + 4 * gamma], "s1": e[12 + 4 * gamma],
+        return {"s0": e[11 + 4 * gamma], "s1": e[12 + 4 * gamma], "g1": e[14 + 4 * gamma],
                 "t0": e[0], "t1": e[1], "t2": e[2], "p1": e[5 + 2 * gamma], "v0": e[3],
                 "t3": e[4], "c1": e[6 + 2 * gamma], "c2": e[7 + 2 * gamma],
                 "c3": e[8 + 2 * gamma], "f8": e[9 + 2 * gamma],
@@ -354,6 +373,7 @@ def main() -> int:
 
     win3_chain = np.median([us(m["t0"], m["t1"]) for m in marks])   # append, then window
     win_chain = np.median([us(m["s0"], m["s1"]) for m in marks])    # the fused step
+    graph_chain = np.median([us(m["s1"], m["g1"]) for m in marks])  # the same, from graphs
     full_chain = np.median([us(m["t1"], m["t2"]) for m in marks])
     wpg_chain = np.median([us(m["t2"], m["p1"]) for m in marks])
     ctx_win = np.median([us(m["t3"], m["c1"]) for m in marks])
@@ -407,6 +427,7 @@ def main() -> int:
                                    "full_fp8_kv_attention_kernel": round(attn8_mean, 2),
                                    "window": round(float(win_step_us), 2),
                                    "window_append_then_attend": round(float(win3_chain / gamma), 2),
+                                   "window_graph_replay": round(float(graph_chain / gamma), 2),
                                    "window_paged_index": round(float(wpg_chain / gamma), 2),
                                    "full_attention_kernel": round(attn_mean, 2)},
         "decode_step_us": {"full": round(float(step_full), 2), "window": round(float(step_window), 2),
