@@ -28,6 +28,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -41,6 +42,8 @@ if ROOT not in sys.path:
 METRIC = "draft-attn µs/step + decode-step µs at 1M ctx (full vs window); HBM GB/s"
 HBM_PEAK_GBS = 8000.0
 WORKLOAD = "ctx1m_g32x2_d256"
+W_CONFIG_NAMES = ("ctx8k_g16x2_d128", "ctx128k_g32x4_d128", "ctx1m_g32x2_d256",
+                  "ragged8_256k_1m_g32x4_d128", "nope8l_1m_g64x2_d128")
 
 # HBM bytes per launch of the native draft split pass measured with rocprofv3
 # (FETCH_SIZE and WRITE_SIZE passes, each scaled by the same counter's reading of a
@@ -85,6 +88,212 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def run_workload(args) -> int:
+    """The decode step of another workload: the windowed arm (fused draft steps), the
+    native arm (paged append + split pass + combine per draft step) and the verify of
+    every attention layer, each sequence at its own length.  K/V and queries are
+    random bf16 (N(0, 1), q / sqrt(D)) generated on the device: only the timing is
+    taken here, parity at these shapes is the tests' business.  Prints one JSON line
+    (no CPU baseline)."""
+    import torch
+
+    import long_context_decode_attention_amd as lib
+    import workloads as W
+    from long_context_decode_attention_amd import scenario as sc
+
+    dev = "cuda"
+    name = args.workload
+    cfg = W.CONFIGS[name]
+    B, Hq, Hkv, D = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["D"]
+    gamma, n_q, layers = cfg["gamma"], cfg["n_q"], cfg["layers"]
+    C, n_sink, n_recent = cfg["C"], cfg["n_sink"], cfg["n_recent"]
+    G = Hq // Hkv
+    S = [int(x) for x in W.context_lengths(cfg, args.seed)]
+    nsteps = args.warmup + args.steps
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed)
+
+    def randn(*shape, scale=1.0):
+        x = torch.randn(*shape, device=dev, generator=gen)
+        return (x * scale).to(torch.bfloat16) if scale != 1.0 else x.to(torch.bfloat16)
+
+    def paged_pool(extra):
+        cap = [s + extra for s in S]
+        n_pages = sum((c + 63) // 64 for c in cap)
+        return sc.alloc_paged_kv(cap, Hkv, D, W.page_permutation(args.seed, "perm", n_pages), dev)
+
+    chunk = 1 << 16
+    log(f"{name}: filling draft KV, rings and {layers} target layer(s) (lengths {S})")
+    dkv = paged_pool(gamma * nsteps)
+    ring_s = lib.new_ring(B, C, Hkv, D, n_sink, n_recent, dev)
+    for b in range(B):
+        per = C // 64
+        sub = lib.Ring(ring_s.k[b * per:(b + 1) * per], ring_s.v[b * per:(b + 1) * per],
+                       ring_s.pos[b:b + 1], ring_s.T[b:b + 1], C, n_sink, n_recent)
+        for lo in range(0, S[b], chunk):
+            n = min(chunk, S[b] - lo)
+            kn, vn = randn(1, n, Hkv, D), randn(1, n, Hkv, D)
+            sp = torch.tensor([lo], dtype=torch.int32, device=dev)
+            lib.paged_append(dkv.k, dkv.v, dkv.block_table[b:b + 1], sp, kn, vn)
+            lib.ring_append(sub, kn, vn)
+    tkvs = []
+    if n_q:
+        for _ in range(layers):
+            tkv = paged_pool(n_q * nsteps)
+            for b in range(B):
+                for lo in range(0, S[b], chunk):
+                    n = min(chunk, S[b] - lo)
+                    sp = torch.tensor([lo], dtype=torch.int32, device=dev)
+                    lib.paged_append(tkv.k, tkv.v, tkv.block_table[b:b + 1], sp,
+                                     randn(1, n, Hkv, D), randn(1, n, Hkv, D))
+            tkvs.append(tkv)
+    torch.cuda.synchronize()
+
+    qs = 1.0 / math.sqrt(D)
+    qd = randn(nsteps, gamma, B, Hq, D, scale=qs)
+    kd = randn(nsteps, gamma, B, 1, Hkv, D)
+    vd = randn(nsteps, gamma, B, 1, Hkv, D)
+    d_pos = torch.tensor([[[s + k * gamma + j for s in S] for j in range(gamma)]
+                          for k in range(nsteps)], dtype=torch.int32, device=dev)
+    d_len = d_pos + 1
+    max_d = max(S) + gamma * nsteps
+    o_w, l_w = torch.empty(B, Hq, D, device=dev), torch.empty(B, Hq, device=dev)
+    o_f, l_f = torch.empty(B, Hq, D, device=dev), torch.empty(B, Hq, device=dev)
+    ws_s = lib.new_workspace(lib.step_workspace_bytes(B, Hq, Hkv, D, C), dev)
+    ns = args.num_splits
+    ws_f = lib.new_workspace(lib.workspace_bytes(B, Hq, Hkv, D, 1, max_d, ns, partials_only=True),
+                             dev)
+    po, pl = lib.partials_view(ws_f, B, Hq, Hkv, D, 1, max_d, ns)
+    splits_f = lib.plan_splits(B, Hq, Hkv, D, 1, max_d, ns)
+    if n_q:
+        qv = randn(nsteps, layers, B, n_q, Hq, D, scale=qs)
+        kt = randn(nsteps, layers, B, n_q, Hkv, D)
+        vt = randn(nsteps, layers, B, n_q, Hkv, D)
+        t_pos = torch.tensor([[s + k * n_q for s in S] for k in range(nsteps)], dtype=torch.int32,
+                             device=dev)
+        t_len = t_pos + n_q
+        max_t = max(S) + n_q * nsteps
+        o_v = torch.empty(B, n_q, Hq, D, device=dev)
+        l_v = torch.empty(B, n_q, Hq, device=dev)
+        ws_v = lib.new_workspace(lib.workspace_bytes(B, Hq, Hkv, D, n_q, max_t, ns), dev)
+    stream = torch.cuda.current_stream()
+    plan = []
+    for k in range(nsteps):
+        win = [lib.draft_step_window(qd[k, j], ring_s, kd[k, j], vd[k, j], 1.0, o_w, l_w, ws_s,
+                                     prepare=True) for j in range(gamma)]
+        full = [(lib.paged_append(dkv.k, dkv.v, dkv.block_table, d_pos[k, j], kd[k, j], vd[k, j],
+                                  prepare=True),
+                 lib.draft_attn_full(qd[k, j], dkv.k, dkv.v, dkv.block_table, d_len[k, j], max_d,
+                                     1.0, workspace=ws_f, num_splits=ns, partials_only=True,
+                                     prepare=True),
+                 lib.split_combine(po, pl, B, Hkv, G, 1, splits_per_group=splits_f,
+                                   o=o_f.view(B, 1, Hq, D), lse=l_f.view(B, 1, Hq), prepare=True))
+                for j in range(gamma)]
+        ver = []
+        if n_q:
+            for li, tkv in enumerate(tkvs):
+                ver.append(lib.paged_append(tkv.k, tkv.v, tkv.block_table, t_pos[k], kt[k, li],
+                                            vt[k, li], prepare=True))
+                ver.append(lib.verify_attn(qv[k, li], tkv.k, tkv.v, tkv.block_table, t_len[k],
+                                           max_t, 1.0, o_v, l_v, ws_v, num_splits=ns,
+                                           prepare=True))
+        plan.append((win, full, ver))
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4 + 2 * gamma)]
+           for _ in range(nsteps)]
+
+    def step(k):
+        win, full, ver = plan[k]
+        e = evs[k]
+        e[0].record(stream)
+        for c in win:
+            c()
+        e[1].record(stream)
+        for j, (app, attn, comb) in enumerate(full):
+            app()
+            e[4 + 2 * j].record(stream)
+            attn()
+            e[5 + 2 * j].record(stream)
+            comb()
+        e[2].record(stream)
+        for c in ver:
+            c()
+        e[3].record(stream)
+        return e
+
+    log("warmup")
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    log("timed steps")
+    t0 = time.perf_counter()
+    marks = [step(k) for k in range(args.warmup, nsteps)]
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    def us(a, b):
+        return a.elapsed_time(b) * 1000.0
+
+    win_chain = float(np.median([us(e[0], e[1]) for e in marks]))
+    full_chain = float(np.median([us(e[1], e[2]) for e in marks]))
+    verify_us = float(np.median([us(e[2], e[3]) for e in marks])) if n_q else 0.0
+    attn_us = float(np.mean([us(e[4 + 2 * j], e[5 + 2 * j]) for e in marks for j in range(gamma)]))
+    kv_bytes = 2 * Hkv * D * 2
+    # mean keys read by a timed draft step, summed over the batch
+    keys = sum(S) + B * (gamma * (args.warmup + nsteps - 1) / 2.0 + (gamma + 1) / 2.0)
+    attn_bytes = kv_bytes * keys + B * Hq * D * 2
+    achieved = attn_bytes / (attn_us * 1e-6) / 1e9
+    step_window = verify_us + win_chain
+    step_full = verify_us + full_chain
+    out = {
+        "metric": METRIC,
+        "value": round(step_window, 2),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1000.0, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (random N(0,1) bf16 K/V generated on the device, q ~ N(0,1)/sqrt(D))",
+        "config": {"workload": name, "batch": B, "context": S, "q_heads": Hq, "kv_heads": Hkv,
+                   "head_dim": D, "page_tokens": 64, "pages": "seeded permutation",
+                   "draft_depth": gamma, "window": f"{n_sink}+{n_recent}", "ring_slots": C,
+                   "verify_queries": n_q, "attention_layers": layers,
+                   "splits_per_kv_head": {"draft": splits_f}},
+        "draft_attn_us_per_step": {"full": round(full_chain / gamma, 2),
+                                   "window": round(win_chain / gamma, 2),
+                                   "full_attention_kernel": round(attn_us, 2)},
+        "decode_step_us": {"full": round(step_full, 2), "window": round(step_window, 2),
+                           "verify_all_layers": round(verify_us, 2)},
+        "cost_reduction": {"native_over_window_minus_1": round(step_full / step_window - 1.0, 4),
+                           "one_minus_window_over_native": round(1.0 - step_window / step_full, 4)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "attn_split_kernel (native draft, split pass)",
+                     "bytes_per_launch": int(attn_bytes)},
+    }
+    if n_q:
+        v_keys = sum(S) + B * n_q * (args.warmup + nsteps) / 2.0
+        v_bytes = layers * (kv_bytes * v_keys + B * n_q * Hq * (D * 2 + D * 4 + 4))
+        vg = v_bytes / (verify_us * 1e-6) / 1e9
+        out["roofline_verify"] = {"bound": "hbm", "achieved": round(vg, 1), "peak": HBM_PEAK_GBS,
+                                  "unit": "GB/s", "frac": round(vg / HBM_PEAK_GBS, 4),
+                                  "note": "verify of every layer with its target append"}
+    if layers > 1:
+        # draft KV a native draft keeps (every position) against what the ring keeps,
+        # over all the KV of the stack: the share the ring gives back
+        t_d = sum(S)
+        draft_bytes = kv_bytes * t_d
+        ring_bytes = kv_bytes * B * C
+        target_bytes = layers * kv_bytes * sum(S)
+        out["draft_kv_reclaimed_fraction"] = round((draft_bytes - ring_bytes) /
+                                                   (target_bytes + draft_bytes), 5)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -93,6 +302,10 @@ def main() -> int:
     ap.add_argument("--seed", type=int, default=2026)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--workload", default=WORKLOAD, choices=sorted(W_CONFIG_NAMES),
+                    help="the workload to time; the default is the 1M-context single "
+                         "sequence, the others time the same arms at their own shapes "
+                         "with random bf16 inputs generated on the device")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one plain 1 GiB device copy before the steps, so that a profiler "
                          "pass sees a kernel of known traffic to scale its byte counters by")
@@ -108,6 +321,9 @@ def main() -> int:
     import long_context_decode_attention_amd as lib
     import workloads as W
     from long_context_decode_attention_amd import scenario as sc
+
+    if args.workload != WORKLOAD:
+        return run_workload(args)
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
