@@ -647,6 +647,7 @@ bool plan_attention(int B, int Hq, int Hkv, int D, int n_q, int max_keys, int nu
   int cap;        // most 32-key tiles per split
   // Few rows: each wave holds every row and the four waves split the keys.
   // Two row blocks per wave need too many registers at D = 256 (they spill).
+  p->nw = 0;
   if (ring || p->R <= 32) {
     p->shared = 0;
     p->nrb = 1;                             // one 32-row block per wave
@@ -658,10 +659,18 @@ bool plan_attention(int B, int Hq, int Hkv, int D, int n_q, int max_keys, int nu
     // A wave holds 32 * rbw rows: the fewest that cover R, at most one block at
     // D = 256 and two below (register file); beyond that the rows go to row groups.
     p->shared = 1;
-    const int nw = shared_kernel_waves();
+    int nw = shared_kernel_waves();
     const int rbw_max = D == 256 ? 1 : 2;
     int rbw = 1;
-    while (rbw < rbw_max && 32 * nw * rbw < p->R) rbw *= 2;
+    if (D == 128 && p->R > 32 * nw) {
+      // more rows than four waves of 32 hold at D = 128: eight waves of 32 rows, two
+      // per SIMD, so that one wave's refill and softmax stalls overlap the other's
+      // MFMAs (instead of four waves of 64 rows, one per SIMD)
+      nw = 8;
+    } else {
+      while (rbw < rbw_max && 32 * nw * rbw < p->R) rbw *= 2;
+    }
+    p->nw = nw;
     p->nrb = rbw;
     p->nrg = (p->R + 32 * nw * rbw - 1) / (32 * nw * rbw);
     target = WMTP_TARGET_WG_SHARED;

@@ -362,11 +362,11 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
   // Half tiles stream through two rings of LDS slots, K and V, filled by
   // direct global-to-LDS loads: the K half of tile u goes to K slot u % kSlots,
   // its V half to V slot u % kSlots.  Step t reads K(t+1) (for S(t+1)) and V(t)
-  // (for PV(t)), so each ring has one resident half and four in flight: after
-  // the barrier of step t, K(t+5) refills the slot K(t) left and V(t+4) the slot
-  // V(t-1) left.  A page id outside the cache still issues its loads (from page
+  // (for PV(t)), so each ring has one resident half and kSlots - 1 in flight:
+  // after the barrier of step t, K(t+kSlots) refills the slot K(t) left and
+  // V(t+kSlots-1) the slot V(t-1) left.  A page id outside the cache still issues its loads (from page
   // 0) so that every half costs the same number of loads; the tile is skipped.
-  uint32_t ok_tile = 0;                 // bit u % 8: tile u has a valid page
+  uint32_t ok_tile = 0;                 // bit u % 32: tile u has a valid page
   auto page_of = [&](int u, bool& ok) -> size_t {
     const int kb = kb0 + u;
     const int idx = (kb >> 1) - page0;   // 0 .. 64*kPageRegs - 1, wave-uniform
@@ -383,7 +383,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
   auto issue_k = [&](int u) {
     bool ok;
     const uint16_t* kt = a.kc + page_of(u, ok) * (size_t)(32 * D);
-    ok_tile = (ok_tile & ~(1u << (u & 7))) | ((ok ? 1u : 0u) << (u & 7));
+    ok_tile = (ok_tile & ~(1u << (u & 31))) | ((ok ? 1u : 0u) << (u & 31));
     unsigned char* base = k_slot(u);
 #pragma unroll
     for (int i = 0; i < NH; ++i) {
@@ -407,7 +407,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
     }
   };
 
-  // Prologue: K(0..4) and V(0..3) in the order the steps would have issued them,
+  // Prologue: K(0..kSlots-1) and V(0..kSlots-2) in the order the steps would have issued them,
   // publish K(0), issue S(0).
 #pragma unroll
   for (int u = 0; u < kSlots; ++u) {
@@ -417,7 +417,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
   f32x16 s_acc[RBW];
   if (ntile > 0) {
     if (ntile >= kSlots) {
-      wait_vmcnt<(kSlots - 1) * 2 * NH>();   // K(1..4), V(0..3) may still be in flight
+      wait_vmcnt<(kSlots - 1) * 2 * NH>();   // K(1..), V(0..) may still be in flight
     } else {
       wait_vmcnt<0>();
     }
@@ -427,8 +427,8 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
 
   // Publish K(t+1) and V(t); then refill the freed slots (issue_for).
   auto publish = [&](int t) {
-    // Issued after K(t+1), V(t): K(t+2..t+4) and V(t+1..t+3), all present
-    // unless the split ends within the next few tiles.
+    // Issued after K(t+1), V(t): K(t+2..t+kSlots-1) and V(t+1..t+kSlots-2),
+    // all present unless the split ends within the next few tiles.
     if (t + kSlots - 1 < ntile) {
       wait_vmcnt<(kSlots - 2) * 2 * NH>();
     } else {
@@ -473,12 +473,12 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
       for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(x[rb][i]));
     }
   };
-  auto tile_ok = [&](int t) { return any_row && ((ok_tile >> (t & 7)) & 1u); };
+  auto tile_ok = [&](int t) { return any_row && ((ok_tile >> (t & 31)) & 1u); };
 
   // Tiles run through a fast path or a general one.  The fast path takes a tile
   // that is full (every key present and visible to every row), whose rows all
   // have a running maximum that no score of the tile exceeds by more than the
-  // lazy margin, and whose refill, K(t+5) and V(t+4), exists: one branch-free
+  // lazy margin, and whose refill, K(t+kSlots) and V(t+kSlots-1), exists: one branch-free
   // block, no cross-lane work.  Any other tile (a split's first and last
   // tiles, the causal boundary, bad pages, a rescale) takes the general path,
   // and the fast path resumes after it.  Waves that own no row take only part
@@ -521,7 +521,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
         const uint16_t* vt = a.vc + page_of(t + kSlots - 1, ok_v) * (size_t)(32 * D);
         {
           const int u = t + kSlots;
-          ok_tile = (ok_tile & ~(1u << (u & 7))) | ((ok_k ? 1u : 0u) << (u & 7));
+          ok_tile = (ok_tile & ~(1u << (u & 31))) | ((ok_k ? 1u : 0u) << (u & 31));
         }
         unsigned char* kdst = k_slot(t + kSlots);
         unsigned char* vdst = v_slot(t + kSlots - 1);
@@ -586,14 +586,14 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
 
 constexpr int kWaves = 4;
 
-template <int D, int RBW>
+template <int D, int RBW, int NW = kWaves>
 hipError_t launch_shared_one(const AttnArgs& a, int grid, hipStream_t stream) {
   AttnArgs arg = a;
   void* args[] = {&arg};
   const void* k = a.tree_mask
-                      ? reinterpret_cast<const void*>(&attn_shared_kernel<D, RBW, kWaves, true>)
-                      : reinterpret_cast<const void*>(&attn_shared_kernel<D, RBW, kWaves, false>);
-  return hipLaunchKernel(k, dim3(grid), dim3(64 * kWaves), args, 0, stream);
+                      ? reinterpret_cast<const void*>(&attn_shared_kernel<D, RBW, NW, true>)
+                      : reinterpret_cast<const void*>(&attn_shared_kernel<D, RBW, NW, false>);
+  return hipLaunchKernel(k, dim3(grid), dim3(64 * NW), args, 0, stream);
 }
 
 }  // namespace
@@ -607,6 +607,8 @@ hipError_t launch_attention_shared(const AttnArgs& a, const AttnPlan& p, hipStre
       return p.nrb == 1 ? launch_shared_one<64, 1>(a, p.grid, stream)
                         : launch_shared_one<64, 2>(a, p.grid, stream);
     case 128:
+      if (p.nw == 8) return p.nrb == 1 ? launch_shared_one<128, 1, 8>(a, p.grid, stream)
+                                       : hipErrorInvalidValue;
       return p.nrb == 1 ? launch_shared_one<128, 1>(a, p.grid, stream)
                         : launch_shared_one<128, 2>(a, p.grid, stream);
     case 256:

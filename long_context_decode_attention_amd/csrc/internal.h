@@ -55,6 +55,7 @@ struct AttnPlan {
   int shared;   // 0: attn_split_kernel (one wave holds all rows, waves split keys)
                 // 1: attn_shared_kernel (waves split rows, K/V tiles shared in LDS)
   int G, R, nrb, nrg, nkb, kb_per_split, nsplit, items, grid;
+  int nw;       // attn_shared_kernel: waves per workgroup (4, or 8 at D = 128 with many rows)
   int direct;
   size_t part_o_bytes, lse_offset, ws_bytes;
 };
