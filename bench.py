@@ -51,7 +51,7 @@ W_CONFIG_NAMES = ("ctx8k_g16x2_d128", "ctx128k_g32x4_d128", "ctx1m_g32x2_d256",
 # keyed by a hash of the sources that kernel is built from: a changed kernel
 # reports null until it is measured again.
 MEASURED_TRAFFIC = {
-    "dd441f4ae9bb37fd": {"read": 2.148e+09, "write": 4.211e+06, "keys": 1048587},
+    "c988d22eeeeb030d": {"read": 2.148e+09, "write": 4.211e+06, "keys": 1048587},
 }
 KERNEL_SOURCES = ("csrc/attn.hip", "csrc/attn_device.h", "csrc/common.h")
 
@@ -86,6 +86,162 @@ def kernel_source_hash() -> str:
         with open(os.path.join(base, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+SWEEP_CONTEXTS = (8192, 32768, 131072, 524288, 1048576)
+
+
+def _fit(xs, ys):
+    """Least-squares line y = a + b x: (a, b, R^2)."""
+    x = np.asarray(xs, dtype=np.float64)
+    y = np.asarray(ys, dtype=np.float64)
+    b, a = np.polyfit(x, y, 1)
+    r = y - (a + b * x)
+    tot = float(np.sum((y - y.mean()) ** 2))
+    r2 = 1.0 - float(np.sum(r * r)) / tot if tot > 0 else 1.0
+    return float(a), float(b), r2
+
+
+def run_sweep(args) -> int:
+    """Decode-step time against context on the 1M workload's heads (32/2, head_dim 256,
+    draft depth 7, window 4 + 4092, verify of 8 queries): at each context the native
+    draft step (paged append + split pass + combine), the fused windowed draft step and
+    the verify (target append + verify), then a straight-line fit of each against the
+    context: the analogue of the pages' time-against-context fit.  K/V are random bf16
+    generated on the device; one cache of the largest context serves every point (each
+    point reads only its first L positions).  Prints one JSON line."""
+    import torch
+
+    import long_context_decode_attention_amd as lib
+    import workloads as W
+    from long_context_decode_attention_amd import scenario as sc
+
+    dev = "cuda"
+    cfg = W.CONFIGS[WORKLOAD]
+    Hq, Hkv, D, gamma, n_q = cfg["Hq"], cfg["Hkv"], cfg["D"], cfg["gamma"], cfg["n_q"]
+    C, n_sink, n_recent = cfg["C"], cfg["n_sink"], cfg["n_recent"]
+    G = Hq // Hkv
+    B = 1
+    nsteps = args.warmup + args.steps
+    Lmax = max(SWEEP_CONTEXTS)
+    extra = max(gamma, n_q) * nsteps
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed)
+
+    def randn(*shape, scale=1.0):
+        x = torch.randn(*shape, device=dev, generator=gen)
+        return (x * scale).to(torch.bfloat16)
+
+    npg = (Lmax + extra + 63) // 64
+    log("context sweep: filling draft and target KV (1M positions) and the ring")
+    dkv = sc.alloc_paged_kv([Lmax + extra], Hkv, D, W.page_permutation(args.seed, "perm", npg), dev)
+    tkv = sc.alloc_paged_kv([Lmax + extra], Hkv, D, W.page_permutation(args.seed + 1, "perm", npg),
+                            dev)
+    ring = lib.new_ring(B, C, Hkv, D, n_sink, n_recent, dev)
+    chunk = 1 << 16
+    for lo in range(0, Lmax, chunk):
+        sp = torch.tensor([lo], dtype=torch.int32, device=dev)
+        kn, vn = randn(1, chunk, Hkv, D), randn(1, chunk, Hkv, D)
+        lib.paged_append(dkv.k, dkv.v, dkv.block_table, sp, kn, vn)
+        lib.ring_append(ring, kn, vn)
+        lib.paged_append(tkv.k, tkv.v, tkv.block_table, sp, randn(1, chunk, Hkv, D),
+                         randn(1, chunk, Hkv, D))
+    torch.cuda.synchronize()
+    qs = 1.0 / math.sqrt(D)
+    qd = randn(nsteps, gamma, B, Hq, D, scale=qs)
+    kd = randn(nsteps, gamma, B, 1, Hkv, D)
+    vd = randn(nsteps, gamma, B, 1, Hkv, D)
+    qv = randn(nsteps, B, n_q, Hq, D, scale=qs)
+    kt = randn(nsteps, B, n_q, Hkv, D)
+    vt = randn(nsteps, B, n_q, Hkv, D)
+    o_w, l_w = torch.empty(B, Hq, D, device=dev), torch.empty(B, Hq, device=dev)
+    o_f, l_f = torch.empty(B, Hq, D, device=dev), torch.empty(B, Hq, device=dev)
+    o_v, l_v = torch.empty(B, n_q, Hq, D, device=dev), torch.empty(B, n_q, Hq, device=dev)
+    ws_s = lib.new_workspace(lib.step_workspace_bytes(B, Hq, Hkv, D, C), dev)
+    ws_f = lib.new_workspace(max(lib.workspace_bytes(B, Hq, Hkv, D, 1, L + extra, partials_only=True)
+                                 for L in SWEEP_CONTEXTS), dev)
+    ws_v = lib.new_workspace(max(lib.workspace_bytes(B, Hq, Hkv, D, n_q, L + extra)
+                                 for L in SWEEP_CONTEXTS), dev)
+    stream = torch.cuda.current_stream()
+    points = []
+    for L in SWEEP_CONTEXTS:
+        max_d = L + extra
+        po, pl = lib.partials_view(ws_f, B, Hq, Hkv, D, 1, max_d)
+        splits = lib.plan_splits(B, Hq, Hkv, D, 1, max_d)
+        # positions and lengths live as long as the prepared calls that point at them
+        d_pos = torch.tensor([[[L + k * gamma + j] for j in range(gamma)] for k in range(nsteps)],
+                             dtype=torch.int32, device=dev)
+        d_len = d_pos + 1
+        t_pos = torch.tensor([[L + k * n_q] for k in range(nsteps)], dtype=torch.int32, device=dev)
+        t_len = t_pos + n_q
+        plan = []
+        for k in range(nsteps):
+            win = [lib.draft_step_window(qd[k, j], ring, kd[k, j], vd[k, j], 1.0, o_w, l_w, ws_s,
+                                         prepare=True) for j in range(gamma)]
+            full = []
+            for j in range(gamma):
+                full += [lib.paged_append(dkv.k, dkv.v, dkv.block_table, d_pos[k, j], kd[k, j],
+                                          vd[k, j], prepare=True),
+                         lib.draft_attn_full(qd[k, j], dkv.k, dkv.v, dkv.block_table, d_len[k, j],
+                                             max_d, 1.0, workspace=ws_f, partials_only=True,
+                                             prepare=True),
+                         lib.split_combine(po, pl, B, Hkv, G, 1, splits_per_group=splits,
+                                           o=o_f.view(B, 1, Hq, D), lse=l_f.view(B, 1, Hq),
+                                           prepare=True)]
+            ver = [lib.paged_append(tkv.k, tkv.v, tkv.block_table, t_pos[k], kt[k], vt[k],
+                                    prepare=True),
+                   lib.verify_attn(qv[k], tkv.k, tkv.v, tkv.block_table, t_len[k], max_d, 1.0,
+                                   o_v, l_v, ws_v, prepare=True)]
+            plan.append((win, full, ver))
+        times = []
+        for k in range(nsteps):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            win, full, ver = plan[k]
+            e[0].record(stream)
+            for c in win:
+                c()
+            e[1].record(stream)
+            for c in full:
+                c()
+            e[2].record(stream)
+            for c in ver:
+                c()
+            e[3].record(stream)
+            times.append(e)
+        torch.cuda.synchronize()
+        tw = float(np.median([a[0].elapsed_time(a[1]) * 1000.0 / gamma for a in times[args.warmup:]]))
+        tf = float(np.median([a[1].elapsed_time(a[2]) * 1000.0 / gamma for a in times[args.warmup:]]))
+        tv = float(np.median([a[2].elapsed_time(a[3]) * 1000.0 for a in times[args.warmup:]]))
+        points.append({"context": L, "draft_full_us": round(tf, 2), "draft_window_us": round(tw, 2),
+                       "verify_us": round(tv, 2), "step_full_us": round(tv + gamma * tf, 2),
+                       "step_window_us": round(tv + gamma * tw, 2),
+                       "full_over_window": round((tv + gamma * tf) / (tv + gamma * tw), 4)})
+        log(f"context {L}: draft full {tf:.1f} us, window {tw:.1f} us, verify {tv:.1f} us")
+    xs = [p["context"] / 1e6 for p in points]
+    fits = {}
+    for key in ("draft_full_us", "draft_window_us", "verify_us", "step_full_us", "step_window_us"):
+        a, b, r2 = _fit(xs, [p[key] for p in points])
+        fits[key.replace("_us", "")] = {"intercept_us": round(a, 2),
+                                        "slope_us_per_million_keys": round(b, 2), "r2": round(r2, 5)}
+    ratios = [p["full_over_window"] for p in points]
+    out = {
+        "metric": "decode-step us against context (1M workload's heads), straight-line fits",
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "data": "synthetic (random N(0,1) bf16 K/V generated on the device, q ~ N(0,1)/sqrt(D))",
+        "config": {"workload": f"{WORKLOAD} heads, contexts {list(SWEEP_CONTEXTS)}", "batch": B,
+                   "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "draft_depth": gamma,
+                   "window": f"{n_sink}+{n_recent}", "verify_queries": n_q},
+        "points": points,
+        "fits": fits,
+        "step_slope_reduction": round(1.0 - fits["step_window"]["slope_us_per_million_keys"] /
+                                      fits["step_full"]["slope_us_per_million_keys"], 4),
+        "full_over_window_monotone_in_context": all(b >= a for a, b in zip(ratios, ratios[1:])),
+    }
+    print(json.dumps(out), flush=True)
+    return 0
 
 
 def run_workload(args) -> int:
@@ -306,6 +462,10 @@ def main() -> int:
                     help="the workload to time; the default is the 1M-context single "
                          "sequence, the others time the same arms at their own shapes "
                          "with random bf16 inputs generated on the device")
+    ap.add_argument("--context-sweep", action="store_true",
+                    help="time the native and windowed draft steps and the verify at "
+                         "contexts 8K..1M (the 1M workload's heads) and fit time against "
+                         "context; prints its own JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one plain 1 GiB device copy before the steps, so that a profiler "
                          "pass sees a kernel of known traffic to scale its byte counters by")
@@ -322,6 +482,8 @@ def main() -> int:
     import workloads as W
     from long_context_decode_attention_amd import scenario as sc
 
+    if args.context_sweep:
+        return run_sweep(args)
     if args.workload != WORKLOAD:
         return run_workload(args)
 
