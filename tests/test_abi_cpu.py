@@ -251,6 +251,20 @@ def test_fused_step_argument_checks_and_plan():
     assert lib_mod.step_splits(1, 32, 2, 256, 4096, 1000) == 4096 // 32
 
 
+def test_plan_rounds_for_several_long_sequences():
+    """Paged calls over several sequences of 64K keys or more plan four workgroups per
+    CU (the lengths are on the device); one sequence, short key ranges and rings one."""
+    _lib()
+    one = lib_mod.plan_splits(1, 32, 4, 128, 1, 1 << 20)        # 4 groups x 64 splits = 256
+    eight = lib_mod.plan_splits(8, 32, 4, 128, 1, 1 << 20)      # 32 groups x 32 splits = 1024
+    assert one * 4 == 256 and eight * 32 == 1024
+    assert lib_mod.plan_splits(8, 32, 4, 128, 1, 60000) * 32 <= 256   # under 64K keys: one round
+    assert lib_mod.plan_splits(8, 32, 4, 128, 1, 4096, ring=True) * 32 <= 256
+    assert lib_mod.plan_splits(8, 32, 4, 128, 1, 4096, paged_window=True) * 32 <= 256
+    # verify rows go through the same rule
+    assert lib_mod.plan_splits(8, 32, 4, 128, 4, 1 << 20) * 32 == 1024
+
+
 def _imports(path):
     names = set()
     for dirpath, _, files in os.walk(path):

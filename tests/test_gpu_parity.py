@@ -91,6 +91,17 @@ def test_draft_ragged_batch():
     _draft_chain(DraftScenario(cfg, 4, S, 2))
 
 
+def test_draft_ragged_long_four_rounds():
+    """Several sequences, the longest past 64K keys: the plan runs four workgroups
+    per CU (lengths on the device), splits of short sequences end up empty."""
+    lib = _lib()
+    cfg = CFG["ragged8_256k_1m_g32x4_d128"]
+    S = [66000, 140000, 9000]
+    # more than two rounds of one workgroup per CU (256 CUs)
+    assert lib.plan_splits(3, cfg["Hq"], cfg["Hkv"], cfg["D"], 1, max(S) + 1) * 3 * cfg["Hkv"] > 512
+    _draft_chain(DraftScenario(cfg, 6, S, 1))
+
+
 def test_draft_g64x2_wrapped_ring():
     """64/2 heads (G = 32, two row blocks), D 128; ring of 4096 wrapped (T > C)."""
     cfg = CFG["nope8l_1m_g64x2_d128"]
@@ -397,6 +408,15 @@ def test_verify_ragged_batch():
     cfg = CFG["ragged8_256k_1m_g32x4_d128"]
     S = [int(x) for x in W.ragged_lengths(22, 8, 2000, 7000)]
     _verify_case(cfg, 22, S, 4)
+
+
+@pytest.mark.parametrize("cfg_name,S,n_q", [
+    ("ragged8_256k_1m_g32x4_d128", [70000, 30000], 4),    # 32 rows: split kernel
+    ("ctx128k_g32x4_d128", [66000, 20000], 8),            # 64 rows: shared kernel, two row blocks
+])
+def test_verify_ragged_long_four_rounds(cfg_name, S, n_q):
+    """Verify over several sequences, the longest past 64K keys (four workgroup rounds)."""
+    _verify_case(CFG[cfg_name], 24, S, n_q)
 
 
 def test_verify_g64x2_256_rows():
