@@ -370,10 +370,13 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
   auto page_of = [&](int u, bool& ok) -> size_t {
     const int kb = kb0 + u;
     const int idx = (kb >> 1) - page0;   // 0 .. 64*kPageRegs - 1, wave-uniform
+    // every register's lane idx % 64, then a select: no branch per register
+    int cand[kPageRegs];
+#pragma unroll
+    for (int r = 0; r < kPageRegs; ++r) cand[r] = __builtin_amdgcn_readlane(my_page[r], idx & 63);
     int ppage = -1;
 #pragma unroll
-    for (int r = 0; r < kPageRegs; ++r)
-      if ((idx >> 6) == r) ppage = __builtin_amdgcn_readlane(my_page[r], idx & 63);
+    for (int r = 0; r < kPageRegs; ++r) ppage = (idx >> 6) == r ? cand[r] : ppage;
     ok = (unsigned)ppage < (unsigned)a.num_pages;
     if (!ok) ppage = 0;
     return ((size_t)ppage * a.Hkv + g) * 2 + (kb & 1);
