@@ -172,3 +172,35 @@ def test_fused_step_errors():
     assert e.value.status == 1                     # the scale must be positive
     t.cuda.synchronize()
     assert int(ring.T[0]) == 0 and int((ring.pos >= 0).sum()) == 0
+
+
+def _random_cases(n, seed=2027):
+    """Seeded random shapes for the fused step: ring capacity, sink and window sizes
+    (including windows smaller than the ring, slack, tiny rings), head dims, batch,
+    context lengths around the wrap points, new positions per call and split counts."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        C = int(rng.choice([64, 128, 192, 1024]))
+        n_sink = int(rng.integers(0, min(16, C - 1) + 1))
+        n_recent = int(rng.integers(1, C - n_sink + 1))
+        D = int(rng.choice([64, 128, 256]))
+        Hkv = int(rng.choice([1, 2]))
+        G = int(rng.choice([1, 4, 8, 16, 32]))
+        B = int(rng.integers(1, 4))
+        S = [int(rng.choice([0, 1, n_sink, C - 1, C, C + 1, 3 * C + 5, int(rng.integers(0, 4 * C))]))
+             for _ in range(B)]
+        n_new = int(rng.choice([1, 2, 7, 32]))
+        num_splits = int(rng.choice([0, 1, 2, 5]))
+        cases.append((Hkv * G, Hkv, D, C, n_sink, n_recent, S, n_new, num_splits))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_cases(24), ids=lambda c: "H{}x{}_D{}_C{}_s{}_r{}_B{}_n{}_p{}".format(
+    c[0], c[1], c[2], c[3], c[4], c[5], len(c[6]), c[7], c[8]))
+def test_fused_step_random_shapes(case):
+    """Seeded random shapes, two steps each: oracle parity and ring state equal to
+    append-then-window's, bit for bit."""
+    Hq, Hkv, D, C, n_sink, n_recent, S, n_new, num_splits = case
+    _run_chain(Hq, Hkv, D, C, n_sink, n_recent, S, 2, n_new=n_new, num_splits=num_splits,
+               seed=31)
