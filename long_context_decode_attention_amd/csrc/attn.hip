@@ -453,6 +453,9 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
           // absent keys may hold any bits (an fp8 NaN too): zero them
           if (mask_v) vv[db][kk] = mask8(vv[db][kk], (keep >> (8 * kk)) & 0xFFu);
         }
+      // the raw V bytes are converted: refill them now, so that the next tile's V
+      // loads run under this tile's PV products
+      if constexpr (decltype(has_next)::value) load_v<D, KV8>(vt, a, tile_n, m, h);
       pv<D, NB>(st, vv, p_hi, p_lo);
     } else {
       if (mask_v) {
@@ -465,7 +468,7 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
       }
       pv<D, NB>(st, vt.v, p_hi, p_lo);
     }
-    if constexpr (decltype(has_next)::value) load_v<D, KV8>(vt, a, tile_n, m, h);
+    if constexpr (!KV8 && decltype(has_next)::value) load_v<D, KV8>(vt, a, tile_n, m, h);
   };
   const std::true_type more;
   const std::false_type last;
