@@ -89,18 +89,24 @@ const char* wmtp_status_string(wmtp_status s);
 /*
  * Split plan of the attention calls.  n_q = 1 for the draft calls;
  * max_keys = min(max_seq_len, max_pages * 64) for the paged calls, C for
- * the ring call and n_sink + n_recent for the truncated paged index (its
+ * the ring calls and n_sink + n_recent for the truncated paged index (its
  * plan then covers any max_seq_len); num_splits = 0 lets the library choose.  Returns the number
  * of key splits per (sequence, kv head) that a call with these arguments
- * will use, or -1 if the sizes are invalid.
+ * will use, or -1 if the sizes are invalid.  For WMTP_CALL_RING_STEP it is the
+ * number of ring splits; each (sequence, kv head) then has one more partial,
+ * the new positions'.  With num_splits = 0, paged calls over several sequences
+ * of 64K keys or more plan about four workgroups per compute unit (the lengths
+ * are on the device, and the extra rounds even out unequal ones), other calls
+ * about one.
  */
 int wmtp_plan_splits(int call, int B, int Hq, int Hkv, int D, int n_q, int max_keys,
                      int num_splits);
 
 /*
  * Workspace bytes the same call needs (0 when one split suffices and the
- * result is written directly, unless partials_only is non-zero).  Layout:
- * with P = B * Hkv * splits partials of R = n_q * Hq / Hkv rows each,
+ * result is written directly, unless partials_only is non-zero; never 0 for
+ * WMTP_CALL_RING_STEP).  Layout: with P = B * Hkv * splits partials
+ * (splits + 1 for WMTP_CALL_RING_STEP) of R = n_q * Hq / Hkv rows each,
  *   part_o   fp32 [P][R][D] at byte 0 (partial p = (b * Hkv + g) * splits + s;
  *            row r = i * G + (h - g * G) for query i, head h),
  *   part_lse fp32 [P][R]    at byte ((P * R * D * 4 + 255) / 256) * 256;
