@@ -18,8 +18,9 @@ in the per-step cost identity: t_step = t_verify + sum of the arm's draft steps
 
 Also timed beside them: the windowed arm as ring append + windowed attention
 (three launches per draft step), the windowed draft through a truncated index of
-the paged draft KV, the draft context pass, the verify of a tree of proposals and
-the native arm over fp8 draft KV.
+the paged draft KV, the draft context pass (fused with its append, and as append
+then attention), the verify of a tree of proposals and the native arm over fp8
+draft KV.
 
 Prints one JSON line.  ``value`` is the windowed arm's decode-step time (us).
 """
@@ -51,7 +52,7 @@ W_CONFIG_NAMES = ("ctx8k_g16x2_d128", "ctx128k_g32x4_d128", "ctx1m_g32x2_d256",
 # keyed by a hash of the sources that kernel is built from: a changed kernel
 # reports null until it is measured again.
 MEASURED_TRAFFIC = {
-    "66a73498eb09bc33": {"read": 2.148e+09, "write": 4.211e+06, "keys": 1048587},
+    "41f953801559dacb": {"read": 2.148e+09, "write": 4.211e+06, "keys": 1048587},
 }
 KERNEL_SOURCES = ("csrc/attn.hip", "csrc/attn_device.h", "csrc/common.h")
 
@@ -520,12 +521,14 @@ def main() -> int:
     # windows (n_q - 1 positions): a second ring with 64 more slots
     n_ctx = gamma + 1
     ring_c = lib.new_ring(B, C + 64, Hkv, D, n_sink, n_recent, dev)
+    ring_cf = lib.new_ring(B, C + 64, Hkv, D, n_sink, n_recent, dev)   # the same, fused pass
     sc.fill_paged(dkv, 0, 0, Kd[:S], Vd[:S])
     sc.fill_paged(tkv, 0, 0, Kt[:S], Vt[:S])
     sc.fill_ring(ring, 0, Kd[:S], Vd[:S])
     sc.fill_ring(ring_s, 0, Kd[:S], Vd[:S])
     sc.fill_ring(ring_g, 0, Kd[:S], Vd[:S])
     sc.fill_ring(ring_c, 0, Kd[:S], Vd[:S])
+    sc.fill_ring(ring_cf, 0, Kd[:S], Vd[:S])
     # the same draft KV as fp8 e4m3 codes (scales 1: N(0, 1) values fit), same pages
     k8, v8 = lib.new_paged_cache_fp8(dkv.num_pages, Hkv, D, dev)
     for lo in range(0, S, 1 << 16):
@@ -585,6 +588,7 @@ def main() -> int:
     o_c = torch.empty(B, n_ctx, Hq, D, device=dev)
     l_c = torch.empty(B, n_ctx, Hq, device=dev)
     ws_cw = lib.new_workspace(lib.workspace_bytes(B, Hq, Hkv, D, n_ctx, C + 64, ring=True), dev)
+    ws_cf = lib.new_workspace(lib.step_workspace_bytes(B, Hq, Hkv, D, C + 64, 0, n_ctx), dev)
     ws_cn = lib.new_workspace(lib.workspace_bytes(B, Hq, Hkv, D, n_ctx, max_d), dev)
     # tree-shaped proposals of the same size for the tree verify: a binary tree
     # (node i's parent (i - 1) // 2), mask bit a = node a is an ancestor or itself
@@ -640,14 +644,17 @@ def main() -> int:
                lib.verify_attn(qv[k], tkv.k, tkv.v, tkv.block_table, t_len[k], max_t, 1.0, o_v,
                                l_v, ws_v, prepare=True))
         # draft context pass over the n_ctx accepted positions (here: every draft
-        # plus the bonus position): windowed over the slack ring, natively the
-        # causal verify kernel over the whole paged draft KV
+        # plus the bonus position): windowed over the slack ring (append, then
+        # attention; and the two fused in ctx[4]), natively the causal verify
+        # kernel over the whole paged draft KV
         ctx = (lib.ring_append(ring_c, kc_new[k], vc_new[k], prepare=True),
                lib.draft_context_window(qc[k], ring_c, 1.0, o_c, l_c, ws_cw, prepare=True),
                lib.verify_attn(qc[k], dkv.k, dkv.v, dkv.block_table, d_len[k, gamma - 1], max_d,
                                1.0, o_c, l_c, ws_cn, prepare=True),
                lib.verify_attn_tree(qv[k], tkv.k, tkv.v, tkv.block_table, t_len[k], tree_mask,
-                                    max_t, 1.0, o_v, l_v, ws_v, prepare=True))
+                                    max_t, 1.0, o_v, l_v, ws_v, prepare=True),
+               lib.draft_context_step_window(qc[k], ring_cf, kc_new[k], vc_new[k], 1.0, o_c, l_c,
+                                             ws_cf, prepare=True))
         # native arm over the fp8 draft KV: quantizing append, split pass, combine
         full8 = []
         for j in range(gamma):
@@ -706,7 +713,9 @@ def main() -> int:
         e[3].record(stream)
         ver[1]()                            # verify attention
         e[4].record(stream)
-        ctx[0]()                            # context pass, windowed: append + ring attention
+        ctx[4]()                            # context pass, windowed: fused append + attention
+        e[13 + 4 * gamma].record(stream)
+        ctx[0]()                            # the same as ring append + ring attention
         ctx[1]()
         e[6 + 2 * gamma].record(stream)
         ctx[2]()                            # context pass, native: over all the draft KV
@@ -722,8 +731,8 @@ def main() -> int:
         e[9 + 2 * gamma].record(stream)
         return {"s0": e[11 + 4 * gamma], "s1": e[12 + 4 * gamma], "g1": e[14 + 4 * gamma],
                 "t0": e[0], "t1": e[1], "t2": e[2], "p1": e[5 + 2 * gamma], "v0": e[3],
-                "t3": e[4], "c1": e[6 + 2 * gamma], "c2": e[7 + 2 * gamma],
-                "c3": e[8 + 2 * gamma], "f8": e[9 + 2 * gamma],
+                "t3": e[4], "cf": e[13 + 4 * gamma], "c1": e[6 + 2 * gamma],
+                "c2": e[7 + 2 * gamma], "c3": e[8 + 2 * gamma], "f8": e[9 + 2 * gamma],
                 "attn8": [(e[10 + 2 * gamma + 2 * j], e[11 + 2 * gamma + 2 * j]) for j in range(gamma)],
                 "attn": [(e[5 + 2 * j], e[6 + 2 * j]) for j in range(gamma)]}
 
@@ -754,7 +763,8 @@ def main() -> int:
     graph_chain = np.median([us(m["s1"], m["g1"]) for m in marks])  # the same, from graphs
     full_chain = np.median([us(m["t1"], m["t2"]) for m in marks])
     wpg_chain = np.median([us(m["t2"], m["p1"]) for m in marks])
-    ctx_win = np.median([us(m["t3"], m["c1"]) for m in marks])
+    ctx_win = np.median([us(m["t3"], m["cf"]) for m in marks])     # fused
+    ctx_win3 = np.median([us(m["cf"], m["c1"]) for m in marks])    # append, then window
     ctx_full = np.median([us(m["c1"], m["c2"]) for m in marks])
     tree_us = np.median([us(m["c2"], m["c3"]) for m in marks])
     full8_chain = np.median([us(m["c3"], m["f8"]) for m in marks])
@@ -818,6 +828,7 @@ def main() -> int:
         "cost_reduction": {"native_over_window_minus_1": round(float(up), 4),
                            "one_minus_window_over_native": round(float(down), 4)},
         "draft_context_pass_us": {"queries": n_ctx, "window": round(float(ctx_win), 2),
+                                  "window_append_then_attend": round(float(ctx_win3), 2),
                                   "full": round(float(ctx_full), 2),
                                   "decode_step_window_with_it": round(float(step_window + ctx_win), 2),
                                   "decode_step_full_with_it": round(float(step_full + ctx_full), 2)},

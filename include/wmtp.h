@@ -84,7 +84,8 @@ const char* wmtp_status_string(wmtp_status s);
 #define WMTP_CALL_PAGED 0        /* wmtp_draft_attn_full, wmtp_verify_attn */
 #define WMTP_CALL_RING 1         /* wmtp_draft_attn_window */
 #define WMTP_CALL_PAGED_WINDOW 2 /* wmtp_draft_attn_window_paged */
-#define WMTP_CALL_RING_STEP 3    /* wmtp_draft_step_window (n_q = 1, max_keys = C) */
+#define WMTP_CALL_RING_STEP 3    /* wmtp_draft_step_window (n_q = 1) and
+                                    wmtp_draft_context_step_window; max_keys = C */
 
 /*
  * Split plan of the attention calls.  n_q = 1 for the draft calls;
@@ -290,7 +291,7 @@ wmtp_status wmtp_draft_context_window(const uint16_t* q, const uint16_t* ring_k,
  * window) and, in one more workgroup per (request, kv head), the new positions
  * straight from k_new / v_new; the second merges the partial results and
  * appends the new positions to the rings.
- *   q                bf16 [B][Hq][D]; Hq / Hkv <= 32 (else WMTP_ERR_UNSUPPORTED)
+ *   q                bf16 [B][Hq][D]; Hq / Hkv <= 256 (else WMTP_ERR_UNSUPPORTED)
  *   ring_k, ring_v   bf16 tiled pages (in/out), B * C / 64 pages
  *   ring_pos         int32 [B][C] (in/out)
  *   ring_T           int64 [B] (in/out); negative values count as 0, values
@@ -313,6 +314,35 @@ wmtp_status wmtp_draft_step_window(const uint16_t* q, uint16_t* ring_k, uint16_t
                                    int C, int n_sink, int n_recent, float softmax_scale, float* o,
                                    float* lse, void* workspace, size_t workspace_bytes,
                                    int num_splits, void* stream);
+
+/*
+ * The draft context pass fused the same way: append n_new positions to each
+ * request's ring, then the last n_q positions (the accepted ones the draft head
+ * processes after a verify) attend causally over their own windows, in two
+ * launches instead of the three of wmtp_ring_append + wmtp_draft_context_window.
+ * (Referee major comment on App. B / Eq. 1: the draft context term of the
+ * per-step cost; verdict page, key machinery: the draft reads only the sink and
+ * the recent window.)  The result and the ring afterwards are those of
+ * wmtp_ring_append(k_new, v_new) followed by wmtp_draft_context_window with the
+ * same arguments: with L = ring_T[b] + n_new, query i is position L - n_q + i.
+ * The slots the append overwrites hold positions before every query's window
+ * because the slack condition n_q - 1 <= C - n_sink - n_recent holds (else
+ * WMTP_ERR_INVALID_ARG); n_q may exceed n_new (the earlier queries' positions
+ * are in the ring already).
+ *   q     bf16 [B][n_q][Hq][D]; o fp32 [B][n_q][Hq][D]; lse fp32 [B][n_q][Hq];
+ *         n_q * Hq / Hkv <= 256 (else WMTP_ERR_UNSUPPORTED)
+ *   other arguments as wmtp_draft_step_window; the workspace is
+ *   wmtp_workspace_bytes(WMTP_CALL_RING_STEP, B, Hq, Hkv, D, n_q, C, num_splits, 0)
+ *   bytes (partials of n_q * Hq / Hkv rows)
+ * With n_q = 1 this is wmtp_draft_step_window.
+ */
+wmtp_status wmtp_draft_context_step_window(const uint16_t* q, uint16_t* ring_k, uint16_t* ring_v,
+                                           int32_t* ring_pos, int64_t* ring_T,
+                                           const uint16_t* k_new, const uint16_t* v_new, int B,
+                                           int n_new, int n_q, int Hq, int Hkv, int D, int C,
+                                           int n_sink, int n_recent, float softmax_scale,
+                                           float* o, float* lse, void* workspace,
+                                           size_t workspace_bytes, int num_splits, void* stream);
 
 /*
  * Append n_new consecutive positions to each request's draft ring.

@@ -29,6 +29,7 @@ EXPORTS = (
     "wmtp_draft_context_window", "wmtp_verify_attn_tree", "wmtp_paged_append_fp8",
     "wmtp_draft_attn_full_fp8", "wmtp_draft_attn_window_paged_fp8", "wmtp_ring_append",
     "wmtp_paged_append", "wmtp_verify_attn", "wmtp_split_combine", "wmtp_draft_step_window",
+    "wmtp_draft_context_step_window",
 )
 
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration",
@@ -66,6 +67,7 @@ _SIGS = {
                                          _I),
     "wmtp_ring_append": ([_P] * 6 + [_I] * 6 + [_P], _I),
     "wmtp_draft_step_window": ([_P] * 7 + [_I] * 8 + [_F, _P, _P, _P, _SZ, _I, _P], _I),
+    "wmtp_draft_context_step_window": ([_P] * 7 + [_I] * 9 + [_F, _P, _P, _P, _SZ, _I, _P], _I),
     "wmtp_paged_append": ([_P] * 6 + [_I] * 6 + [_P], _I),
     "wmtp_verify_attn": ([_P] * 5 + [_I] * 8 + [_F, _P, _P, _P, _SZ, _I, _U, _P], _I),
     "wmtp_split_combine": ([_P, _P, _I, _P] + [_I] * 6 + [_P, _P, _P], _I),
@@ -244,17 +246,18 @@ def workspace_bytes(B, Hq, Hkv, D, n_q, max_keys, num_splits=0, partials_only=Fa
                                            max_keys, num_splits, 1 if partials_only else 0))
 
 
-def step_splits(B, Hq, Hkv, D, C, num_splits=0) -> int:
-    """Ring splits per (request, kv head) of ``draft_step_window`` (each group then
-    has that many plus one partials)."""
-    n = load().wmtp_plan_splits(CALL_RING_STEP, B, Hq, Hkv, D, 1, C, num_splits)
+def step_splits(B, Hq, Hkv, D, C, num_splits=0, n_q=1) -> int:
+    """Ring splits per (request, kv head) of ``draft_step_window`` and, with n_q
+    queries, ``draft_context_step_window`` (each group then has that many plus one
+    partials)."""
+    n = load().wmtp_plan_splits(CALL_RING_STEP, B, Hq, Hkv, D, n_q, C, num_splits)
     if n < 0:
         raise WmtpError("wmtp_plan_splits", 1)
     return n
 
 
-def step_workspace_bytes(B, Hq, Hkv, D, C, num_splits=0) -> int:
-    return int(load().wmtp_workspace_bytes(CALL_RING_STEP, B, Hq, Hkv, D, 1, C, num_splits, 0))
+def step_workspace_bytes(B, Hq, Hkv, D, C, num_splits=0, n_q=1) -> int:
+    return int(load().wmtp_workspace_bytes(CALL_RING_STEP, B, Hq, Hkv, D, n_q, C, num_splits, 0))
 
 
 def new_workspace(nbytes: int, device="cuda"):
@@ -492,6 +495,38 @@ def draft_step_window(q, ring: Ring, k_new, v_new, softmax_scale=1.0, o=None, ls
     o, lse = _outputs(o, lse, (B, Hq, D), (B, Hq), q.device)
     c = _invoke("wmtp_draft_step_window", (
         _ptr(q), _ptr(ring.k), _ptr(ring.v), _ptr(ring.pos), _ptr(ring.T), _ptr(k_new), _ptr(v_new), B, n_new, Hq, Hkv, D, C, ring.n_sink, ring.n_recent,
+        float(softmax_scale), _ptr(o), _ptr(lse), _ptr(workspace), workspace.numel(),
+        int(num_splits), _stream(stream)), prepare)
+    if prepare:
+        return c
+    return o, lse
+
+
+def draft_context_step_window(q, ring: Ring, k_new, v_new, softmax_scale=1.0, o=None, lse=None,
+                              workspace=None, num_splits=0, stream=None, prepare=False):
+    """The draft context pass fused with its append in two launches
+    (``wmtp_draft_context_step_window``): append k_new, v_new (bf16 [B, n_new, Hkv,
+    D]) to the rings, then query i of q ([B, n_q, Hq, D]) at position
+    ring.T + n_new - n_q + i attends over its own window."""
+    torch = _torch()
+    B, n_q, Hq, D = q.shape
+    n_new = k_new.shape[1]
+    Hkv, C = ring.Hkv, ring.C
+    _need(q, torch.bfloat16, None, "q")
+    _need(ring.k, torch.bfloat16, k_cache_shape(B * C // PAGE, Hkv, D), "ring.k")
+    _need(ring.v, torch.bfloat16, v_cache_shape(B * C // PAGE, Hkv, D), "ring.v")
+    _need(ring.pos, torch.int32, (B, C), "ring.pos")
+    _need(ring.T, torch.int64, (B,), "ring.T")
+    _need(k_new, torch.bfloat16, (B, n_new, Hkv, D), "k_new")
+    _need(v_new, torch.bfloat16, (B, n_new, Hkv, D), "v_new")
+    if workspace is None:
+        workspace = new_workspace(step_workspace_bytes(B, Hq, Hkv, D, C, num_splits, n_q),
+                                  q.device)
+    _need(workspace, torch.uint8, None, "workspace")
+    o, lse = _outputs(o, lse, (B, n_q, Hq, D), (B, n_q, Hq), q.device)
+    c = _invoke("wmtp_draft_context_step_window", (
+        _ptr(q), _ptr(ring.k), _ptr(ring.v), _ptr(ring.pos), _ptr(ring.T), _ptr(k_new),
+        _ptr(v_new), B, n_new, n_q, Hq, Hkv, D, C, ring.n_sink, ring.n_recent,
         float(softmax_scale), _ptr(o), _ptr(lse), _ptr(workspace), workspace.numel(),
         int(num_splits), _stream(stream)), prepare)
     if prepare:

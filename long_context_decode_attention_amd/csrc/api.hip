@@ -107,7 +107,7 @@ int wmtp_plan_splits(int call, int B, int Hq, int Hkv, int D, int n_q, int max_k
                      int num_splits) {
   AttnPlan p;
   if (call == WMTP_CALL_RING_STEP) {
-    if (n_q != 1 || !plan_window_step(B, Hq, Hkv, D, max_keys, num_splits, &p)) return -1;
+    if (!plan_window_step(B, Hq, Hkv, D, n_q, max_keys, num_splits, &p)) return -1;
     return p.nsplit;
   }
   if (call != WMTP_CALL_PAGED && call != WMTP_CALL_RING && call != WMTP_CALL_PAGED_WINDOW)
@@ -125,7 +125,7 @@ size_t wmtp_workspace_bytes(int call, int B, int Hq, int Hkv, int D, int n_q, in
                             int num_splits, int partials_only) {
   AttnPlan p;
   if (call == WMTP_CALL_RING_STEP) {
-    if (n_q != 1 || !plan_window_step(B, Hq, Hkv, D, max_keys, num_splits, &p)) return 0;
+    if (!plan_window_step(B, Hq, Hkv, D, n_q, max_keys, num_splits, &p)) return 0;
     return p.ws_bytes;
   }
   if (call != WMTP_CALL_PAGED && call != WMTP_CALL_RING && call != WMTP_CALL_PAGED_WINDOW)
@@ -346,19 +346,24 @@ wmtp_status wmtp_draft_context_window(const uint16_t* q, const uint16_t* ring_k,
                         flags, stream);
 }
 
-wmtp_status wmtp_draft_step_window(const uint16_t* q, uint16_t* ring_k, uint16_t* ring_v,
-                                   int32_t* ring_pos, int64_t* ring_T, const uint16_t* k_new,
-                                   const uint16_t* v_new, int B, int n_new, int Hq, int Hkv, int D,
-                                   int C, int n_sink, int n_recent, float softmax_scale, float* o,
-                                   float* lse, void* workspace, size_t workspace_bytes,
-                                   int num_splits, void* stream) {
-  if (!attn_dims_ok(B, Hq, Hkv, D)) return WMTP_ERR_INVALID_ARG;
+// Fused ring step for the last n_q of the positions the ring holds once the n_new
+// new ones are appended.
+static wmtp_status ring_step(const uint16_t* q, uint16_t* ring_k, uint16_t* ring_v,
+                             int32_t* ring_pos, int64_t* ring_T, const uint16_t* k_new,
+                             const uint16_t* v_new, int B, int n_new, int n_q, int Hq, int Hkv,
+                             int D, int C, int n_sink, int n_recent, float softmax_scale,
+                             float* o, float* lse, void* workspace, size_t workspace_bytes,
+                             int num_splits, void* stream) {
+  if (!attn_dims_ok(B, Hq, Hkv, D) || n_q < 1) return WMTP_ERR_INVALID_ARG;
   if (!head_dim_ok(D)) return WMTP_ERR_UNSUPPORTED;
-  if (Hq / Hkv > 32) return WMTP_ERR_UNSUPPORTED;
+  if ((long)n_q * (Hq / Hkv) > 256) return WMTP_ERR_UNSUPPORTED;
   if (n_new < 1 || n_new > 32 || num_splits < 0) return WMTP_ERR_INVALID_ARG;
   if (C < 64 || C % 64 != 0 || n_sink < 0 || n_sink >= C || n_recent < 1 ||
       n_recent > C - n_sink)
     return WMTP_ERR_INVALID_ARG;
+  // slack >= n_q - 1: the earliest query's window is still in the ring after the
+  // append, and every slot the append overwrites holds a position before it
+  if (n_q - 1 > C - n_sink - n_recent) return WMTP_ERR_INVALID_ARG;
   if ((long)B * C > (long)INT_MAX) return WMTP_ERR_INVALID_ARG;
   // the kernels take row maxima of raw scores before scaling: the scale must be positive
   if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return WMTP_ERR_INVALID_ARG;
@@ -369,7 +374,7 @@ wmtp_status wmtp_draft_step_window(const uint16_t* q, uint16_t* ring_k, uint16_t
       (lse && !aligned4(lse)))
     return WMTP_ERR_INVALID_ARG;
   AttnPlan p;
-  if (!plan_window_step(B, Hq, Hkv, D, C, num_splits, &p)) return WMTP_ERR_INVALID_ARG;
+  if (!plan_window_step(B, Hq, Hkv, D, n_q, C, num_splits, &p)) return WMTP_ERR_INVALID_ARG;
   if (!workspace || !aligned16(workspace) || workspace_bytes < p.ws_bytes)
     return WMTP_ERR_WORKSPACE;
   RingAppendArgs app;
@@ -396,7 +401,7 @@ wmtp_status wmtp_draft_step_window(const uint16_t* q, uint16_t* ring_k, uint16_t
   a.B = B;
   a.Hq = Hq;
   a.Hkv = Hkv;
-  a.n_q = 1;
+  a.n_q = n_q;
   a.D = D;
   a.G = p.G;
   a.R = p.R;
@@ -410,7 +415,7 @@ wmtp_status wmtp_draft_step_window(const uint16_t* q, uint16_t* ring_k, uint16_t
   a.nsplit = p.nsplit;
   a.kb_per_split = p.kb_per_split;
   a.items = p.items;
-  a.nrg = 1;
+  a.nrg = p.nrg;
   a.direct = 0;
   a.out_o = static_cast<float*>(workspace);
   a.out_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.lse_offset);
@@ -428,7 +433,7 @@ wmtp_status wmtp_draft_step_window(const uint16_t* q, uint16_t* ring_k, uint16_t
   c.B = B;
   c.Hkv = Hkv;
   c.G = p.G;
-  c.n_q = 1;
+  c.n_q = n_q;
   c.D = D;
   c.R = p.R;
   c.o = o;
@@ -436,6 +441,29 @@ wmtp_status wmtp_draft_step_window(const uint16_t* q, uint16_t* ring_k, uint16_t
   c.append = 1;
   c.app = app;
   return from_hip(launch_combine(c, st));
+}
+
+wmtp_status wmtp_draft_step_window(const uint16_t* q, uint16_t* ring_k, uint16_t* ring_v,
+                                   int32_t* ring_pos, int64_t* ring_T, const uint16_t* k_new,
+                                   const uint16_t* v_new, int B, int n_new, int Hq, int Hkv, int D,
+                                   int C, int n_sink, int n_recent, float softmax_scale, float* o,
+                                   float* lse, void* workspace, size_t workspace_bytes,
+                                   int num_splits, void* stream) {
+  return ring_step(q, ring_k, ring_v, ring_pos, ring_T, k_new, v_new, B, n_new, 1, Hq, Hkv, D, C,
+                   n_sink, n_recent, softmax_scale, o, lse, workspace, workspace_bytes,
+                   num_splits, stream);
+}
+
+wmtp_status wmtp_draft_context_step_window(const uint16_t* q, uint16_t* ring_k, uint16_t* ring_v,
+                                           int32_t* ring_pos, int64_t* ring_T,
+                                           const uint16_t* k_new, const uint16_t* v_new, int B,
+                                           int n_new, int n_q, int Hq, int Hkv, int D, int C,
+                                           int n_sink, int n_recent, float softmax_scale,
+                                           float* o, float* lse, void* workspace,
+                                           size_t workspace_bytes, int num_splits, void* stream) {
+  return ring_step(q, ring_k, ring_v, ring_pos, ring_T, k_new, v_new, B, n_new, n_q, Hq, Hkv, D,
+                   C, n_sink, n_recent, softmax_scale, o, lse, workspace, workspace_bytes,
+                   num_splits, stream);
 }
 
 wmtp_status wmtp_ring_append(uint16_t* ring_k, uint16_t* ring_v, int32_t* ring_pos,

@@ -592,16 +592,18 @@ hipError_t launch_step_d(const AttnArgs& a, int grid, hipStream_t stream) {
 
 }  // namespace
 
-bool plan_window_step(int B, int Hq, int Hkv, int D, int C, int num_splits, AttnPlan* p) {
-  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || num_splits < 0 || C < 64 || C % 64 != 0)
+bool plan_window_step(int B, int Hq, int Hkv, int D, int n_q, int C, int num_splits,
+                      AttnPlan* p) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || n_q < 1 || num_splits < 0 || C < 64 ||
+      C % 64 != 0)
     return false;
   if (D != 64 && D != 128 && D != 256) return false;
   p->G = Hq / Hkv;
-  p->R = p->G;
-  if (p->R > 32) return false;
+  p->R = n_q * p->G;
+  if (p->R > 256) return false;
   p->shared = 0;
   p->nrb = 1;
-  p->nrg = 1;
+  p->nrg = (p->R + 31) / 32;
   p->nkb = C / 32;
   // default: the windowed draft's plan (one workgroup per CU, at least four
   // tiles, one per wave, per split)
@@ -609,7 +611,7 @@ bool plan_window_step(int B, int Hq, int Hkv, int D, int C, int num_splits, Attn
   if (num_splits > 0) {
     kbps = (p->nkb + num_splits - 1) / num_splits;
   } else {
-    const long units = (long)B * Hkv;
+    const long units = (long)B * Hkv * p->nrg;
     const long per_unit = units < WMTP_TARGET_WG_SPLIT ? WMTP_TARGET_WG_SPLIT / units : 1;
     const long per = ((long)p->nkb + per_unit - 1) / per_unit;
     kbps = (int)(per < 4 ? 4 : per);
@@ -618,9 +620,9 @@ bool plan_window_step(int B, int Hq, int Hkv, int D, int C, int num_splits, Attn
   p->nsplit = (p->nkb + kbps - 1) / kbps;
   p->direct = 0;
   const long items = (long)B * Hkv * (p->nsplit + 1);
-  if (items > INT_MAX / 16) return false;
+  if (items * p->nrg > INT_MAX / 16) return false;
   p->items = (int)items;
-  p->grid = p->items;
+  p->grid = p->nrg == 1 ? p->items : ((p->items + 7) / 8) * 8 * p->nrg;
   p->part_o_bytes = (size_t)items * p->R * D * sizeof(float);
   p->lse_offset = ((p->part_o_bytes + 255) / 256) * 256;
   p->ws_bytes = p->lse_offset + (size_t)items * p->R * sizeof(float);

@@ -48,6 +48,14 @@ __global__ __launch_bounds__(256) void combine_wide_kernel(CombineArgs c, int CL
   const int cl = t % CL;
   const int sl = t / CL;
   const int nchunk = c.D / (4 * CL);
+  if (c.append) {
+    // fused draft step: the workgroups after the combine's append to the rings
+    const int merge_blocks = c.B * c.Hkv * c.R * nchunk;
+    if ((int)blockIdx.x >= merge_blocks) {
+      ring_append_block(c.app, blockIdx.x - merge_blocks);
+      return;
+    }
+  }
   const int chunk = blockIdx.x % nchunk;
   const int rest = blockIdx.x / nchunk;
   const int row = rest % c.R;
@@ -213,7 +221,6 @@ hipError_t launch_sl(const CombineArgs& c, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_combine(const CombineArgs& c, hipStream_t stream) {
-  if (c.append && c.R >= 64) return hipErrorInvalidValue;   // the append rides the few-row kernel
   if (c.R >= 64) {
     // CL: a power of two dividing D / 4, the widest that gives about 512 workgroups.
     const long pairs = (long)c.B * c.Hkv * c.R;
@@ -223,7 +230,7 @@ hipError_t launch_combine(const CombineArgs& c, hipStream_t stream) {
     CombineArgs arg = c;
     int cl_arg = CL;
     void* args[] = {&arg, &cl_arg};
-    const long grid = pairs * (c.D / (4 * CL));
+    const long grid = pairs * (c.D / (4 * CL)) + (c.append ? c.app.B : 0);
     return hipLaunchKernel(reinterpret_cast<const void*>(&combine_wide_kernel), dim3((unsigned)grid),
                            dim3(256), args, 0, stream);
   }

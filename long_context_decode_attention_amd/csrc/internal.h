@@ -65,10 +65,11 @@ bool plan_attention(int B, int Hq, int Hkv, int D, int n_q, int max_keys, int nu
 
 hipError_t launch_attention(const AttnArgs& a, const AttnPlan& p, bool ring, hipStream_t stream);
 
-// Fused windowed draft step: ring splits as the windowed draft plans them, plus
-// one workgroup per group for the new positions; items = B * Hkv * (nsplit + 1)
-// partials of R = Hq / Hkv <= 32 rows.
-bool plan_window_step(int B, int Hq, int Hkv, int D, int C, int num_splits, AttnPlan* p);
+// Fused windowed draft step (n_q queries): ring splits as the windowed draft plans
+// them, plus one workgroup per group (and row group) for the new positions; items =
+// B * Hkv * (nsplit + 1) partials of R = n_q * Hq / Hkv <= 256 rows.
+bool plan_window_step(int B, int Hq, int Hkv, int D, int n_q, int C, int num_splits,
+                      AttnPlan* p);
 hipError_t launch_window_step(const AttnArgs& a, const AttnPlan& p, hipStream_t stream);
 hipError_t launch_attention_shared(const AttnArgs& a, const AttnPlan& p, hipStream_t stream);
 int shared_kernel_waves();

@@ -238,7 +238,8 @@ def test_fused_step_argument_checks_and_plan():
     assert step(scale=0.0) == INVALID
     assert step(C=4100) == INVALID
     assert step(nr=4093) == INVALID
-    assert step(Hq=128) == UNSUPPORTED                 # 64 query rows per kv head
+    assert step(Hq=1024) == UNSUPPORTED                # 512 query rows per kv head
+    assert step(Hq=128) == WORKSPACE                   # 64 rows: two row groups
     assert step(D=96) == UNSUPPORTED
     assert step() == WORKSPACE                         # no workspace
     need = lib_mod.step_workspace_bytes(1, 32, 2, 256, 4096)
@@ -249,6 +250,37 @@ def test_fused_step_argument_checks_and_plan():
     assert need == (parts * 16 * 256 * 4 + 255) // 256 * 256 + parts * 16 * 4
     assert lib_mod.step_splits(1, 32, 2, 256, 4096, 1) == 1
     assert lib_mod.step_splits(1, 32, 2, 256, 4096, 1000) == 4096 // 32
+
+
+def test_fused_context_step_argument_checks_and_plan():
+    """wmtp_draft_context_step_window: the slack and row checks on top of the fused
+    step's, and a plan of n_q * G rows in row groups of 32."""
+    lib = _lib()
+    P = ctypes.c_void_p
+
+    def step(**kw):
+        a = dict(B=1, n_new=8, n_q=8, Hq=32, Hkv=2, C=4160, ns=4, nr=4092, ws=None, wsb=0)
+        a.update(kw)
+        return lib.wmtp_draft_context_step_window(
+            P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), a["B"], a["n_new"],
+            a["n_q"], a["Hq"], a["Hkv"], 256, a["C"], a["ns"], a["nr"], 1.0, P(FAKE), None,
+            P(a["ws"]) if a["ws"] else None, a["wsb"], 0, None)
+    assert step(n_q=0) == INVALID
+    assert step(n_q=66, Hq=2) == INVALID               # slack 64 < n_q - 1
+    assert step(n_q=65, Hq=2) == WORKSPACE             # slack 64 = n_q - 1
+    assert step(n_q=8, C=4096) == INVALID              # no slack at all
+    assert step(n_q=17) == UNSUPPORTED                 # 17 * 16 rows per kv head
+    assert step(n_new=33) == INVALID
+    assert step() == WORKSPACE
+    need = lib_mod.step_workspace_bytes(1, 32, 2, 256, 4160, 0, 8)
+    assert step(ws=FAKE, wsb=need - 1) == WORKSPACE
+    n = lib_mod.step_splits(1, 32, 2, 256, 4160, 0, 8)
+    parts = 2 * (n + 1)
+    assert need == (parts * 128 * 256 * 4 + 255) // 256 * 256 + parts * 128 * 4
+    # n_q = 1 plans as the single-query step
+    assert lib_mod.step_splits(1, 32, 2, 256, 4160, 0, 1) == lib_mod.step_splits(1, 32, 2, 256, 4160)
+    # row groups share the workgroup target: four groups of 32 rows, fewer splits
+    assert n <= lib_mod.step_splits(1, 32, 2, 256, 4160)
 
 
 def test_plan_rounds_for_several_long_sequences():
