@@ -81,8 +81,8 @@ def test_ctx1m_draft_chain_and_verify_full_size():
 
 def test_ctx1m_next_rows_full_size():
     """The widened rows at 1M: the truncated paged index, the fp8 draft KV, the
-    draft context pass over a ring with slack and the tree verify, each in its
-    automatic split plan, checked on kv head 1's rows."""
+    draft context pass over a ring with slack (also fused with its append) and the
+    tree verify, each in its automatic split plan, checked on kv head 1's rows."""
     import long_context_decode_attention_amd as lib
     from long_context_decode_attention_amd import scenario as scn
     from oracle import fp8 as F
@@ -110,7 +110,16 @@ def test_ctx1m_next_rows_full_size():
     scn.fill_ring(ring, 0, sc.K[0][:L], sc.V[0][:L])
     qc = W.queries(103, "q_ctx", (1, n_q, cfg["Hq"]), D)
     oc, lc = lib.draft_context_window(dev_bf16(qc), ring)
+    # the same pass fused with the append of its 8 positions, on a ring holding the rest
+    ring_f = lib.new_ring(1, cfg["C"] + 64, Hkv, D, ns, nr)
+    scn.fill_ring(ring_f, 0, sc.K[0][:L - n_q], sc.V[0][:L - n_q])
+    kc, vc = dev_bf16(sc.K[0][L - n_q:L][None]), dev_bf16(sc.V[0][L - n_q:L][None])
+    ocf, lcf = lib.draft_context_step_window(dev_bf16(qc), ring_f, kc, vc)
     torch().cuda.synchronize()
+    t = torch()
+    assert t.equal(ring_f.T, ring.T) and t.equal(ring_f.pos, ring.pos)
+    assert t.equal(ring_f.k.view(t.int16), ring.k.view(t.int16))
+    assert t.equal(ring_f.v.view(t.int16), ring.v.view(t.int16))
     _say("oracle on kv head 1")
     qg, Kg, Vg = _group(q[0], sc.K[0], sc.V[0], 1, G)
     ro, rl = OA.draft_window(qg, Kg, Vg, L, ns, nr, 1.0)
@@ -125,8 +134,9 @@ def test_ctx1m_next_rows_full_size():
     qcg = qc[0][:, G:2 * G]
     ro, rl = OA.draft_context_window(qcg, Kg, Vg, L, ns, nr, 1.0)
     compare(oc[0, :, G:2 * G], lc[0, :, G:2 * G], ro, rl, "context pass 1M")
-    _say("context pass matches")
-    del sc, ring, k8, v8
+    compare(ocf[0, :, G:2 * G], lcf[0, :, G:2 * G], ro, rl, "fused context pass 1M")
+    _say("context pass matches (and fused with its append; rings equal)")
+    del sc, ring, ring_f, k8, v8
     _say("building target state (1M + 8 positions)")
     vs = VerifyScenario(cfg, 104, [S], n_q, poison=False)
     vs.append_proposed()

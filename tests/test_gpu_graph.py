@@ -36,10 +36,12 @@ def test_decode_step_graph_replays_match_eager():
     V = W.kv_positions(seed, "draft_v", 0, 0, S + steps + n_q, Hkv, D)
     ring = lib.new_ring(1, C, Hkv, D, n_sink, n_recent)
     sc.fill_ring(ring, 0, K[:S], V[:S])
+    ring_c = lib.new_ring(1, C + 64, Hkv, D, n_sink, n_recent)   # slack for the context pass
+    sc.fill_ring(ring_c, 0, K[:S], V[:S])
     n_pages = (S + steps + n_q + 63) // 64
     kv = sc.alloc_paged_kv([S + steps + n_q], Hkv, D, W.page_permutation(seed, "draft_k", n_pages))
     sc.fill_paged(kv, 0, 0, K[:S], V[:S])
-    state = [ring.k, ring.v, ring.pos, ring.T, kv.k, kv.v]
+    state = [ring.k, ring.v, ring.pos, ring.T, kv.k, kv.v, ring_c.k, ring_c.v, ring_c.pos, ring_c.T]
     snap = [x.clone() for x in state]
 
     qd = [dev_bf16(W.queries(seed, "q_draft", (1, Hq), D, step=j)) for j in range(steps)]
@@ -60,6 +62,9 @@ def test_decode_step_graph_replays_match_eager():
     lses = [t.empty(1, Hq, device="cuda") for _ in range(steps)]
     o_f, l_f = t.empty(1, Hq, D, device="cuda"), t.empty(1, Hq, device="cuda")
     o_v, l_v = t.empty(1, n_q, Hq, D, device="cuda"), t.empty(1, n_q, Hq, device="cuda")
+    qc = dev_bf16(W.queries(seed, "q_ctx", (1, n_q, Hq), D))
+    ws_c = lib.new_workspace(lib.step_workspace_bytes(1, Hq, Hkv, D, C + 64, 0, n_q))
+    o_c, l_c = t.empty(1, n_q, Hq, D, device="cuda"), t.empty(1, n_q, Hq, device="cuda")
 
     def step():
         for j in range(steps):
@@ -68,6 +73,7 @@ def test_decode_step_graph_replays_match_eager():
         lib.draft_attn_full(qd[0], kv.k, kv.v, kv.block_table, lens, Lmax, 1.0, o_f, l_f, ws_f)
         lib.paged_append(kv.k, kv.v, kv.block_table, pos_t, kt, vt)
         lib.verify_attn(qv, kv.k, kv.v, kv.block_table, lens_t, Lmax, 1.0, o_v, l_v, ws_v)
+        lib.draft_context_step_window(qc, ring_c, kt, vt, 1.0, o_c, l_c, ws_c)
 
     def restore():
         for x, y in zip(state, snap):
@@ -75,7 +81,7 @@ def test_decode_step_graph_replays_match_eager():
         t.cuda.synchronize()
 
     def results():
-        return [x.clone() for x in outs + lses + [o_f, l_f, o_v, l_v] + state]
+        return [x.clone() for x in outs + lses + [o_f, l_f, o_v, l_v, o_c, l_c] + state]
 
     restore()
     step()
@@ -89,7 +95,7 @@ def test_decode_step_graph_replays_match_eager():
     t.cuda.synchronize()
     for r in range(4):
         restore()
-        for x in outs + lses + [o_f, l_f, o_v, l_v]:
+        for x in outs + lses + [o_f, l_f, o_v, l_v, o_c, l_c]:
             x.fill_(float("nan"))   # stale results must not pass for replayed ones
         t.cuda.synchronize()
         g.replay()
@@ -102,5 +108,5 @@ def test_decode_step_graph_replays_match_eager():
                 assert t.equal(a.view(t.int16), b.view(t.int16)), f"replay {r}: cache {i} differs"
             else:
                 assert t.equal(a, b), f"replay {r}: state {i} differs"
-        assert int(ring.T[0]) == S + steps
+        assert int(ring.T[0]) == S + steps and int(ring_c.T[0]) == S + n_q
     assert np.isfinite(eager[0].cpu().numpy()).all()
