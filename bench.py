@@ -52,7 +52,7 @@ W_CONFIG_NAMES = ("ctx8k_g16x2_d128", "ctx128k_g32x4_d128", "ctx1m_g32x2_d256",
 # keyed by a hash of the sources that kernel is built from: a changed kernel
 # reports null until it is measured again.
 MEASURED_TRAFFIC = {
-    "41f953801559dacb": {"read": 2.148e+09, "write": 4.211e+06, "keys": 1048587},
+    "5c4123d36bd622da": {"read": 2.148e+09, "write": 4.211e+06, "keys": 1048587},
 }
 KERNEL_SOURCES = ("csrc/attn.hip", "csrc/attn_device.h", "csrc/common.h")
 
@@ -581,7 +581,8 @@ def main() -> int:
     ws_f = lib.new_workspace(lib.workspace_bytes(B, Hq, Hkv, D, 1, max_d, args.num_splits,
                                                  partials_only=True), dev)
     ws_8 = lib.new_workspace(lib.workspace_bytes(B, Hq, Hkv, D, 1, max_d, args.num_splits,
-                                                 partials_only=True), dev)
+                                                 partials_only=True, fp8=True), dev)
+    splits_8 = lib.plan_splits(B, Hq, Hkv, D, 1, max_d, args.num_splits, fp8=True)
     o_8 = torch.empty(B, Hq, D, device=dev)
     l_8 = torch.empty(B, Hq, device=dev)
     ws_v = lib.new_workspace(lib.workspace_bytes(B, Hq, Hkv, D, n_q, max_t), dev)
@@ -664,8 +665,9 @@ def main() -> int:
                 lib.draft_attn_full_fp8(qd[k, j], k8, v8, dkv.block_table, d_len[k, j], max_d,
                                         workspace=ws_8, num_splits=args.num_splits,
                                         partials_only=True, prepare=True),
-                lib.split_combine(*lib.partials_view(ws_8, B, Hq, Hkv, D, 1, max_d, args.num_splits),
-                                  B, Hkv, G, 1, splits_per_group=splits_f,
+                lib.split_combine(*lib.partials_view(ws_8, B, Hq, Hkv, D, 1, max_d, args.num_splits,
+                                                     fp8=True),
+                                  B, Hkv, G, 1, splits_per_group=splits_8,
                                   o=o_8.view(B, 1, Hq, D), lse=l_8.view(B, 1, Hq), prepare=True)))
         plan.append((win, full, wpg, ver, ctx, full8, fused))
     # The windowed arm's draft steps once more, each bench step's seven recorded in a

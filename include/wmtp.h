@@ -86,6 +86,7 @@ const char* wmtp_status_string(wmtp_status s);
 #define WMTP_CALL_PAGED_WINDOW 2 /* wmtp_draft_attn_window_paged */
 #define WMTP_CALL_RING_STEP 3    /* wmtp_draft_step_window (n_q = 1) and
                                     wmtp_draft_context_step_window; max_keys = C */
+#define WMTP_CALL_PAGED_FP8 4    /* wmtp_draft_attn_full_fp8 */
 
 /*
  * Split plan of the attention calls.  n_q = 1 for the draft calls;
@@ -98,7 +99,8 @@ const char* wmtp_status_string(wmtp_status s);
  * the new positions'.  With num_splits = 0, paged calls over several sequences
  * of 64K keys or more plan about four workgroups per compute unit (the lengths
  * are on the device, and the extra rounds even out unequal ones), other calls
- * about one.
+ * about one; WMTP_CALL_PAGED_FP8 at D = 128 over 64K keys or more plans twice
+ * the workgroups of WMTP_CALL_PAGED (two fit on a compute unit).
  */
 int wmtp_plan_splits(int call, int B, int Hq, int Hkv, int D, int n_q, int max_keys,
                      int num_splits);
@@ -164,7 +166,8 @@ wmtp_status wmtp_draft_attn_full(const uint16_t* q, const uint16_t* k_cache,
  * values (every e4m3 value is a bf16 value, so the MFMA operands are exact);
  * k_scale folds into the logit scale, v_scale into the output.  At most 32
  * query rows per kv head (Hq / Hkv), else WMTP_ERR_UNSUPPORTED.  Workspace and
- * plan as the bf16 calls.
+ * plan: wmtp_draft_attn_full_fp8 as WMTP_CALL_PAGED_FP8 (below),
+ * wmtp_draft_attn_window_paged_fp8 as the bf16 truncated index.
  */
 wmtp_status wmtp_paged_append_fp8(uint8_t* k_cache, uint8_t* v_cache, const int32_t* block_table,
                                   const int32_t* start_pos, const uint16_t* k_new,

@@ -223,17 +223,23 @@ CALL_PAGED = 0
 CALL_RING = 1
 CALL_PAGED_WINDOW = 2
 CALL_RING_STEP = 3
+CALL_PAGED_FP8 = 4
 
 
-def _call_kind(ring, paged_window):
-    return CALL_RING if ring else (CALL_PAGED_WINDOW if paged_window else CALL_PAGED)
+def _call_kind(ring, paged_window, fp8=False):
+    if ring:
+        return CALL_RING
+    if paged_window:
+        return CALL_PAGED_WINDOW
+    return CALL_PAGED_FP8 if fp8 else CALL_PAGED
 
 
 def plan_splits(B, Hq, Hkv, D, n_q, max_keys, num_splits=0, ring=False,
-                paged_window=False) -> int:
+                paged_window=False, fp8=False) -> int:
     """Splits per (sequence, kv head); with ``paged_window`` max_keys is the window
-    n_sink + n_recent of ``draft_attn_window_paged``."""
-    n = load().wmtp_plan_splits(_call_kind(ring, paged_window), B, Hq, Hkv, D, n_q, max_keys,
+    n_sink + n_recent of ``draft_attn_window_paged``; ``fp8`` for
+    ``draft_attn_full_fp8``."""
+    n = load().wmtp_plan_splits(_call_kind(ring, paged_window, fp8), B, Hq, Hkv, D, n_q, max_keys,
                                 num_splits)
     if n < 0:
         raise WmtpError("wmtp_plan_splits", 1)
@@ -241,9 +247,9 @@ def plan_splits(B, Hq, Hkv, D, n_q, max_keys, num_splits=0, ring=False,
 
 
 def workspace_bytes(B, Hq, Hkv, D, n_q, max_keys, num_splits=0, partials_only=False,
-                    ring=False, paged_window=False) -> int:
-    return int(load().wmtp_workspace_bytes(_call_kind(ring, paged_window), B, Hq, Hkv, D, n_q,
-                                           max_keys, num_splits, 1 if partials_only else 0))
+                    ring=False, paged_window=False, fp8=False) -> int:
+    return int(load().wmtp_workspace_bytes(_call_kind(ring, paged_window, fp8), B, Hq, Hkv, D,
+                                           n_q, max_keys, num_splits, 1 if partials_only else 0))
 
 
 def step_splits(B, Hq, Hkv, D, C, num_splits=0, n_q=1) -> int:
@@ -266,11 +272,11 @@ def new_workspace(nbytes: int, device="cuda"):
 
 
 def partials_view(workspace, B, Hq, Hkv, D, n_q, max_keys, num_splits=0, ring=False,
-                  paged_window=False):
+                  paged_window=False, fp8=False):
     """(part_o [P, R, D], part_lse [P, R]) views of a workspace left by a
     partials-only call with the same arguments."""
     torch = _torch()
-    splits = plan_splits(B, Hq, Hkv, D, n_q, max_keys, num_splits, ring, paged_window)
+    splits = plan_splits(B, Hq, Hkv, D, n_q, max_keys, num_splits, ring, paged_window, fp8)
     P = B * Hkv * splits
     R = n_q * (Hq // Hkv)
     ob = P * R * D * 4
@@ -588,7 +594,7 @@ def draft_attn_full_fp8(q, k_cache, v_cache, block_table, seq_lens, max_seq_len,
     _need(seq_lens, torch.int32, (B,), "seq_lens")
     if window is None:
         need = workspace_bytes(B, Hq, Hkv, D, 1, min(int(max_seq_len), max_pages * PAGE),
-                               num_splits, partials_only)
+                               num_splits, partials_only, fp8=True)
     else:
         need = workspace_bytes(B, Hq, Hkv, D, 1, int(window[0]) + int(window[1]), num_splits,
                                partials_only, paged_window=True)

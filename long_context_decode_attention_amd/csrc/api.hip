@@ -37,7 +37,7 @@ wmtp_status run_attention(AttnArgs a, bool ring, int max_keys, int plan_keys, fl
   const int partials_only = (flags & WMTP_FLAG_PARTIALS_ONLY) ? 1 : 0;
   AttnPlan p;
   if (!plan_attention(a.B, a.Hq, a.Hkv, a.D, a.n_q, plan_keys, num_splits, partials_only, ring,
-                      &p))
+                      &p, a.kv8 != 0))
     return (a.n_q * (a.Hq / a.Hkv) > 256) ? WMTP_ERR_UNSUPPORTED : WMTP_ERR_INVALID_ARG;
   if (a.win && p.shared) return WMTP_ERR_UNSUPPORTED;   // truncated index: split kernel only
   if (a.kv8 && p.shared) return WMTP_ERR_UNSUPPORTED;   // fp8 caches: split kernel only
@@ -110,13 +110,15 @@ int wmtp_plan_splits(int call, int B, int Hq, int Hkv, int D, int n_q, int max_k
     if (!plan_window_step(B, Hq, Hkv, D, n_q, max_keys, num_splits, &p)) return -1;
     return p.nsplit;
   }
-  if (call != WMTP_CALL_PAGED && call != WMTP_CALL_RING && call != WMTP_CALL_PAGED_WINDOW)
+  if (call != WMTP_CALL_PAGED && call != WMTP_CALL_RING && call != WMTP_CALL_PAGED_WINDOW &&
+      call != WMTP_CALL_PAGED_FP8)
     return -1;
   if (call == WMTP_CALL_PAGED_WINDOW) {
     if (max_keys < 0) return -1;
     max_keys = window_plan_keys(max_keys, INT_MAX);
   }
-  if (!plan_attention(B, Hq, Hkv, D, n_q, max_keys, num_splits, 0, call == WMTP_CALL_RING, &p))
+  if (!plan_attention(B, Hq, Hkv, D, n_q, max_keys, num_splits, 0, call == WMTP_CALL_RING, &p,
+                      call == WMTP_CALL_PAGED_FP8))
     return -1;
   return p.nsplit;
 }
@@ -128,14 +130,15 @@ size_t wmtp_workspace_bytes(int call, int B, int Hq, int Hkv, int D, int n_q, in
     if (!plan_window_step(B, Hq, Hkv, D, n_q, max_keys, num_splits, &p)) return 0;
     return p.ws_bytes;
   }
-  if (call != WMTP_CALL_PAGED && call != WMTP_CALL_RING && call != WMTP_CALL_PAGED_WINDOW)
+  if (call != WMTP_CALL_PAGED && call != WMTP_CALL_RING && call != WMTP_CALL_PAGED_WINDOW &&
+      call != WMTP_CALL_PAGED_FP8)
     return 0;
   if (call == WMTP_CALL_PAGED_WINDOW) {
     if (max_keys < 0) return 0;
     max_keys = window_plan_keys(max_keys, INT_MAX);
   }
   if (!plan_attention(B, Hq, Hkv, D, n_q, max_keys, num_splits, partials_only,
-                      call == WMTP_CALL_RING, &p))
+                      call == WMTP_CALL_RING, &p, call == WMTP_CALL_PAGED_FP8))
     return 0;
   return p.ws_bytes;
 }

@@ -639,7 +639,7 @@ hipError_t launch_window_step(const AttnArgs& a, const AttnPlan& p, hipStream_t 
 }
 
 bool plan_attention(int B, int Hq, int Hkv, int D, int n_q, int max_keys, int num_splits,
-                    int partials_only, bool ring, AttnPlan* p) {
+                    int partials_only, bool ring, AttnPlan* p, bool kv8) {
   if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || n_q < 1 || max_keys < 0 || num_splits < 0)
     return false;
   if (D != 64 && D != 128 && D != 256) return false;
@@ -689,6 +689,12 @@ bool plan_attention(int B, int Hq, int Hkv, int D, int n_q, int max_keys, int nu
   // at 79 % against 72 %).  One sequence keeps one round (its second round
   // would add a prologue, a merge and a tail), and short key ranges (windows) too.
   if (!ring && B > 1 && p->nkb >= 2048) target *= 4;
+  // fp8 caches at D = 128: the split kernel fits two workgroups per CU (246
+  // registers per wave, 73 KB of LDS), and with 8 KB per tile it needs the second
+  // one's loads in flight: twice the workgroups for long key ranges (measured at
+  // 128K keys, 32/4 heads: 33 us against 44 us; the bf16 kernel, at 283
+  // registers, stays at one per CU)
+  if (kv8 && D == 128 && !ring && !p->shared && p->nkb >= 2048) target *= 2;
   int kbps;
   if (num_splits > 0) {
     kbps = (p->nkb + num_splits - 1) / num_splits;

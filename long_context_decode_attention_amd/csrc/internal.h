@@ -60,8 +60,9 @@ struct AttnPlan {
   size_t part_o_bytes, lse_offset, ws_bytes;
 };
 
+// kv8: the call reads fp8 caches (the plan may then aim at more workgroups)
 bool plan_attention(int B, int Hq, int Hkv, int D, int n_q, int max_keys, int num_splits,
-                    int partials_only, bool ring, AttnPlan* p);
+                    int partials_only, bool ring, AttnPlan* p, bool kv8 = false);
 
 hipError_t launch_attention(const AttnArgs& a, const AttnPlan& p, bool ring, hipStream_t stream);
 

@@ -297,6 +297,20 @@ def test_plan_rounds_for_several_long_sequences():
     assert lib_mod.plan_splits(8, 32, 4, 128, 4, 1 << 20) * 32 == 1024
 
 
+def test_plan_fp8_head_dim_128_two_per_cu():
+    """The fp8 native pass at D = 128 over 64K keys or more plans twice the
+    workgroups of the bf16 pass (two fit on a CU); other shapes plan the same."""
+    _lib()
+    ps = lib_mod.plan_splits
+    assert ps(1, 32, 4, 128, 1, 131072, fp8=True) == 2 * ps(1, 32, 4, 128, 1, 131072)
+    assert ps(8, 32, 4, 128, 1, 1 << 20, fp8=True) == 2 * ps(8, 32, 4, 128, 1, 1 << 20)
+    assert ps(1, 32, 2, 256, 1, 1 << 20, fp8=True) == ps(1, 32, 2, 256, 1, 1 << 20)
+    assert ps(1, 32, 4, 128, 1, 60000, fp8=True) == ps(1, 32, 4, 128, 1, 60000)
+    assert ps(1, 32, 4, 128, 1, 131072, 7, fp8=True) == 7          # explicit split count
+    wb = lib_mod.workspace_bytes
+    assert wb(1, 32, 4, 128, 1, 131072, fp8=True) > wb(1, 32, 4, 128, 1, 131072)
+
+
 def _imports(path):
     names = set()
     for dirpath, _, files in os.walk(path):

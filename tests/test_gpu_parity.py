@@ -683,6 +683,7 @@ def test_fp8_append_codes_bitexact(k_scale, v_scale):
     ("ctx1m_g32x2_d256", 40000, 1.0, 1.0, 0),
     ("ctx1m_g32x2_d256", 9000, 0.5, 2.0, 1),
     ("ctx128k_g32x4_d128", 20011, 0.25, 0.5, 0),
+    ("ctx128k_g32x4_d128", 70001, 1.0, 1.0, 0),     # >= 64K keys: twice the workgroups
     ("nope8l_1m_g64x2_d128", 3000, 1.0, 1.0, 3),     # 32 rows per kv head
     ("ctx8k_g16x2_d128", 65, 1.0, 1.0, 0),
 ])
