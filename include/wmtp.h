@@ -99,8 +99,9 @@ const char* wmtp_status_string(wmtp_status s);
  * the new positions'.  With num_splits = 0, paged calls over several sequences
  * of 64K keys or more plan about four workgroups per compute unit (the lengths
  * are on the device, and the extra rounds even out unequal ones), other calls
- * about one; WMTP_CALL_PAGED_FP8 at D = 128 over 64K keys or more plans twice
- * the workgroups of WMTP_CALL_PAGED (two fit on a compute unit).
+ * about one; WMTP_CALL_PAGED_FP8 at D = 128 over 64K keys or more aims at twice
+ * the workgroups of WMTP_CALL_PAGED (two fit on a compute unit; whole tiles per
+ * split, so the count is about twice).
  */
 int wmtp_plan_splits(int call, int B, int Hq, int Hkv, int D, int n_q, int max_keys,
                      int num_splits);

@@ -704,6 +704,19 @@ def test_fp8_draft_full_and_window(cfg_name, S, k_scale, v_scale, num_splits):
     compare(o[0], l[0], ro, rl, f"fp8 full {cfg_name} S={S}")
     rwo, rwl = OA.draft_window(q[0], c["Kq"], c["Vq"], S, cfg["n_sink"], cfg["n_recent"], 1.0)
     compare(ow[0], lw[0], rwo, rwl, f"fp8 window {cfg_name} S={S}")
+    if S >= 65536:
+        # the partials of the fp8 plan (twice the workgroups at D = 128) merge to the same
+        # result through the exported combine, in the layout partials_view(fp8=True) gives
+        G = cfg["Hq"] // cfg["Hkv"]
+        ws = lib.draft_attn_full_fp8(dev_bf16(q), c["k8"], c["v8"], c["bt"], dev_i32([S]), S,
+                                     k_scale, v_scale, 1.0, partials_only=True)
+        po, pl = lib.partials_view(ws, 1, cfg["Hq"], cfg["Hkv"], cfg["D"], 1, S, fp8=True)
+        splits = lib.plan_splits(1, cfg["Hq"], cfg["Hkv"], cfg["D"], 1, S, fp8=True)
+        bf16_splits = lib.plan_splits(1, cfg["Hq"], cfg["Hkv"], cfg["D"], 1, S)
+        assert bf16_splits < splits <= 2 * bf16_splits     # about twice (whole tiles per split)
+        oc, lc = lib.split_combine(po, pl, 1, cfg["Hkv"], G, 1, splits_per_group=splits)
+        torch().cuda.synchronize()
+        assert torch().equal(oc.view(o.shape), o) and torch().equal(lc.view(l.shape), l)
 
 
 def test_draft_context_pass_batch_of_two():
