@@ -170,11 +170,14 @@ __device__ __forceinline__ void load_v_new(VTile<D, false>& t, const uint16_t* s
 
 // Which of this lane's 16 keys exist for every row: inside the sequence length
 // (and, for a truncated paged index, below sink_end or from r0 on), or (ring)
-// holding a position of the current window.
+// holding a position of the current window.  Ring mode reads positions below
+// p_end only: T for a window over the ring; the count before the append for the
+// ring splits of a fused step, whose slots may still hold positions at or past
+// that count from before a rollback (the new positions come from k_new alone).
 template <int D, bool RING, bool KV8>
 __device__ __forceinline__ uint32_t present_keys(const KTile<D, RING, KV8>& t, const AttnArgs& a,
-                                                 int kb, int L, int T, int h, int sink_end,
-                                                 int r0) {
+                                                 int kb, int L, int T, int p_end, int h,
+                                                 int sink_end, int r0) {
   if constexpr (RING) {
     uint32_t keep = 0;
 #pragma unroll
@@ -182,7 +185,7 @@ __device__ __forceinline__ uint32_t present_keys(const KTile<D, RING, KV8>& t, c
       const int p = t.pos[i];
       // in the window of some query: the last n_q positions T - n_q .. T - 1 each
       // see the sink and their own last n_recent positions
-      const bool ok = p >= 0 && p < T && (p < a.n_sink || p >= T - (a.n_q - 1) - a.n_recent);
+      const bool ok = p >= 0 && p < p_end && (p < a.n_sink || p >= T - (a.n_q - 1) - a.n_recent);
       keep |= (ok ? 1u : 0u) << i;
     }
     return keep;
@@ -271,13 +274,17 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
     const int64_t t_max = STEP ? INT_MAX - 64 : INT_MAX;   // step: room for the new positions
     T = t64 < 0 ? 0 : (t64 > t_max ? (int)t_max : (int)t64);
     // fused step: the window ends after the new positions; the slots they will
-    // overwrite hold positions outside it, so the window test skips them
+    // overwrite hold positions outside it, so the window test skips them, and
+    // slots holding positions >= T0 (left by a rollback) are skipped by p_end
     T0 = T;
     if (STEP) T += a.app.n_new;
   } else {
     L = len_raw < 0 ? 0 : (len_raw > a.max_keys ? a.max_keys : len_raw);
   }
   const int nkb = (L + 31) >> 5;
+  // ring: the positions a tile may contribute (fused step: the ring splits stop
+  // at the count before the append; the new positions' workgroup reads T0 .. T - 1)
+  const int p_end = (STEP && !newk) ? T0 : T;
   // Truncated paged index (win): the key set [0, sink_end) u [r0, L) as virtual
   // tiles, the sink tiles [0, st_end) then the recent tiles from kr on; phys()
   // maps a virtual tile to its 32-key tile of the sequence.
@@ -387,7 +394,7 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
   // S^T of tile kb, refill K (when there is a next tile), masked scores.
   auto scores_of = [&](auto has_next) {
     const int pk = phys(kb);   // the tile's place in the sequence
-    keep = ok ? present_keys<D, RING, KV8>(kt, a, pk, L, T, h, sink_end, r0) : 0u;
+    keep = ok ? present_keys<D, RING, KV8>(kt, a, pk, L, T, p_end, h, sink_end, r0) : 0u;
     bool all_vis;
     uint32_t rvis[NB];   // ring, several queries: the keys in each row's own window
     if (RING) {

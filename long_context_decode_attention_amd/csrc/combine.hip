@@ -236,11 +236,13 @@ hipError_t launch_combine(const CombineArgs& c, hipStream_t stream) {
   }
   // Split lanes: the smallest power of two covering the splits of a group (all 64
   // with a CSR split list, whose counts the host does not see), and no fewer
-  // than 256 / (D / 4) so that a workgroup's column lanes fit in one row.
+  // than make the column lanes 256 / sl a divisor of D / 4, so that a row's column
+  // blocks cover it exactly (D is a multiple of 16: sl = 64 gives 4 column lanes,
+  // which always divide D / 4).
   int splits = c.indptr ? 64 : c.splits_per_group;
   int sl = 1;
   while (sl < splits && sl < 64) sl *= 2;
-  while (256 / sl > c.D / 4) sl *= 2;
+  while (sl < 64 && (256 / sl > c.D / 4 || (c.D / 4) % (256 / sl) != 0)) sl *= 2;
   switch (sl) {
     case 1: return launch_sl<1>(c, stream);
     case 2: return launch_sl<2>(c, stream);

@@ -348,20 +348,34 @@ def test_partials_only_then_combine_equals_direct():
     assert torch().equal(o.view(-1), o2.view(-1)) and torch().equal(l.view(-1), l2.view(-1))
 
 
-def test_split_combine_against_oracle_csr():
-    """Direct test of the combine with a CSR split list, empty splits and an empty group."""
+@pytest.mark.parametrize("D,G,n_q,csr", [
+    (128, 4, 2, True),      # 8 rows: the few-row merge
+    (96, 4, 2, True),       # head dims that are not powers of two: every column written
+    (192, 8, 1, True),
+    (48, 2, 1, False),
+    (80, 16, 1, False),
+    (240, 4, 4, False),
+    (16, 1, 1, True),
+    (96, 16, 4, True),      # 64 rows: the many-row merge
+    (192, 32, 4, False),
+])
+def test_split_combine_against_oracle_csr(D, G, n_q, csr):
+    """Direct test of the combine with empty splits and an empty group, at head dims
+    that are multiples of 16 up to 256, through a CSR split list or a fixed count."""
     lib = _lib()
     rng = np.random.default_rng(13)
-    B, Hkv, G, n_q, D = 2, 3, 4, 2, 128
+    B, Hkv = 2, 3
     R = G * n_q
-    counts = [3, 0, 5, 1, 7, 2]                      # group 1 has no split
+    counts = [3, 0, 5, 1, 7, 2] if csr else [4] * (B * Hkv)   # group 1 has no split (CSR)
     indptr = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     P = int(indptr[-1])
     po = rng.standard_normal((P, R, D)).astype(np.float32)
     pl = (rng.standard_normal((P, R)) * 3).astype(np.float32)
     pl[1, :] = -np.inf                               # an empty split
+    o = torch().full((B, n_q, Hkv * G, D), float("nan"), device="cuda")   # unwritten shows
     o, l = lib.split_combine(torch().tensor(po, device="cuda"), torch().tensor(pl, device="cuda"),
-                             B, Hkv, G, n_q, split_indptr=dev_i32(indptr))
+                             B, Hkv, G, n_q, split_indptr=dev_i32(indptr) if csr else None,
+                             splits_per_group=0 if csr else 4, o=o)
     torch().cuda.synchronize()
     o = o.cpu().numpy()
     l = l.cpu().numpy()

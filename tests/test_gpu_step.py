@@ -288,3 +288,43 @@ def test_fused_context_step_random_shapes(case):
     Hq, Hkv, D, C, n_sink, n_recent, S, n_new, n_q, num_splits = case
     _run_chain(Hq, Hkv, D, C, n_sink, n_recent, S, 2, n_new=n_new, num_splits=num_splits,
                seed=37, n_q=n_q)
+
+
+@pytest.mark.parametrize("n_q,n_new,rolled", [
+    (0, 1, 3),     # single-query step after rolling back 3 speculative positions
+    (0, 2, 3),     # two new positions; one stale slot stays past the window's end
+    (4, 3, 3),     # context pass over the re-appended positions
+    (8, 8, 8),     # context pass re-appending every rolled-back position
+])
+def test_fused_steps_after_rollback(n_q, n_new, rolled):
+    """A rollback (a smaller ring_T) leaves slots holding positions >= ring_T with
+    the rejected drafts' K/V.  The fused step re-appends those positions with new
+    values: its result must count each position once, with the new values (the
+    oracle over the accepted prefix plus the new positions), and the ring afterwards
+    must equal the one that append-then-window leaves."""
+    lib = _lib()
+    Hq, Hkv, D, C, n_sink, n_recent, T = 16, 2, 128, 1024, 4, 960, 5000
+    K_old = W.kv_positions(60, "draft_k", 0, 0, T + rolled, Hkv, D)
+    V_old = W.kv_positions(60, "draft_v", 0, 0, T + rolled, Hkv, D)
+    K_new = W.kv_positions(61, "draft_k", 0, T, T + n_new, Hkv, D)
+    V_new = W.kv_positions(61, "draft_v", 0, T, T + n_new, Hkv, D)
+    fused, ref = _rings(1, C, Hkv, D, n_sink, n_recent, [K_old], [V_old], [T + rolled])
+    fused.T.fill_(T)
+    ref.T.fill_(T)
+    K = np.concatenate([K_old[:T], K_new])
+    V = np.concatenate([V_old[:T], V_new])
+    kt, vt = dev_bf16(K_new[None]), dev_bf16(V_new[None])
+    L = T + n_new
+    if n_q:
+        q = W.queries(62, "q_ctx", (1, n_q, Hq), D)
+        ws = lib.new_workspace(lib.step_workspace_bytes(1, Hq, Hkv, D, C, 0, n_q))
+        o, lse = lib.draft_context_step_window(dev_bf16(q), fused, kt, vt, 1.0, workspace=ws)
+        ro, rl = OA.draft_context_window(q[0], K, V, L, n_sink, n_recent, 1.0)
+    else:
+        q = W.queries(62, "q_draft", (1, Hq), D)
+        o, lse = lib.draft_step_window(dev_bf16(q), fused, kt, vt, 1.0)
+        ro, rl = OA.draft_window(q[0], K, V, L, n_sink, n_recent, 1.0)
+    lib.ring_append(ref, kt, vt)
+    torch().cuda.synchronize()
+    compare(o[0], lse[0], ro, rl, f"fused step after rollback of {rolled}")
+    _same_ring(fused, ref, "after rollback")

@@ -66,3 +66,56 @@ def test_scale_divides_before_rounding():
     # 1.0 / 0.75 = 1.333..: between 1.25 (0x3A) and 1.375 (0x3B), nearer 1.375
     assert F.quantize_e4m3(np.float32(1.0), np.float32(1.0) / np.float32(0.75)) == 0x3B
     assert F.dequantize_e4m3(np.uint8(0x3B), 0.75) == 1.375 * 0.75
+
+
+@pytest.mark.parametrize("bits,inv,code", [
+    (0x3F80, 1.0, 0x38),          # 1.0
+    (0x3FC0, 1.0, 0x3C),          # 1.5
+    (0xBFC0, 1.0, 0xBC),          # -1.5
+    (0x43E0, 1.0, 0x7E),          # 448, the largest e4m3 value
+    (0x4400, 1.0, 0x7E),          # 512 saturates
+    (0xC400, 1.0, 0xFE),          # -512 saturates
+    (0x8000, 1.0, 0x80),          # -0 keeps its sign
+    (0x0000, 1.0, 0x00),
+    (0x0001, 1.0, 0x00),          # a bf16 subnormal (~9e-41) rounds to zero
+    (0x8001, 1.0, 0x80),          # ... and its negative to -0
+    (0x3F88, 1.0, 0x38),          # 1.0625: halfway 1.0 .. 1.125, the even code
+    (0x3F98, 1.0, 0x3A),          # 1.1875: halfway 1.125 .. 1.25, the even code
+    (0x3B40, 1.0, 0x02),          # 3 * 2^-10: halfway between subnormal codes 1 and 2
+    (0x3B00, 1.0, 0x01),          # 2^-9, the smallest subnormal
+    (0x3A80, 1.0, 0x00),          # 2^-10: halfway 0 .. 2^-9, the even code 0
+    (0x3F80, 1.0 / 0.75, 0x3B),   # 1 / 0.75 = 1.333..: nearest 1.375
+    (0x4040, 0.5, 0x3C),          # 3 * 0.5 = 1.5
+    (0x4396, 2.0, 0x7E),          # 300 * 2 = 600 saturates
+    (0x3C00, 64.0, 0x30),         # 2^-7 * 64 = 0.5
+])
+def test_bf16_bits_to_codes(bits, inv, code):
+    """The stored form of a bf16 K/V value, from its bit pattern: expected codes
+    follow from the two formats' definitions (bf16: 1 sign, 8 exponent bits of bias
+    127, 7 mantissa bits; e4m3 as above)."""
+    got = F.bf16_to_e4m3(np.array([bits], dtype=np.uint16), np.float32(inv))
+    assert got.dtype == np.uint8 and got.shape == (1,)
+    assert int(got[0]) == code
+
+
+def _bf16_value(bits: int) -> float:
+    """bf16 bit pattern -> value, decoded field by field (no float reinterpretation)."""
+    s, e, m = bits >> 15, (bits >> 7) & 0xFF, bits & 0x7F
+    mag = m * 2.0 ** -133 if e == 0 else (1 + m / 128.0) * 2.0 ** (e - 127)
+    return -mag if s else mag
+
+
+def test_bf16_bits_every_finite_pattern():
+    """All 65,280 finite bf16 patterns at once: the codes equal the quantizer applied
+    to values decoded field by field, and each code is a nearest e4m3 value to its
+    input clamped to +-448 (a wrong shift or widening fails this)."""
+    bits = np.array([b for b in range(1 << 16) if ((b >> 7) & 0xFF) != 0xFF], dtype=np.uint16)
+    vals = np.array([_bf16_value(int(b)) for b in bits])
+    codes = F.bf16_to_e4m3(bits)
+    assert np.array_equal(codes, F.quantize_e4m3(vals.astype(np.float32)))
+    back = F.dequantize_e4m3(codes)
+    clamped = np.clip(vals, -448.0, 448.0)
+    table = np.concatenate([-F.e4m3_positive_values(), F.e4m3_positive_values()])
+    nearest = np.min(np.abs(clamped[:, None] - table[None, :]), axis=1)
+    assert np.array_equal(np.abs(back - clamped), nearest)
+    assert np.array_equal(np.signbit(back) | (back == 0), np.signbit(vals) | (back == 0))
