@@ -20,7 +20,9 @@
  * Conventions for every call
  *   - Pointers are device pointers unless marked (host).  The caller allocates
  *     and owns every buffer, including the workspace; the library never
- *     allocates or frees device memory and keeps no state between calls.
+ *     allocates or frees device memory and keeps no state between calls (the
+ *     one exception, wmtp_draft_step_window_static, uses a static scratch
+ *     buffer the library holds on each GPU instead of a workspace).
  *   - bf16 tensors are passed as uint16_t bit patterns.  Every bf16/float
  *     pointer must be 16-byte aligned.
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
@@ -318,6 +320,31 @@ wmtp_status wmtp_draft_step_window(const uint16_t* q, uint16_t* ring_k, uint16_t
                                    int C, int n_sink, int n_recent, float softmax_scale, float* o,
                                    float* lse, void* workspace, size_t workspace_bytes,
                                    int num_splits, void* stream);
+
+/*
+ * wmtp_draft_step_window with no workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops and
+ * harnesses that forbid allocation.  The split partials go to a static scratch
+ * buffer of WMTP_STATIC_SCRATCH_BYTES that the library holds on each GPU it runs
+ * on until the process ends (its address is looked up once per device, on the
+ * first call there).  Arguments, result and ring update as wmtp_draft_step_window;
+ * the stream must belong to the current device (else WMTP_ERR_INVALID_ARG).
+ * Sizes whose partials need more than the scratch
+ * (wmtp_workspace_bytes(WMTP_CALL_RING_STEP, B, Hq, Hkv, D, 1, C, num_splits, 0)
+ * > WMTP_STATIC_SCRATCH_BYTES) return WMTP_ERR_WORKSPACE and launch nothing.
+ * Every call on one GPU shares that GPU's scratch: calls that overlap in time on
+ * one GPU (on different streams, or from several threads without ordering) race
+ * and give undefined results; calls ordered on one stream do not.  Nothing in the
+ * scratch needs to start at zero.
+ */
+#define WMTP_STATIC_SCRATCH_BYTES (16u << 20)
+
+wmtp_status wmtp_draft_step_window_static(const uint16_t* q, uint16_t* ring_k, uint16_t* ring_v,
+                                          int32_t* ring_pos, int64_t* ring_T,
+                                          const uint16_t* k_new, const uint16_t* v_new, int B,
+                                          int n_new, int Hq, int Hkv, int D, int C, int n_sink,
+                                          int n_recent, float softmax_scale, float* o, float* lse,
+                                          int num_splits, void* stream);
 
 /*
  * The draft context pass fused the same way: append n_new positions to each

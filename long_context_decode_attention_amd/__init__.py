@@ -29,7 +29,7 @@ EXPORTS = (
     "wmtp_draft_context_window", "wmtp_verify_attn_tree", "wmtp_paged_append_fp8",
     "wmtp_draft_attn_full_fp8", "wmtp_draft_attn_window_paged_fp8", "wmtp_ring_append",
     "wmtp_paged_append", "wmtp_verify_attn", "wmtp_split_combine", "wmtp_draft_step_window",
-    "wmtp_draft_context_step_window",
+    "wmtp_draft_context_step_window", "wmtp_draft_step_window_static",
 )
 
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration",
@@ -68,6 +68,7 @@ _SIGS = {
     "wmtp_ring_append": ([_P] * 6 + [_I] * 6 + [_P], _I),
     "wmtp_draft_step_window": ([_P] * 7 + [_I] * 8 + [_F, _P, _P, _P, _SZ, _I, _P], _I),
     "wmtp_draft_context_step_window": ([_P] * 7 + [_I] * 9 + [_F, _P, _P, _P, _SZ, _I, _P], _I),
+    "wmtp_draft_step_window_static": ([_P] * 7 + [_I] * 8 + [_F, _P, _P, _I, _P], _I),
     "wmtp_paged_append": ([_P] * 6 + [_I] * 6 + [_P], _I),
     "wmtp_verify_attn": ([_P] * 5 + [_I] * 8 + [_F, _P, _P, _P, _SZ, _I, _U, _P], _I),
     "wmtp_split_combine": ([_P, _P, _I, _P] + [_I] * 6 + [_P, _P, _P], _I),
@@ -503,6 +504,35 @@ def draft_step_window(q, ring: Ring, k_new, v_new, softmax_scale=1.0, o=None, ls
         _ptr(q), _ptr(ring.k), _ptr(ring.v), _ptr(ring.pos), _ptr(ring.T), _ptr(k_new), _ptr(v_new), B, n_new, Hq, Hkv, D, C, ring.n_sink, ring.n_recent,
         float(softmax_scale), _ptr(o), _ptr(lse), _ptr(workspace), workspace.numel(),
         int(num_splits), _stream(stream)), prepare)
+    if prepare:
+        return c
+    return o, lse
+
+
+STATIC_SCRATCH_BYTES = 16 << 20
+
+
+def draft_step_window_static(q, ring: Ring, k_new, v_new, softmax_scale=1.0, o=None, lse=None,
+                             num_splits=0, stream=None, prepare=False):
+    """``draft_step_window`` without a workspace (``wmtp_draft_step_window_static``):
+    the partials go to the library's static scratch on this GPU (at most
+    ``STATIC_SCRATCH_BYTES``); calls overlapping in time on one GPU race."""
+    torch = _torch()
+    B, Hq, D = q.shape
+    n_new = k_new.shape[1]
+    Hkv, C = ring.Hkv, ring.C
+    _need(q, torch.bfloat16, None, "q")
+    _need(ring.k, torch.bfloat16, k_cache_shape(B * C // PAGE, Hkv, D), "ring.k")
+    _need(ring.v, torch.bfloat16, v_cache_shape(B * C // PAGE, Hkv, D), "ring.v")
+    _need(ring.pos, torch.int32, (B, C), "ring.pos")
+    _need(ring.T, torch.int64, (B,), "ring.T")
+    _need(k_new, torch.bfloat16, (B, n_new, Hkv, D), "k_new")
+    _need(v_new, torch.bfloat16, (B, n_new, Hkv, D), "v_new")
+    o, lse = _outputs(o, lse, (B, Hq, D), (B, Hq), q.device)
+    c = _invoke("wmtp_draft_step_window_static", (
+        _ptr(q), _ptr(ring.k), _ptr(ring.v), _ptr(ring.pos), _ptr(ring.T), _ptr(k_new),
+        _ptr(v_new), B, n_new, Hq, Hkv, D, C, ring.n_sink, ring.n_recent, float(softmax_scale),
+        _ptr(o), _ptr(lse), int(num_splits), _stream(stream)), prepare)
     if prepare:
         return c
     return o, lse

@@ -1,15 +1,48 @@
 // C ABI of libwmtp (declared in include/wmtp.h): host-side argument checks,
-// split planning and kernel launches.  Nothing here allocates device memory.
+// split planning and kernel launches.  No call allocates device memory; the one
+// library-owned buffer is the static scratch below, part of the code object.
 #include "wmtp.h"
 
 #include "internal.h"
 
 #include <climits>
 #include <cmath>
+#include <mutex>
 
 using namespace wmtp;
 
 namespace {
+
+// Library-owned scratch for wmtp_draft_step_window_static: the split partials of
+// one fused windowed draft step, for callers that cannot allocate a workspace.
+// One copy per GPU, alive until the process ends.  In host code `scratch` names
+// a host-side stand-in, never the device memory: the device address comes from
+// hipGetSymbolAddress, once per device (static_scratch below).
+__device__ __align__(256) unsigned char scratch[WMTP_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this GPU's scratch (the current device, which must be the
+// stream's): looked up on the first call on a device and kept.
+wmtp_status static_scratch(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return WMTP_ERR_HIP;
+  if (stream) {
+    int sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return WMTP_ERR_HIP;
+    if (sdev != dev) return WMTP_ERR_INVALID_ARG;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return WMTP_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return WMTP_OK;
+}
 
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -356,7 +389,7 @@ static wmtp_status ring_step(const uint16_t* q, uint16_t* ring_k, uint16_t* ring
                              const uint16_t* v_new, int B, int n_new, int n_q, int Hq, int Hkv,
                              int D, int C, int n_sink, int n_recent, float softmax_scale,
                              float* o, float* lse, void* workspace, size_t workspace_bytes,
-                             int num_splits, void* stream) {
+                             int num_splits, void* stream, bool use_static = false) {
   if (!attn_dims_ok(B, Hq, Hkv, D) || n_q < 1) return WMTP_ERR_INVALID_ARG;
   if (!head_dim_ok(D)) return WMTP_ERR_UNSUPPORTED;
   if ((long)n_q * (Hq / Hkv) > 256) return WMTP_ERR_UNSUPPORTED;
@@ -378,6 +411,13 @@ static wmtp_status ring_step(const uint16_t* q, uint16_t* ring_k, uint16_t* ring
     return WMTP_ERR_INVALID_ARG;
   AttnPlan p;
   if (!plan_window_step(B, Hq, Hkv, D, n_q, C, num_splits, &p)) return WMTP_ERR_INVALID_ARG;
+  if (use_static) {
+    // the partials go to this GPU's static scratch; sizes beyond it are refused
+    if (p.ws_bytes > (size_t)WMTP_STATIC_SCRATCH_BYTES) return WMTP_ERR_WORKSPACE;
+    const wmtp_status s = static_scratch(static_cast<hipStream_t>(stream), &workspace);
+    if (s != WMTP_OK) return s;
+    workspace_bytes = WMTP_STATIC_SCRATCH_BYTES;
+  }
   if (!workspace || !aligned16(workspace) || workspace_bytes < p.ws_bytes)
     return WMTP_ERR_WORKSPACE;
   RingAppendArgs app;
@@ -455,6 +495,16 @@ wmtp_status wmtp_draft_step_window(const uint16_t* q, uint16_t* ring_k, uint16_t
   return ring_step(q, ring_k, ring_v, ring_pos, ring_T, k_new, v_new, B, n_new, 1, Hq, Hkv, D, C,
                    n_sink, n_recent, softmax_scale, o, lse, workspace, workspace_bytes,
                    num_splits, stream);
+}
+
+wmtp_status wmtp_draft_step_window_static(const uint16_t* q, uint16_t* ring_k, uint16_t* ring_v,
+                                          int32_t* ring_pos, int64_t* ring_T,
+                                          const uint16_t* k_new, const uint16_t* v_new, int B,
+                                          int n_new, int Hq, int Hkv, int D, int C, int n_sink,
+                                          int n_recent, float softmax_scale, float* o, float* lse,
+                                          int num_splits, void* stream) {
+  return ring_step(q, ring_k, ring_v, ring_pos, ring_T, k_new, v_new, B, n_new, 1, Hq, Hkv, D, C,
+                   n_sink, n_recent, softmax_scale, o, lse, nullptr, 0, num_splits, stream, true);
 }
 
 wmtp_status wmtp_draft_context_step_window(const uint16_t* q, uint16_t* ring_k, uint16_t* ring_v,
