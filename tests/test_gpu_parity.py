@@ -468,6 +468,70 @@ def test_verify_long_splits(cfg_name, S, n_q, num_splits, peak):
           f"max|o err| {err:.2e} (max|o| {float(np.max(np.abs(ro))):.2e}), max|lse err| {lerr:.2e}")
 
 
+def _verify_custom(cfg_name, seed, S, n_q, K, V, q, num_splits):
+    """Verify over caller-built K/V bits (positions 0 .. S + n_q - 1) against the oracle."""
+    lib = _lib()
+    from long_context_decode_attention_amd import scenario as scn
+    cfg = CFG[cfg_name]
+    L = S + n_q
+    kv = scn.alloc_paged_kv([L], cfg["Hkv"], cfg["D"], W.page_permutation(seed, "target_k", (L + 63) // 64))
+    scn.poison(kv.k)
+    scn.poison(kv.v)
+    scn.fill_paged(kv, 0, 0, K, V)
+    o, l = lib.verify_attn(dev_bf16(q), kv.k, kv.v, kv.block_table, dev_i32([L]), L, 1.0,
+                           num_splits=num_splits)
+    torch().cuda.synchronize()
+    ro, rl = OA.verify(q[0], K, V, L, 1.0)
+    return o[0], l[0], ro, rl
+
+
+@pytest.mark.parametrize("cfg_name,S,num_splits", [
+    ("ctx1m_g32x2_d256", 24000, 1),          # 128 rows per kv head, one split of 750 tiles
+    ("nope8l_1m_g64x2_d128", 16000, 1),      # 256 rows per kv head
+])
+def test_verify_long_split_wide_values(cfg_name, S, num_splits):
+    """V x 16 (exact in bf16: an exponent shift): outputs ~16x larger, so the fast
+    tiles' bf16-rounded weights are checked against the relative bound (error at
+    most 1e-2 of the largest output), not only the absolute one."""
+    cfg = CFG[cfg_name]
+    n_q, Hkv, D = 8, cfg["Hkv"], cfg["D"]
+    K = W.kv_positions(91, "target_k", 0, 0, S + n_q, Hkv, D)
+    V = W.bf16_round(16.0 * W.bf16_to_f32(W.kv_positions(91, "target_v", 0, 0, S + n_q, Hkv, D)))
+    q = W.queries(91, "q_verify", (1, n_q, cfg["Hq"]), D)
+    o, l, ro, rl = _verify_custom(cfg_name, 91, S, n_q, K, V, q, num_splits)
+    got = o.double().cpu().numpy().reshape(ro.shape)
+    err = float(np.max(np.abs(got - ro)))
+    scale = float(np.max(np.abs(ro)))
+    lerr = float(np.max(np.abs(l.double().cpu().numpy().reshape(rl.shape) - rl)))
+    print(f"verify wide values {cfg_name}: max|o err| {err:.2e}, max|o| {scale:.2e}, "
+          f"relative {err / scale:.2e}, max|lse err| {lerr:.2e}")
+    assert err <= 1e-2 * scale
+    assert lerr <= 1e-3
+
+
+@pytest.mark.parametrize("cfg_name,S,num_splits", [
+    ("ctx1m_g32x2_d256", 20000, 1),
+    ("nope8l_1m_g64x2_d128", 12000, 2),
+])
+def test_verify_needle_raises_the_maximum_mid_split(cfg_name, S, num_splits):
+    """A key aligned with one query row's query, in the middle of a long split, lifts
+    that row's score far above the running maximum (a raise beyond the lazy margin):
+    the row owner rescales and the other waves' accumulators of that row block
+    follow the published factors."""
+    cfg = CFG[cfg_name]
+    n_q, Hq, Hkv, D = 8, cfg["Hq"], cfg["Hkv"], cfg["D"]
+    K = W.kv_positions(92, "target_k", 0, 0, S + n_q, Hkv, D)
+    V = W.kv_positions(92, "target_v", 0, 0, S + n_q, Hkv, D)
+    q = W.queries(92, "q_verify", (1, n_q, Hq), D)
+    qf = W.bf16_to_f32(q)
+    p = S // 2 + 7
+    for g in range(Hkv):
+        # query 3 of the first head of kv head g: score ~ 8 * sum |q| ~ 100+
+        K[p, g] = W.bf16_round(8.0 * np.sign(qf[0, 3, g * (Hq // Hkv)]))
+    o, l, ro, rl = _verify_custom(cfg_name, 92, S, n_q, K, V, q, num_splits)
+    compare(o, l, ro, rl, f"verify needle {cfg_name}")
+
+
 def _tree_masks(n_q, kind):
     if kind == "binary":      # node i's parent is (i - 1) // 2
         masks = []
