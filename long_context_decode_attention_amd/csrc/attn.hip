@@ -2,14 +2,14 @@
 // the windowed draft (the valid slots of a sink-plus-recent ring) and a verify
 // with at most 32 query rows per kv head share this kernel.
 //
-// Work decomposition.  One workgroup (4 waves) owns one key split of one
+// Work decomposition.  One workgroup (NW = 4 waves) owns one key split of one
 // (sequence b, kv head g) pair and a group of up to 32 * NB query rows of that
-// kv head (the G query heads of the group, times n_q verify queries).  The split
-// is a run of 32-key tiles; wave w of the workgroup takes tiles w, w + 4, ...,
-// so the four waves stream neighbouring memory.  Each wave keeps its own
-// online-softmax state; the four are merged through LDS at the end and the
-// workgroup writes one partial (o, lse) per row, or the final result when the
-// sequence has a single split.
+// kv head (the G query heads of the group, times n_q verify queries).  The
+// split is a run of 32-key tiles; wave w of the workgroup takes tiles w,
+// w + NW, ..., so the four waves stream neighbouring memory.  Each wave keeps
+// its own online-softmax state; the four are merged through LDS at the end and
+// the workgroup writes one partial (o, lse) per row, or the final result when
+// the sequence has a single split.
 //
 // Per tile a wave runs the products of attn_device.h on MFMA 32x32x16.  K and V
 // operands are 16-byte non-temporal loads straight from the tiled page layout
@@ -123,15 +123,21 @@ __device__ __forceinline__ void load_v(VTile<D, KV8>& t, const AttnArgs& a, size
 
 // Fused draft step: K operands of the tile of new positions (key j = position
 // T0 + j of app.k_new, j < n_new; the other keys load key 0 and are marked
-// absent), with the positions the window test reads.
+// absent).  The loads do not depend on T0; new_positions() sets the positions
+// the window test reads once T0 is known.
 template <int D>
 __device__ __forceinline__ void load_k_new(KTile<D, true, false>& t, const AttnArgs& a, int b, int g,
-                                           int T0, int m, int h) {
+                                           int m, int h) {
   const int key = s_row_key(m);
   const int kk = key < a.app.n_new ? key : 0;
   const uint16_t* src = a.app.k_new + (((size_t)b * a.app.n_new + kk) * a.Hkv + g) * D + 8 * h;
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) t.k[ks] = ld_bf16x8(src + 16 * ks);
+}
+
+template <int D>
+__device__ __forceinline__ void new_positions(KTile<D, true, false>& t, const AttnArgs& a, int T0,
+                                              int h) {
 #pragma unroll
   for (int r = 0; r < 2; ++r)
 #pragma unroll
@@ -143,10 +149,10 @@ __device__ __forceinline__ void load_k_new(KTile<D, true, false>& t, const AttnA
 
 // V^T of the new positions, staged in LDS as [D][32 keys] bf16 (keys >= n_new
 // left as they are: the window test marks them absent and PV zeroes them).
-template <int D>
+template <int D, int NT>
 __device__ __forceinline__ void stage_v_new(uint16_t* sm_vt, const AttnArgs& a, int b, int g) {
   const int pieces = a.app.n_new * (D / 8);
-  for (int idx = threadIdx.x; idx < pieces; idx += 256) {
+  for (int idx = threadIdx.x; idx < pieces; idx += NT) {
     const int j = idx / (D / 8);
     const int d0 = (idx - j * (D / 8)) * 8;
     const u32x4 w = *reinterpret_cast<const u32x4*>(
@@ -199,12 +205,27 @@ __device__ __forceinline__ uint32_t present_keys(const KTile<D, RING, KV8>& t, c
 template <int D, int NB, bool RING, bool KV8, bool STEP = false>
 __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
   static_assert(!STEP || (RING && !KV8 && NB == 1), "the fused step reads a bf16 ring");
+  constexpr int NW = 4;         // waves
+  constexpr int NT = 64 * NW;   // threads
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int m = lane & 31;   // MFMA row / column of this lane
   const int h = lane >> 5;   // lane group
+
+  // The arguments the prologue reads are fetched in one round trip: held in
+  // registers here, they no longer wait one after another behind the branches
+  // that use them.
+  asm volatile("" ::"s"(a.nrg), "s"(a.items), "s"(a.nsplit), "s"(a.Hkv), "s"(a.kb_per_split),
+               "s"(a.q), "s"(a.kc), "s"(a.vc), "s"(a.Hq), "s"(a.G), "s"(a.n_q), "s"(a.R),
+               "s"(a.num_pages));
+  if constexpr (RING) {
+    asm volatile("" ::"s"(a.ring_pos), "s"(a.ring_T), "s"(a.C));
+  } else {
+    asm volatile("" ::"s"(a.block_table), "s"(a.seq_lens), "s"(a.max_pages), "s"(a.max_keys),
+                 "s"(a.win));
+  }
 
   // Workgroup -> (item, row group).  With several row groups, the workgroups of
   // one item are spaced 8 apart in launch order so that they land on the same
@@ -241,50 +262,45 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
   // the four waves' O^T chunks for the final merge (fused step: first the V^T
   // staging of the new positions, which is consumed before the merge starts)
   constexpr int U = DB * 4;
-  __shared__ f32x4 sm_acc[4][U][64];
+  __shared__ f32x4 sm_acc[NW][U][64];
   static_assert(sizeof(sm_acc) >= D * 32 * sizeof(uint16_t), "V^T staging fits the merge buffer");
-  constexpr int kQPer = NB * KS * 64 / 256;   // Q operands per thread
-  static_assert(kQPer * 256 == NB * KS * 64, "Q operands split evenly over the threads");
+  constexpr int kQPer = NB * KS * 64 / NT;   // Q operands per thread
+  static_assert(kQPer * NT == NB * KS * 64, "Q operands split evenly over the threads");
   // The sequence length and the wave's first page id are read first: the tile
-  // loads depend on them.
+  // loads depend on them.  The tiles of a ring do not depend on its position
+  // count, which is read after they are issued (except by the workgroup of a
+  // fused step's new positions, whose positions are counted from it).
   const int len_raw = RING ? 0 : a.seq_lens[b];
-  const int64_t t64 = RING ? a.ring_T[b] : 0;
+  const int64_t t_raw = RING ? a.ring_T[b] : 0;   // issued here, waited for below
   const int kb_first = s * a.kb_per_split + wave;
   const int page_first =
       RING ? 0 : a.block_table[(size_t)b * a.max_pages + min(kb_first >> 1, a.max_pages - 1)];
   bf16x8 qv[kQPer];
-  bool qok[kQPer];
 #pragma unroll
   for (int r = 0; r < kQPer; ++r) {
-    const int idx = threadIdx.x + 256 * r;
+    const int idx = threadIdx.x + NT * r;
     const int ln = idx & 63;
     const int ks = (idx >> 6) % KS;
     const int rb = idx / (64 * KS);
     const int row = row0 + rb * 32 + (ln & 31);
-    qok[r] = row < a.R;
-    const int rr = qok[r] ? row : 0;   // rows past R load row 0, then read as zero
+    // rows past R repeat row 0: their results are never written
+    const int rr = row < a.R ? row : 0;
     const int qi = rr / a.G;
     const int hl = rr - qi * a.G;
     qv[r] = ld_bf16x8(a.q + ((size_t)(b * a.n_q + qi) * a.Hq + g * a.G + hl) * D + ks * 16 +
                       (ln >> 5) * 8);
   }
-  int L, T = 0, T0 = 0;
-  if (RING) {
-    L = a.C;
-    const int64_t t_max = STEP ? INT_MAX - 64 : INT_MAX;   // step: room for the new positions
-    T = t64 < 0 ? 0 : (t64 > t_max ? (int)t_max : (int)t64);
-    // fused step: the window ends after the new positions; the slots they will
-    // overwrite hold positions outside it, so the window test skips them, and
-    // slots holding positions >= T0 (left by a rollback) are skipped by p_end
-    T0 = T;
-    if (STEP) T += a.app.n_new;
-  } else {
-    L = len_raw < 0 ? 0 : (len_raw > a.max_keys ? a.max_keys : len_raw);
-  }
+  // ring: the position count, clamped (step: room for the new positions).  The
+  // empty asm is its first use: the wait for the load goes there, after the
+  // tile loads issued before it, and not before them.
+  auto ring_count = [&]() {
+    int64_t t64 = t_raw;
+    asm volatile("" : "+v"(t64));
+    const int64_t t_max = STEP ? INT_MAX - 64 : INT_MAX;
+    return t64 < 0 ? 0 : (t64 > t_max ? (int)t_max : (int)t64);
+  };
+  const int L = RING ? a.C : (len_raw < 0 ? 0 : (len_raw > a.max_keys ? a.max_keys : len_raw));
   const int nkb = (L + 31) >> 5;
-  // ring: the positions a tile may contribute (fused step: the ring splits stop
-  // at the count before the append; the new positions' workgroup reads T0 .. T - 1)
-  const int p_end = (STEP && !newk) ? T0 : T;
   // Truncated paged index (win): the key set [0, sink_end) u [r0, L) as virtual
   // tiles, the sink tiles [0, st_end) then the recent tiles from kr on; phys()
   // maps a virtual tile to its 32-key tile of the sequence.
@@ -309,9 +325,25 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
   VTile<D, KV8> vt;
   int kb = kb0 + wave;
   bool ok = false;
+  int T0 = 0;
+  // Store the loaded Q operands and publish them: the barrier waits for this
+  // wave's LDS stores only, so the tile loads stay in flight across it.  Each
+  // path below stages Q itself, after its own tile loads: with one shared copy
+  // after the paths join, the wait for the Q loads would be counted as if
+  // either path's loads might be the newer ones, and the ring splits would
+  // wait for their whole first tile before staging Q.
+  auto stage_q = [&]() {
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int r = 0; r < kQPer; ++r) {
+      const int idx = threadIdx.x + NT * r;
+      sm_q[idx / (64 * KS)][(idx >> 6) % KS][idx & 63] = qv[r];
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
   {
     // unconditional (a wave without tiles loads a valid tile it never uses), so
-    // that the Q stores below wait only for the Q loads
+    // that the Q stores wait only for the Q loads
     const int kbl = kb < kb1 ? kb : 0;
     size_t tile;
     if (newk) {
@@ -323,32 +355,31 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
     } else {
       tile = tile_of_page(a, kb < kb1 ? page_first : 0, g, kbl, ok);
     }
-    if constexpr (STEP) {
-      if (newk) {
-        load_k_new<D>(kt, a, b, g, T0, m, h);
+    if (STEP && newk) {
+      if constexpr (STEP) {
+        load_k_new<D>(kt, a, b, g, m, h);
         ok = true;
-        stage_v_new<D>(reinterpret_cast<uint16_t*>(&sm_acc[0][0][0]), a, b, g);
-      } else {
-        load_k<D, RING, KV8>(kt, a, tile, b, kbl, m, h);
-        load_v<D, KV8>(vt, a, tile, m, h);
+        stage_v_new<D, NT>(reinterpret_cast<uint16_t*>(&sm_acc[0][0][0]), a, b, g);
+        stage_q();
+        load_v_new<D>(vt, reinterpret_cast<const uint16_t*>(&sm_acc[0][0][0]), m, h);
+        T0 = ring_count();
+        new_positions<D>(kt, a, T0, h);
       }
     } else {
       load_k<D, RING, KV8>(kt, a, tile, b, kbl, m, h);
       load_v<D, KV8>(vt, a, tile, m, h);
+      asm volatile("" ::: "memory");
+      if (RING) T0 = ring_count();
+      stage_q();
     }
   }
-  asm volatile("" ::: "memory");
-#pragma unroll
-  for (int r = 0; r < kQPer; ++r) {
-    const int idx = threadIdx.x + 256 * r;
-    sm_q[idx / (64 * KS)][(idx >> 6) % KS][idx & 63] = qok[r] ? qv[r] : zero_bf16x8();
-  }
-  // publish the staged Q: wait for this wave's LDS stores only, so the tile
-  // loads stay in flight across the barrier
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  if constexpr (STEP) {
-    if (newk) load_v_new<D>(vt, reinterpret_cast<const uint16_t*>(&sm_acc[0][0][0]), m, h);
-  }
+  // Ring: the window ends at T.  Fused step: T counts the new positions too; the
+  // slots they will overwrite hold positions outside the window, so the window
+  // test skips them, and p_end stops the ring splits at the count before the
+  // append (slots holding positions >= T0, left by a rollback, are skipped; the
+  // new positions' workgroup reads T0 .. T - 1).
+  const int T = RING ? (STEP ? T0 + a.app.n_new : T0) : 0;
+  const int p_end = (STEP && !newk) ? T0 : T;
   int lim[NB];
 #pragma unroll
   for (int rb = 0; rb < NB; ++rb) {
@@ -384,7 +415,7 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
   uint32_t keep = 0;
   bool mask_v = false;
   auto next_tile = [&]() {
-    kbn = kb + 4;
+    kbn = kb + NW;
     tile_n = tile_index<RING>(a, b, g, phys(kbn), ok_n);
   };
   auto advance = [&]() {
@@ -483,7 +514,7 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
   // Fast loop over the tiles that have a successor: no accumulator rescale.  It
   // leaves early when tile kb needs one; its scores are then already in x / mx.
   bool general = false;
-  while (kb + 4 < kb1) {
+  while (kb + NW < kb1) {
     next_tile();
     scores_of(more);
     if (first_max_or_rescale<D, NB>(st, mx)) {
@@ -498,7 +529,7 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
     raise_and_rescale<D, NB>(st, mx);
     finish(more);
     advance();
-    while (kb + 4 < kb1) {
+    while (kb + NW < kb1) {
       next_tile();
       scores_of(more);
       raise_and_rescale<D, NB>(st, mx);
@@ -517,8 +548,8 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
   // Every wave stores its rescaled O^T chunks (chunk u = 4*db + c: dims
   // 32*db + 8*c + 4*h .. +3 of row m), then wave w sums and writes chunks
   // [w*U/4, (w+1)*U/4) of all four waves.
-  __shared__ float sm_m[4][32];
-  __shared__ float sm_l[4][32];
+  __shared__ float sm_m[NW][32];
+  __shared__ float sm_l[NW][32];
 
 #pragma unroll
   for (int rb = 0; rb < NB; ++rb) {
@@ -531,11 +562,11 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
     __syncthreads();
     float M = sm_m[0][m];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) M = fmaxf(M, sm_m[w][m]);
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, sm_m[w][m]);
     const float Mu = (M == -INFINITY) ? 0.f : M;
     float Ltot = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) Ltot += sm_l[w][m] * fast_exp2(sm_m[w][m] - Mu);
+    for (int w = 0; w < NW; ++w) Ltot += sm_l[w][m] * fast_exp2(sm_m[w][m] - Mu);
     const float f = fast_exp2(st.m[rb] - Mu);
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -562,10 +593,11 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
         lp = a.out_lse + (size_t)item * a.R + row;
       }
 #pragma unroll
-      for (int j = 0; j < U / 4; ++j) {
-        const int u = wave * (U / 4) + j;
-        const f32x4 v = sm_acc[0][u][lane] + sm_acc[1][u][lane] + sm_acc[2][u][lane] +
-                        sm_acc[3][u][lane];
+      for (int j = 0; j < U / NW; ++j) {
+        const int u = wave * (U / NW) + j;
+        f32x4 v = sm_acc[0][u][lane];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) v += sm_acc[w][u][lane];
         *reinterpret_cast<f32x4*>(op + (u >> 2) * 32 + 8 * (u & 3) + 4 * h) = v * inv;
       }
       if (wave == 0 && h == 0 && lp) *lp = Ltot > 0.f ? (M + fast_log2(Ltot)) * kLn2 : -INFINITY;
@@ -613,7 +645,10 @@ bool plan_window_step(int B, int Hq, int Hkv, int D, int n_q, int C, int num_spl
   p->nrg = (p->R + 31) / 32;
   p->nkb = C / 32;
   // default: the windowed draft's plan (one workgroup per CU, at least four
-  // tiles, one per wave, per split)
+  // tiles, one per wave, per split).  Measured at 2 x 128 tiles, D = 256: four
+  // waves of one tile each in 64 workgroups take 12.7 us a step against 13.8 us
+  // for 256 one-wave workgroups, whose four times as many partials the merge
+  // launch then reads.
   int kbps;
   if (num_splits > 0) {
     kbps = (p->nkb + num_splits - 1) / num_splits;

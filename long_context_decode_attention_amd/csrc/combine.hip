@@ -10,9 +10,10 @@
 //    partial row per load) and the split lanes in different waves, summed
 //    through LDS; CL is the widest that still gives about 512 workgroups.  The
 //    partials of a many-row verify are tens of MB: coalescing decides there.
-// Either way split lane sl visits splits sl, sl + SL, ... with eight independent
-// 16-byte loads in flight, and the sums run in a fixed order, so the result
-// does not depend on timing.
+// Either way split lane sl visits splits sl, sl + SL, ... in one pass, with
+// eight independent (o_s, lse_s) loads in flight and a running maximum (one
+// memory round trip when a lane has at most eight splits), and the sums run in
+// a fixed order, so the result does not depend on timing.
 #include "common.h"
 #include "internal.h"
 #include "ring_device.h"
@@ -26,6 +27,55 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr int kUnroll = 8;
+
+// One split lane's share of the merge, in a single pass over its splits
+// p0 + sl, p0 + sl + SL, ... < p1: kUnroll (o_s, lse_s) pairs are loaded at a
+// time, all independent of one another, and folded into a running maximum m
+// and sums acc = sum_s exp(lse_s - m) * o_s, wsum = sum_s exp(lse_s - m),
+// rescaled when m rises.  The lanes' states are then brought to the common
+// maximum by the caller.
+struct LaneMerge {
+  f32x4 acc;
+  float wsum;
+  float m;   // log2 units; -inf while the lane has seen no key
+};
+
+__device__ __forceinline__ LaneMerge merge_lane(const float* base, const float* lse, size_t stride,
+                                                int R, int row, int p0, int p1, int sl, int SL) {
+  LaneMerge s = {f32x4{0.f, 0.f, 0.f, 0.f}, 0.f, -INFINITY};
+  for (int p = p0 + sl; p < p1; p += SL * kUnroll) {
+    f32x4 v[kUnroll];
+    float l[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int q = p + u * SL;
+      if (q < p1) {
+        v[u] = *reinterpret_cast<const f32x4*>(base + (size_t)q * stride);
+        l[u] = lse[(size_t)q * R + row] * kLog2e;
+      } else {
+        v[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        l[u] = -INFINITY;
+      }
+    }
+    float bm = l[0];
+#pragma unroll
+    for (int u = 1; u < kUnroll; ++u) bm = fmaxf(bm, l[u]);
+    if (bm == -INFINITY) continue;   // no keys in this batch
+    if (bm > s.m) {
+      const float f = s.m == -INFINITY ? 0.f : fast_exp2(s.m - bm);
+      s.acc *= f;
+      s.wsum *= f;
+      s.m = bm;
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const float w = l[u] == -INFINITY ? 0.f : fast_exp2(l[u] - s.m);
+      s.acc += v[u] * w;
+      s.wsum += w;
+    }
+  }
+  return s;
+}
 
 template <int SL>
 __device__ __forceinline__ float max_over_split_lanes(float v) {
@@ -74,40 +124,18 @@ __global__ __launch_bounds__(256) void combine_wide_kernel(CombineArgs c, int CL
   __shared__ f32x4 sm_acc[256];
   __shared__ float sm_w[256];
 
-  float mx = -INFINITY;
-  for (int p = p0 + t; p < p1; p += 256) mx = fmaxf(mx, c.part_lse[(size_t)p * c.R + row]);
+  LaneMerge st = merge_lane(c.part_o + (size_t)row * c.D + col, c.part_lse, (size_t)c.R * c.D,
+                            c.R, row, p0, p1, sl, SL);
+  // the row's maximum M over all the threads, then each thread's state brought to it
+  float mx = st.m;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
   if ((t & 63) == 0) red[t >> 6] = mx;
   __syncthreads();
   const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float Mu = (M == -INFINITY) ? 0.f : M;
-
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float wsum = 0.f;
-  const size_t stride = (size_t)c.R * c.D;
-  const float* base = c.part_o + (size_t)row * c.D + col;
-  for (int p = p0 + sl; p < p1; p += SL * kUnroll) {
-    f32x4 v[kUnroll];
-    float w[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int q = p + u * SL;
-      if (q < p1) {
-        v[u] = *reinterpret_cast<const f32x4*>(base + (size_t)q * stride);
-        const float l = c.part_lse[(size_t)q * c.R + row];
-        w[u] = (l == -INFINITY) ? 0.f : fast_exp2((l - Mu) * kLog2e);
-      } else {
-        v[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-        w[u] = 0.f;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      acc += v[u] * w[u];
-      wsum += w[u];
-    }
-  }
+  const float f = st.m == -INFINITY ? 0.f : fast_exp2(st.m - M);
+  const f32x4 acc = st.acc * f;
+  const float wsum = st.wsum * f;
   sm_acc[t] = acc;
   sm_w[t] = wsum;
   __syncthreads();
@@ -125,7 +153,7 @@ __global__ __launch_bounds__(256) void combine_wide_kernel(CombineArgs c, int CL
     const size_t oidx = (size_t)(b * c.n_q + qi) * (c.Hkv * c.G) + g * c.G + hl;
     const float inv = wt > 0.f ? 1.f / wt : 0.f;
     *reinterpret_cast<f32x4*>(c.o + oidx * c.D + col) = tot * inv;
-    if (chunk == 0 && cl == 0 && c.lse) c.lse[oidx] = wt > 0.f ? M + fast_log2(wt) * kLn2 : -INFINITY;
+    if (chunk == 0 && cl == 0 && c.lse) c.lse[oidx] = wt > 0.f ? (M + fast_log2(wt)) * kLn2 : -INFINITY;
   }
 }
 
@@ -159,38 +187,13 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs c) {
   }
   const int col = (blk * CL + cl) * 4;
 
-  // pass 1: the largest split lse of this row
-  float mx = -INFINITY;
-  for (int p = p0 + sl; p < p1; p += SL) mx = fmaxf(mx, c.part_lse[(size_t)p * c.R + row]);
-  const float M = max_over_split_lanes<SL>(mx);
-  const float Mu = (M == -INFINITY) ? 0.f : M;
-
-  // pass 2: this lane's share of sum_s w_s * o_s and sum_s w_s
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float wsum = 0.f;
-  const size_t stride = (size_t)c.R * c.D;
-  const float* base = c.part_o + (size_t)row * c.D + col;
-  for (int p = p0 + sl; p < p1; p += SL * kUnroll) {
-    f32x4 v[kUnroll];
-    float w[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int q = p + u * SL;
-      if (q < p1) {
-        v[u] = *reinterpret_cast<const f32x4*>(base + (size_t)q * stride);
-        const float l = c.part_lse[(size_t)q * c.R + row];
-        w[u] = (l == -INFINITY) ? 0.f : fast_exp2((l - Mu) * kLog2e);
-      } else {
-        v[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-        w[u] = 0.f;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      acc += v[u] * w[u];
-      wsum += w[u];
-    }
-  }
+  LaneMerge st = merge_lane(c.part_o + (size_t)row * c.D + col, c.part_lse, (size_t)c.R * c.D,
+                            c.R, row, p0, p1, sl, SL);
+  // bring the lanes to the row's maximum M, then sum them
+  const float M = max_over_split_lanes<SL>(st.m);
+  const float f = st.m == -INFINITY ? 0.f : fast_exp2(st.m - M);
+  f32x4 acc = st.acc * f;
+  float wsum = st.wsum * f;
   acc.x = sum_over_split_lanes<SL>(acc.x);
   acc.y = sum_over_split_lanes<SL>(acc.y);
   acc.z = sum_over_split_lanes<SL>(acc.z);
@@ -204,7 +207,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs c) {
     const size_t oidx = (size_t)(b * c.n_q + qi) * (c.Hkv * c.G) + g * c.G + hl;
     const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
     *reinterpret_cast<f32x4*>(c.o + oidx * c.D + col) = acc * inv;
-    if (col == 0 && c.lse) c.lse[oidx] = wsum > 0.f ? M + fast_log2(wsum) * kLn2 : -INFINITY;
+    if (col == 0 && c.lse) c.lse[oidx] = wsum > 0.f ? (M + fast_log2(wsum)) * kLn2 : -INFINITY;
   }
 }
 

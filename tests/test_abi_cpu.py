@@ -246,6 +246,10 @@ def test_fused_step_argument_checks_and_plan():
     assert step(ws=FAKE, wsb=need - 1) == WORKSPACE
     n = lib_mod.step_splits(1, 32, 2, 256, 4096)
     assert n == lib_mod.plan_splits(1, 32, 2, 256, 1, 4096, ring=True)
+    # 2 groups x 128 tiles: the four-tile minimum per split
+    assert n == 32
+    # 32 groups: 8 workgroups per group, 16 tiles per split
+    assert lib_mod.step_splits(8, 32, 4, 128, 4096) == 8
     parts = 2 * (n + 1)
     assert need == (parts * 16 * 256 * 4 + 255) // 256 * 256 + parts * 16 * 4
     assert lib_mod.step_splits(1, 32, 2, 256, 4096, 1) == 1
