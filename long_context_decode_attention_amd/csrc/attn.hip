@@ -147,8 +147,12 @@ __device__ __forceinline__ void new_positions(KTile<D, true, false>& t, const At
     }
 }
 
-// V^T of the new positions, staged in LDS as [D][32 keys] bf16 (keys >= n_new
-// left as they are: the window test marks them absent and PV zeroes them).
+// V^T of the new positions, staged in LDS as [D][kVtRow] bf16, keys 0..31 of a
+// row first (keys >= n_new left as they are: the window test marks them absent
+// and PV zeroes them).  Rows are padded from 32 to 40 keys (80 bytes): the 16
+// lanes of a 16-byte read then start 20 banks apart and hit distinct banks,
+// where 64-byte rows would put eight lanes on the same ones.
+constexpr int kVtRow = 40;
 template <int D, int NT>
 __device__ __forceinline__ void stage_v_new(uint16_t* sm_vt, const AttnArgs& a, int b, int g) {
   const int pieces = a.app.n_new * (D / 8);
@@ -159,8 +163,8 @@ __device__ __forceinline__ void stage_v_new(uint16_t* sm_vt, const AttnArgs& a, 
         a.app.v_new + (((size_t)b * a.app.n_new + j) * a.Hkv + g) * D + d0);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      sm_vt[(d0 + 2 * e) * 32 + j] = (uint16_t)(w[e] & 0xFFFFu);
-      sm_vt[(d0 + 2 * e + 1) * 32 + j] = (uint16_t)(w[e] >> 16);
+      sm_vt[(d0 + 2 * e) * kVtRow + j] = (uint16_t)(w[e] & 0xFFFFu);
+      sm_vt[(d0 + 2 * e + 1) * kVtRow + j] = (uint16_t)(w[e] >> 16);
     }
   }
 }
@@ -171,7 +175,8 @@ __device__ __forceinline__ void load_v_new(VTile<D, false>& t, const uint16_t* s
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
-      t.v[db][kk] = *reinterpret_cast<const bf16x8*>(sm_vt + (32 * db + m) * 32 + 16 * kk + 8 * h);
+      t.v[db][kk] =
+          *reinterpret_cast<const bf16x8*>(sm_vt + (32 * db + m) * kVtRow + 16 * kk + 8 * h);
 }
 
 // Which of this lane's 16 keys exist for every row: inside the sequence length
@@ -186,12 +191,14 @@ __device__ __forceinline__ uint32_t present_keys(const KTile<D, RING, KV8>& t, c
                                                  int sink_end, int r0) {
   if constexpr (RING) {
     uint32_t keep = 0;
+    // in the window of some query: the last n_q positions T - n_q .. T - 1 each
+    // see the sink and their own last n_recent positions (bitwise tests: no
+    // branches; p_end >= 0, so the unsigned compare is 0 <= p < p_end)
+    const int lo = T - (a.n_q - 1) - a.n_recent;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int p = t.pos[i];
-      // in the window of some query: the last n_q positions T - n_q .. T - 1 each
-      // see the sink and their own last n_recent positions
-      const bool ok = p >= 0 && p < p_end && (p < a.n_sink || p >= T - (a.n_q - 1) - a.n_recent);
+      const bool ok = ((unsigned)p < (unsigned)p_end) & ((p < a.n_sink) | (p >= lo));
       keep |= (ok ? 1u : 0u) << i;
     }
     return keep;
@@ -263,7 +270,7 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
   // staging of the new positions, which is consumed before the merge starts)
   constexpr int U = DB * 4;
   __shared__ f32x4 sm_acc[NW][U][64];
-  static_assert(sizeof(sm_acc) >= D * 32 * sizeof(uint16_t), "V^T staging fits the merge buffer");
+  static_assert(sizeof(sm_acc) >= D * kVtRow * sizeof(uint16_t), "V^T staging fits the merge buffer");
   constexpr int kQPer = NB * KS * 64 / NT;   // Q operands per thread
   static_assert(kQPer * NT == NB * KS * 64, "Q operands split evenly over the threads");
   // The sequence length and the wave's first page id are read first: the tile
@@ -398,14 +405,21 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
     tmask[rb] = (!RING && a.tree_mask && row < a.R) ? a.tree_mask[(size_t)b * a.n_q + row / a.G] : 0;
   }
 
+  // The accumulators are set to zero right before a wave's first PV (or at
+  // the end, for a wave without tiles), so that the products start from the
+  // constant instead of a zeroed register block.
   SoftmaxState<D, NB> st;
+  auto zero_acc = [&]() {
+#pragma unroll
+    for (int rb = 0; rb < NB; ++rb)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) st.acc[rb][db] = f32x16{};
+  };
 #pragma unroll
   for (int rb = 0; rb < NB; ++rb) {
     st.m[rb] = -INFINITY;
     st.l[rb] = 0.f;
     st.l_drop[rb] = 0.f;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) st.acc[rb][db] = f32x16{};
   }
 
   int kbn = kb;
@@ -440,7 +454,7 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int p = kt.pos[i];
-            v |= (p <= pq && (p < a.n_sink || p > pq - a.n_recent) ? 1u : 0u) << i;
+            v |= ((p <= pq) & ((p < a.n_sink) | (p > pq - a.n_recent)) ? 1u : 0u) << i;
           }
           rvis[rb] &= v;
         }
@@ -461,6 +475,25 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
         sacc[rb] = mfma32x32x16(as_operand(kt.k[ks]), sm_q[rb][ks][lane], sacc[rb]);
+      // A wave's last tile, bf16 K: keep four Q reads from LDS in flight ahead
+      // of the products (left to itself, the scheduler serialises them at
+      // D = 256, where the registers are short: one LDS round trip per
+      // product).  That tile's products are on the wave's critical path; the
+      // others overlap the next tile's loads, and there the constraint costs
+      // more than it saves (native draft at 1M keys: 84 % of peak HBM
+      // bandwidth without it, 82 % with it).  fp8 K converts each operand
+      // first, which spaces the reads out already, and at D = 128 the extra
+      // registers would cost it its second workgroup per CU.
+      if constexpr (!KV8 && !decltype(has_next)::value) {
+        constexpr int QD = KS < 4 ? KS : 4;
+        __builtin_amdgcn_sched_group_barrier(0x100, QD, 0);   // LDS reads
+#pragma unroll
+        for (int ks = 0; ks < KS - QD; ++ks) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, QD, 0);
+      }
     }
     if constexpr (decltype(has_next)::value) load_k<D, RING, KV8>(kt, a, tile_n, b, kbn, m, h);
 #pragma unroll
@@ -511,34 +544,50 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
   const std::true_type more;
   const std::false_type last;
 
-  // Fast loop over the tiles that have a successor: no accumulator rescale.  It
-  // leaves early when tile kb needs one; its scores are then already in x / mx.
-  bool general = false;
-  while (kb + NW < kb1) {
+  // A wave's first tile takes the rows' first maxima (no row has one yet, so
+  // nothing is rescaled) and starts the accumulators.
+  if (kb >= kb1) {
+    zero_acc();   // no tiles
+  } else if (kb + NW >= kb1) {
+    scores_of(last);   // the only tile
+    first_max_or_rescale<D, NB>(st, mx);
+    zero_acc();
+    finish(last);
+  } else {
     next_tile();
     scores_of(more);
-    if (first_max_or_rescale<D, NB>(st, mx)) {
-      general = true;
-      break;
-    }
+    first_max_or_rescale<D, NB>(st, mx);
+    zero_acc();
     finish(more);
     advance();
-  }
-  // General loop, from the tile the fast loop left on.
-  if (general) {
-    raise_and_rescale<D, NB>(st, mx);
-    finish(more);
-    advance();
+    // Fast loop over the tiles that have a successor: no accumulator rescale.
+    // It leaves early when tile kb needs one; its scores are then already in
+    // x / mx.
+    bool general = false;
     while (kb + NW < kb1) {
       next_tile();
       scores_of(more);
-      raise_and_rescale<D, NB>(st, mx);
+      if (first_max_or_rescale<D, NB>(st, mx)) {
+        general = true;
+        break;
+      }
       finish(more);
       advance();
     }
-  }
-  // The wave's last tile.
-  if (kb < kb1) {
+    // General loop, from the tile the fast loop left on.
+    if (general) {
+      raise_and_rescale<D, NB>(st, mx);
+      finish(more);
+      advance();
+      while (kb + NW < kb1) {
+        next_tile();
+        scores_of(more);
+        raise_and_rescale<D, NB>(st, mx);
+        finish(more);
+        advance();
+      }
+    }
+    // The wave's last tile.
     scores_of(last);
     if (general || first_max_or_rescale<D, NB>(st, mx)) raise_and_rescale<D, NB>(st, mx);
     finish(last);
@@ -547,9 +596,16 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
   // ---- merge the four waves' states through LDS, one row block at a time ----
   // Every wave stores its rescaled O^T chunks (chunk u = 4*db + c: dims
   // 32*db + 8*c + 4*h .. +3 of row m), then wave w sums and writes chunks
-  // [w*U/4, (w+1)*U/4) of all four waves.
+  // [w*U/4, (w+1)*U/4) of all four waves.  When the row group holds at most 16
+  // query rows, lanes m >= 16 carry no results: a swap of 16-lane rows then
+  // packs two chunks into one register (lanes 16..31 and 48..63 take the next
+  // chunk of rows m - 16), which halves the LDS traffic and the stores.
   __shared__ float sm_m[NW][32];
   __shared__ float sm_l[NW][32];
+  const bool pack = NB == 1 && a.R - row0 <= 16;   // uniform
+  // the query row this lane writes, and which chunk of a packed pair it carries
+  const int orow = pack ? (lane & 15) : m;
+  const int half = pack ? (lane >> 4) & 1 : 0;
 
 #pragma unroll
   for (int rb = 0; rb < NB; ++rb) {
@@ -560,24 +616,45 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
       sm_l[wave][m] = lsum;
     }
     __syncthreads();
-    float M = sm_m[0][m];
+    // this lane's own row m: the factor that brings its state to the row maximum
+    float Mo = sm_m[0][m];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) M = fmaxf(M, sm_m[w][m]);
+    for (int w = 1; w < NW; ++w) Mo = fmaxf(Mo, sm_m[w][m]);
+    const float f = fast_exp2(st.m[rb] - ((Mo == -INFINITY) ? 0.f : Mo));
+    // the row it writes: maximum and total weight
+    float M = sm_m[0][orow];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, sm_m[w][orow]);
     const float Mu = (M == -INFINITY) ? 0.f : M;
     float Ltot = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) Ltot += sm_l[w][m] * fast_exp2(sm_m[w][m] - Mu);
-    const float f = fast_exp2(st.m[rb] - Mu);
+    for (int w = 0; w < NW; ++w) Ltot += sm_l[w][orow] * fast_exp2(sm_m[w][orow] - Mu);
+    auto chunk = [&](int u) {
+      const int db = u >> 2, c = u & 3;
+      const f32x4 v = {st.acc[rb][db][4 * c], st.acc[rb][db][4 * c + 1],
+                       st.acc[rb][db][4 * c + 2], st.acc[rb][db][4 * c + 3]};
+      return v * f;
+    };
+    if (pack) {
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+      for (int v = 0; v < U / 2; ++v) {
+        f32x4 x = chunk(2 * v);
+        const f32x4 y = chunk(2 * v + 1);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const f32x4 v = {st.acc[rb][db][4 * c], st.acc[rb][db][4 * c + 1],
-                         st.acc[rb][db][4 * c + 2], st.acc[rb][db][4 * c + 3]};
-        sm_acc[wave][4 * db + c][lane] = v * f;
+        for (int e = 0; e < 4; ++e) {
+          // 16-lane rows 1 and 3 of x (lanes 16..31, 48..63) take rows 0 and 2 of y
+          const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x[e]),
+                                                          __float_as_uint(y[e]), false, false);
+          x[e] = __uint_as_float(r[0]);
+        }
+        sm_acc[wave][v][lane] = x;
       }
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) sm_acc[wave][u][lane] = chunk(u);
+    }
     __syncthreads();
-    const int row = row0 + rb * 32 + m;
+    const int row = row0 + rb * 32 + orow;
     if (row < a.R) {
       const float inv = (Ltot > 0.f ? 1.f / Ltot : 0.f) * (KV8 ? a.v_scale : 1.f);
       float* op;
@@ -592,15 +669,25 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
         op = a.out_o + ((size_t)item * a.R + row) * D;
         lp = a.out_lse + (size_t)item * a.R + row;
       }
+      // this wave's share of the stored entries: n from j0 on; entry j holds
+      // chunk 2 j + half (packed) or chunk j
+      auto write = [&](int j0, int n) {
 #pragma unroll
-      for (int j = 0; j < U / NW; ++j) {
-        const int u = wave * (U / NW) + j;
-        f32x4 v = sm_acc[0][u][lane];
+        for (int j = 0; j < n; ++j) {
+          const int jj = j0 + j;
+          f32x4 v = sm_acc[0][jj][lane];
 #pragma unroll
-        for (int w = 1; w < NW; ++w) v += sm_acc[w][u][lane];
-        *reinterpret_cast<f32x4*>(op + (u >> 2) * 32 + 8 * (u & 3) + 4 * h) = v * inv;
-      }
-      if (wave == 0 && h == 0 && lp) *lp = Ltot > 0.f ? (M + fast_log2(Ltot)) * kLn2 : -INFINITY;
+          for (int w = 1; w < NW; ++w) v += sm_acc[w][jj][lane];
+          const int u = pack ? 2 * jj + half : jj;
+          *reinterpret_cast<f32x4*>(op + (u >> 2) * 32 + 8 * (u & 3) + 4 * h) = v * inv;
+        }
+      };
+      if (pack)
+        write(wave * (U / 2 / NW), U / 2 / NW);
+      else
+        write(wave * (U / NW), U / NW);
+      if (wave == 0 && lane < (pack ? 16 : 32) && lp)
+        *lp = Ltot > 0.f ? (M + fast_log2(Ltot)) * kLn2 : -INFINITY;
     }
   }
 }

@@ -16,6 +16,7 @@
 // a fixed order, so the result does not depend on timing.
 #include "common.h"
 #include "internal.h"
+#include "merge_device.h"
 #include "ring_device.h"
 
 #include <cmath>
@@ -24,58 +25,7 @@ namespace wmtp {
 
 namespace {
 
-constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.693147180559945309f;
-constexpr int kUnroll = 8;
-
-// One split lane's share of the merge, in a single pass over its splits
-// p0 + sl, p0 + sl + SL, ... < p1: kUnroll (o_s, lse_s) pairs are loaded at a
-// time, all independent of one another, and folded into a running maximum m
-// and sums acc = sum_s exp(lse_s - m) * o_s, wsum = sum_s exp(lse_s - m),
-// rescaled when m rises.  The lanes' states are then brought to the common
-// maximum by the caller.
-struct LaneMerge {
-  f32x4 acc;
-  float wsum;
-  float m;   // log2 units; -inf while the lane has seen no key
-};
-
-__device__ __forceinline__ LaneMerge merge_lane(const float* base, const float* lse, size_t stride,
-                                                int R, int row, int p0, int p1, int sl, int SL) {
-  LaneMerge s = {f32x4{0.f, 0.f, 0.f, 0.f}, 0.f, -INFINITY};
-  for (int p = p0 + sl; p < p1; p += SL * kUnroll) {
-    f32x4 v[kUnroll];
-    float l[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int q = p + u * SL;
-      if (q < p1) {
-        v[u] = *reinterpret_cast<const f32x4*>(base + (size_t)q * stride);
-        l[u] = lse[(size_t)q * R + row] * kLog2e;
-      } else {
-        v[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-        l[u] = -INFINITY;
-      }
-    }
-    float bm = l[0];
-#pragma unroll
-    for (int u = 1; u < kUnroll; ++u) bm = fmaxf(bm, l[u]);
-    if (bm == -INFINITY) continue;   // no keys in this batch
-    if (bm > s.m) {
-      const float f = s.m == -INFINITY ? 0.f : fast_exp2(s.m - bm);
-      s.acc *= f;
-      s.wsum *= f;
-      s.m = bm;
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const float w = l[u] == -INFINITY ? 0.f : fast_exp2(l[u] - s.m);
-      s.acc += v[u] * w;
-      s.wsum += w;
-    }
-  }
-  return s;
-}
 
 template <int SL>
 __device__ __forceinline__ float max_over_split_lanes(float v) {
