@@ -1,6 +1,5 @@
-// Device-side log-sum-exp merge of per-split attention results, shared by the
-// merge kernels (combine.hip) and the merge workgroups of the one-launch fused
-// draft step (attn.hip):
+// Device-side log-sum-exp merge of per-split attention results, the core of the
+// merge kernels (combine.hip):
 //     lse = ln sum_s exp(lse_s),   o = sum_s exp(lse_s - lse) * o_s.
 #pragma once
 
