@@ -544,22 +544,61 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
   const std::true_type more;
   const std::false_type last;
 
-  // A wave's first tile takes the rows' first maxima (no row has one yet, so
-  // nothing is rescaled) and starts the accumulators.
-  if (kb >= kb1) {
-    zero_acc();   // no tiles
-  } else if (kb + NW >= kb1) {
-    scores_of(last);   // the only tile
-    first_max_or_rescale<D, NB>(st, mx);
-    zero_acc();
-    finish(last);
+  // Ring windows (a tile or two per wave): a wave's first tile takes the rows'
+  // first maxima (no row has one yet, so nothing is rescaled) and its PV starts
+  // the accumulators, which are then never zeroed in registers.  The long
+  // paged passes zero them up front and keep one copy of the loop body: there
+  // the saving is one tile's worth in dozens.  (The two structures are written
+  // out in full: at D = 256 the register allocation of either is fragile.)
+  if constexpr (RING) {
+    if (kb >= kb1) {
+      zero_acc();   // no tiles
+    } else if (kb + NW >= kb1) {
+      scores_of(last);   // the only tile
+      first_max_or_rescale<D, NB>(st, mx);
+      zero_acc();
+      finish(last);
+    } else {
+      next_tile();
+      scores_of(more);
+      first_max_or_rescale<D, NB>(st, mx);
+      zero_acc();
+      finish(more);
+      advance();
+      // Fast loop over the tiles that have a successor: no accumulator rescale.
+      // It leaves early when tile kb needs one; its scores are then already in
+      // x / mx.
+      bool general = false;
+      while (kb + NW < kb1) {
+        next_tile();
+        scores_of(more);
+        if (first_max_or_rescale<D, NB>(st, mx)) {
+          general = true;
+          break;
+        }
+        finish(more);
+        advance();
+      }
+      // General loop, from the tile the fast loop left on.
+      if (general) {
+        raise_and_rescale<D, NB>(st, mx);
+        finish(more);
+        advance();
+        while (kb + NW < kb1) {
+          next_tile();
+          scores_of(more);
+          raise_and_rescale<D, NB>(st, mx);
+          finish(more);
+          advance();
+        }
+      }
+      // The wave's last tile.
+      scores_of(last);
+      if (general || first_max_or_rescale<D, NB>(st, mx)) raise_and_rescale<D, NB>(st, mx);
+      finish(last);
+    }
   } else {
-    next_tile();
-    scores_of(more);
-    first_max_or_rescale<D, NB>(st, mx);
     zero_acc();
-    finish(more);
-    advance();
     // Fast loop over the tiles that have a successor: no accumulator rescale.
     // It leaves early when tile kb needs one; its scores are then already in
     // x / mx.
@@ -588,9 +627,11 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
       }
     }
     // The wave's last tile.
-    scores_of(last);
-    if (general || first_max_or_rescale<D, NB>(st, mx)) raise_and_rescale<D, NB>(st, mx);
-    finish(last);
+    if (kb < kb1) {
+      scores_of(last);
+      if (general || first_max_or_rescale<D, NB>(st, mx)) raise_and_rescale<D, NB>(st, mx);
+      finish(last);
+    }
   }
 
   // ---- merge the four waves' states through LDS, one row block at a time ----
