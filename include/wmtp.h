@@ -79,8 +79,10 @@ typedef enum wmtp_status {
                                       e.g. after gathering partials of a sequence that is
                                       split across devices */
 
-/* Human-readable name of a status code (static string, never NULL). */
-const char* wmtp_status_string(wmtp_status s);
+/* Human-readable name of a status code (static string, never NULL).  Takes a
+ * plain int, so that any value a caller holds is valid input: codes outside
+ * wmtp_status give "unknown status". */
+const char* wmtp_status_string(int status);
 
 /* `call` argument of the two planning queries below */
 #define WMTP_CALL_PAGED 0        /* wmtp_draft_attn_full, wmtp_verify_attn */

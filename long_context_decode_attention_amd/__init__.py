@@ -18,7 +18,9 @@ import os
 from dataclasses import dataclass
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libwmtp.so")
+# WMTP_LIBRARY names another build of the same library (e.g. the host-sanitized
+# one the CPU tests load); there is no fallback when the file is missing.
+LIB_PATH = os.environ.get("WMTP_LIBRARY") or os.path.join(HERE, "libwmtp.so")
 PAGE = 64
 FLAG_PARTIALS_ONLY = 1
 

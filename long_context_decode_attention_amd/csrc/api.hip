@@ -71,7 +71,7 @@ wmtp_status run_attention(AttnArgs a, bool ring, int max_keys, int plan_keys, fl
   AttnPlan p;
   if (!plan_attention(a.B, a.Hq, a.Hkv, a.D, a.n_q, plan_keys, num_splits, partials_only, ring,
                       &p, a.kv8 != 0))
-    return (a.n_q * (a.Hq / a.Hkv) > 256) ? WMTP_ERR_UNSUPPORTED : WMTP_ERR_INVALID_ARG;
+    return ((long)a.n_q * (a.Hq / a.Hkv) > 256) ? WMTP_ERR_UNSUPPORTED : WMTP_ERR_INVALID_ARG;
   if (a.win && p.shared) return WMTP_ERR_UNSUPPORTED;   // truncated index: split kernel only
   if (a.kv8 && p.shared) return WMTP_ERR_UNSUPPORTED;   // fp8 caches: split kernel only
   if (p.ws_bytes > 0) {
@@ -125,8 +125,8 @@ bool attn_dims_ok(int B, int Hq, int Hkv, int D) {
 
 extern "C" {
 
-const char* wmtp_status_string(wmtp_status s) {
-  switch (s) {
+const char* wmtp_status_string(int status) {
+  switch (status) {
     case WMTP_OK: return "ok";
     case WMTP_ERR_INVALID_ARG: return "invalid argument";
     case WMTP_ERR_UNSUPPORTED: return "unsupported configuration";
@@ -188,7 +188,7 @@ static wmtp_status paged_attention(const uint16_t* q, const uint16_t* k_cache,
                                    bool kv8 = false, float k_scale = 1.f, float v_scale = 1.f) {
   if (!attn_dims_ok(B, Hq, Hkv, D) || n_q < 1) return WMTP_ERR_INVALID_ARG;
   if (!head_dim_ok(D)) return WMTP_ERR_UNSUPPORTED;
-  if (n_q * (Hq / Hkv) > 256) return WMTP_ERR_UNSUPPORTED;
+  if ((long)n_q * (Hq / Hkv) > 256) return WMTP_ERR_UNSUPPORTED;
   if (num_pages < 1 || max_pages < 1 || max_seq_len < 0 || num_splits < 0)
     return WMTP_ERR_INVALID_ARG;
   if ((flags & ~WMTP_FLAG_PARTIALS_ONLY) != 0) return WMTP_ERR_INVALID_ARG;
@@ -221,7 +221,7 @@ static wmtp_status paged_attention(const uint16_t* q, const uint16_t* k_cache,
         !(v_scale > 0.f))
       return WMTP_ERR_INVALID_ARG;
     // fp8 caches: the split kernel only (up to 32 query rows per kv head)
-    if (n_q * (Hq / Hkv) > 32) return WMTP_ERR_UNSUPPORTED;
+    if ((long)n_q * (Hq / Hkv) > 32) return WMTP_ERR_UNSUPPORTED;
     a.kv8 = 1;
     a.scale_log2 = softmax_scale * k_scale * kLog2e;   // logits of the K codes
     a.v_scale = v_scale;

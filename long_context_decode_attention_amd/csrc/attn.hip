@@ -307,7 +307,7 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
     return t64 < 0 ? 0 : (t64 > t_max ? (int)t_max : (int)t64);
   };
   const int L = RING ? a.C : (len_raw < 0 ? 0 : (len_raw > a.max_keys ? a.max_keys : len_raw));
-  const int nkb = (L + 31) >> 5;
+  const int nkb = (int)(((unsigned)L + 31u) >> 5);   // L >= 0
   // Truncated paged index (win): the key set [0, sink_end) u [r0, L) as virtual
   // tiles, the sink tiles [0, st_end) then the recent tiles from kr on; phys()
   // maps a virtual tile to its 32-key tile of the sequence.
@@ -315,7 +315,7 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
   if (!RING && a.win) {
     sink_end = min(a.n_sink, L);
     r0 = max(a.n_sink, L - a.n_recent);
-    st_end = (sink_end + 31) >> 5;
+    st_end = (int)(((unsigned)sink_end + 31u) >> 5);
     kr = max(r0 >> 5, st_end);
     nvt = st_end + max(nkb - kr, 0);
   }
@@ -766,8 +766,8 @@ bool plan_window_step(int B, int Hq, int Hkv, int D, int n_q, int C, int num_spl
     return false;
   if (D != 64 && D != 128 && D != 256) return false;
   p->G = Hq / Hkv;
+  if ((long)n_q * p->G > 256) return false;
   p->R = n_q * p->G;
-  if (p->R > 256) return false;
   p->shared = 0;
   p->nrb = 1;
   p->nrg = (p->R + 31) / 32;
@@ -779,7 +779,7 @@ bool plan_window_step(int B, int Hq, int Hkv, int D, int n_q, int C, int num_spl
   // launch then reads.
   int kbps;
   if (num_splits > 0) {
-    kbps = (p->nkb + num_splits - 1) / num_splits;
+    kbps = (int)(((long)p->nkb + num_splits - 1) / num_splits);
   } else {
     const long units = (long)B * Hkv * p->nrg;
     const long per_unit = units < WMTP_TARGET_WG_SPLIT ? WMTP_TARGET_WG_SPLIT / units : 1;
@@ -814,9 +814,9 @@ bool plan_attention(int B, int Hq, int Hkv, int D, int n_q, int max_keys, int nu
     return false;
   if (D != 64 && D != 128 && D != 256) return false;
   p->G = Hq / Hkv;
+  if ((long)n_q * p->G > 256) return false;
   p->R = n_q * p->G;
-  if (p->R > 256) return false;
-  p->nkb = (max_keys + 31) / 32;
+  p->nkb = (int)(((long)max_keys + 31) / 32);
   const long groups = (long)B * Hkv;
   long target;    // workgroups to aim at
   int cap;        // most 32-key tiles per split
@@ -867,7 +867,7 @@ bool plan_attention(int B, int Hq, int Hkv, int D, int n_q, int max_keys, int nu
   if (kv8 && D == 128 && !ring && !p->shared && p->nkb >= 2048) target *= 2;
   int kbps;
   if (num_splits > 0) {
-    kbps = (p->nkb + num_splits - 1) / num_splits;
+    kbps = (int)(((long)p->nkb + num_splits - 1) / num_splits);
   } else {
     // As many splits per (group, row group) as keep the workgroups within the
     // target, the tiles spread evenly over them: at one workgroup per CU, a

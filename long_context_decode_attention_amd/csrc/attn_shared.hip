@@ -298,7 +298,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
 
   const int l_in = a.seq_lens[b];
   const int L = l_in < 0 ? 0 : (l_in > a.max_keys ? a.max_keys : l_in);
-  const int nkb = (L + 31) >> 5;
+  const int nkb = (int)(((unsigned)L + 31u) >> 5);   // L >= 0
   const int kb0 = s * a.kb_per_split;
   const int kb1 = min(kb0 + a.kb_per_split, nkb);
   const int ntile = kb1 > kb0 ? kb1 - kb0 : 0;

@@ -361,3 +361,40 @@ def test_cache_and_ring_shapes():
         assert (r.B, r.Hkv, r.D) == (2, 2, D)
         assert r.k.shape[0] == 2 * 128 // 64
         assert int(r.pos.min()) == -1 and int(r.T.sum()) == 0
+
+
+def test_planner_sweep_extremes():
+    """The planning queries over a grid that includes extreme and invalid sizes:
+    each answers -1 / 0 or a consistent plan, and nothing in the host arithmetic
+    overflows (run under the host sanitizers by test_abi_hostsan.py, where a
+    signed overflow or an out-of-range shift aborts the process)."""
+    lib = _lib()
+    big = 2 ** 31 - 1
+    calls = (0, 1, 2, 3, 4, 7, -1)
+    Bs = (1, 8, 4096, 65535, 65536, big, 0, -1)
+    heads = ((32, 2), (64, 2), (32, 4), (1, 1), (256, 1), (512, 2), (big, 1), (32, 0), (0, 1), (33, 2))
+    Ds = (64, 128, 256, 96, 0, -64)
+    nqs = (1, 8, 16, 256, 0, big)
+    keys = (0, 1, 31, 32, 4096, 1048576, 2 ** 30, big, -1)
+    splits = (0, 1, 7, 1000, big, -1)
+    n = 0
+    for call in calls:
+        for B in Bs:
+            for Hq, Hkv in heads:
+                for D in Ds:
+                    for n_q in nqs:
+                        for mk in keys:
+                            for ns in splits[:3] if n_q != 1 else splits:
+                                s = lib.wmtp_plan_splits(call, B, Hq, Hkv, D, n_q, mk, ns)
+                                w = lib.wmtp_workspace_bytes(call, B, Hq, Hkv, D, n_q, mk, ns, 0)
+                                n += 1
+                                if s == -1:
+                                    assert w == 0
+                                    continue
+                                assert s >= 1, (call, B, Hq, Hkv, D, n_q, mk, ns, s)
+                                R = n_q * (Hq // Hkv)
+                                parts = B * Hkv * (s + 1 if call == 3 else s)
+                                # a plan with one split per group may write o directly (no workspace)
+                                assert w == 0 and s == 1 or w >= parts * R * D * 4, \
+                                    (call, B, Hq, Hkv, D, n_q, mk, ns, s, w)
+    assert n > 10000
