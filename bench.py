@@ -24,7 +24,8 @@ Also timed beside them: the windowed arm as ring append + windowed attention
 before every step (cold) against back-to-back steps (warm), the windowed draft
 through a truncated index of the paged draft KV, the draft context pass (fused
 with its append, and as append then attention), the verify of a tree of
-proposals and the native arm over fp8 draft KV.  Then the other workloads (8K,
+proposals, the native arm over fp8 draft KV and the verify over fp8 target KV.
+Then the other workloads (8K,
 128K, the ragged batch of 8 and the 8-layer stack) run the same arms at their own
 shapes with K/V generated on the device, and the float64 oracle is timed on the
 host for one native draft step, one windowed draft step and one verify of the 1M
@@ -537,6 +538,13 @@ def measure_main(args):
         lib.paged_append_fp8(k8, v8, dkv.block_table, torch.tensor([lo], dtype=torch.int32, device=dev),
                              sc.to_device_bf16(Kd[lo:hi]).unsqueeze(0),
                              sc.to_device_bf16(Vd[lo:hi]).unsqueeze(0))
+    # the target KV as fp8 codes too, on the target's pages: the verify over fp8 KV
+    kt8, vt8 = lib.new_paged_cache_fp8(tkv.num_pages, Hkv, D, dev)
+    for lo in range(0, S, 1 << 16):
+        hi = min(S, lo + (1 << 16))
+        lib.paged_append_fp8(kt8, vt8, tkv.block_table, torch.tensor([lo], dtype=torch.int32, device=dev),
+                             sc.to_device_bf16(Kt[lo:hi]).unsqueeze(0),
+                             sc.to_device_bf16(Vt[lo:hi]).unsqueeze(0))
     # per-step inputs, resident on the device
     kd_new = sc.to_device_bf16(Kd[S:S + d_extra]).view(nsteps, gamma, 1, 1, Hkv, D)
     vd_new = sc.to_device_bf16(Vd[S:S + d_extra]).view(nsteps, gamma, 1, 1, Hkv, D)
@@ -587,6 +595,9 @@ def measure_main(args):
     o_8 = torch.empty(B, Hq, D, device=dev)
     l_8 = torch.empty(B, Hq, device=dev)
     ws_v = lib.new_workspace(lib.workspace_bytes(B, Hq, Hkv, D, n_q, max_t), dev)
+    ws_v8 = lib.new_workspace(lib.workspace_bytes(B, Hq, Hkv, D, n_q, max_t, fp8=True), dev)
+    o_v8 = torch.empty(B, n_q, Hq, D, device=dev)
+    l_v8 = torch.empty(B, n_q, Hq, device=dev)
     o_c = torch.empty(B, n_ctx, Hq, D, device=dev)
     l_c = torch.empty(B, n_ctx, Hq, device=dev)
     ws_cw = lib.new_workspace(lib.workspace_bytes(B, Hq, Hkv, D, n_ctx, C + 64, ring=True), dev)
@@ -670,7 +681,13 @@ def measure_main(args):
                                                      fp8=True),
                                   B, Hkv, G, 1, splits_per_group=splits_8,
                                   o=o_8.view(B, 1, Hq, D), lse=l_8.view(B, 1, Hq), prepare=True)))
-        plan.append((win, full, wpg, ver, ctx, full8, fused))
+        # the verify over the fp8 target KV: quantizing append of the proposed
+        # positions, then the verify (same queries, same outputs' shapes)
+        ver8 = (lib.paged_append_fp8(kt8, vt8, tkv.block_table, t_pos[k], kt_new[k], vt_new[k],
+                                     prepare=True),
+                lib.verify_attn_fp8(qv[k], kt8, vt8, tkv.block_table, t_len[k], max_t, 1.0, 1.0,
+                                    1.0, o_v8, l_v8, ws_v8, prepare=True))
+        plan.append((win, full, wpg, ver, ctx, full8, fused, ver8))
     # The windowed arm's draft steps once more, each bench step's seven recorded in a
     # HIP graph (14 launches) and replayed: the launches without per-call host work.
     ws_g = lib.new_workspace(lib.step_workspace_bytes(B, Hq, Hkv, D, C), dev)
@@ -696,7 +713,7 @@ def measure_main(args):
     cold = [[lib.draft_step_window(qd[k, j], ring_k, kd_new[k, j], vd_new[k, j], 1.0, o_k, l_k,
                                    ws_k, prepare=True) for j in range(gamma)] for k in range(nsteps)]
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(15 + 4 * gamma)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(17 + 4 * gamma)]
            for _ in range(nsteps)]
     evc = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
             for _ in range(gamma)] for _ in range(nsteps)]
@@ -709,7 +726,7 @@ def measure_main(args):
             evc[k][j][1].record(stream)
 
     def step(k):
-        win, full, wpg, ver, ctx, full8, fused = plan[k]
+        win, full, wpg, ver, ctx, full8, fused, ver8 = plan[k]
         e = evs[k]
         e[11 + 4 * gamma].record(stream)
         for c in fused:                     # windowed arm: gamma x fused draft step
@@ -751,10 +768,15 @@ def measure_main(args):
             e[11 + 2 * gamma + 2 * j].record(stream)
             comb()
         e[9 + 2 * gamma].record(stream)
+        ver8[0]()                           # fp8 target append of the proposed positions
+        e[15 + 4 * gamma].record(stream)
+        ver8[1]()                           # verify over the fp8 target KV
+        e[16 + 4 * gamma].record(stream)
         return {"s0": e[11 + 4 * gamma], "s1": e[12 + 4 * gamma], "g1": e[14 + 4 * gamma],
                 "t0": e[0], "t1": e[1], "t2": e[2], "p1": e[5 + 2 * gamma], "v0": e[3],
                 "t3": e[4], "cf": e[13 + 4 * gamma], "c1": e[6 + 2 * gamma],
                 "c2": e[7 + 2 * gamma], "c3": e[8 + 2 * gamma], "f8": e[9 + 2 * gamma],
+                "v8a": e[15 + 4 * gamma], "v8": e[16 + 4 * gamma],
                 "attn8": [(e[10 + 2 * gamma + 2 * j], e[11 + 2 * gamma + 2 * j]) for j in range(gamma)],
                 "attn": [(e[5 + 2 * j], e[6 + 2 * j]) for j in range(gamma)]}
 
@@ -800,6 +822,8 @@ def measure_main(args):
     full8 = per("c3", "f8")
     verify = per("p1", "t3")
     verify_k = per("v0", "t3")
+    verify8 = per("f8", "v8")                    # fp8 append + verify over fp8 target KV
+    verify8_k = per("v8a", "v8")
     attn8 = [us(a, b) for m in marks for (a, b) in m["attn8"]]
     attn = [us(a, b) for m in marks for (a, b) in m["attn"]]
     cold_step = [us(a, b) for k in range(args.warmup, nsteps) for (a, b) in evc[k]]
@@ -818,6 +842,7 @@ def measure_main(args):
     attn8_bytes = kv_bytes / 2 * L_avg + B * Hq * D * 2    # fp8 K + V of the keys + q
     attn_bytes = kv_bytes * L_avg + B * Hq * D * 2         # keys' K/V + q (algorithmic)
     verify_bytes = kv_bytes * (S + n_q * (args.warmup + nsteps) / 2.0) + B * n_q * Hq * (D * 2 + D * 4 + 4)
+    verify8_bytes = kv_bytes / 2 * (S + n_q * (args.warmup + nsteps) / 2.0) + B * n_q * Hq * (D * 2 + D * 4 + 4)
     win_bytes = kv_bytes * (n_sink + n_recent) + B * Hq * D * 2
     achieved = attn_bytes / (attn_mean * 1e-6) / 1e9
     verify_gbs = verify_bytes / (md(verify_k) * 1e-6) / 1e9
@@ -865,7 +890,9 @@ def measure_main(args):
                            "window_append_then_attend": stats([v + w for v, w in zip(verify, win3)]),
                            "verify": stats(verify),
                            "verify_kernel": stats(verify_k),
-                           "verify_tree_kernel": stats(tree)},
+                           "verify_tree_kernel": stats(tree),
+                           "verify_fp8_kv": stats(verify8),
+                           "verify_fp8_kv_kernel": stats(verify8_k)},
         "cost_reduction": {"native_over_window_minus_1": round(sf / sw - 1.0, 4),
                            "one_minus_window_over_native": round(1.0 - sw / sf, 4)},
         "draft_context_pass_us": {"queries": n_ctx, "window": stats(ctx_w),
@@ -890,6 +917,11 @@ def measure_main(args):
         "roofline_verify": {"bound": "hbm", "achieved": round(verify_gbs, 1), "peak": HBM_PEAK_GBS,
                             "unit": "GB/s", "frac": round(verify_gbs / HBM_PEAK_GBS, 4),
                             "bytes_per_launch": int(verify_bytes)},
+        "roofline_verify_fp8_kv": {
+            "bound": "hbm", "achieved": round(verify8_bytes / (md(verify8_k) * 1e-6) / 1e9, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(verify8_bytes / (md(verify8_k) * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "bytes_per_launch": int(verify8_bytes)},
         "roofline_full_fp8_kv": {
             "bound": "hbm", "achieved": round(attn8_bytes / (attn8_mean * 1e-6) / 1e9, 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -90,7 +90,7 @@ const char* wmtp_status_string(int status);
 #define WMTP_CALL_PAGED_WINDOW 2 /* wmtp_draft_attn_window_paged */
 #define WMTP_CALL_RING_STEP 3    /* wmtp_draft_step_window (n_q = 1) and
                                     wmtp_draft_context_step_window; max_keys = C */
-#define WMTP_CALL_PAGED_FP8 4    /* wmtp_draft_attn_full_fp8 */
+#define WMTP_CALL_PAGED_FP8 4    /* wmtp_draft_attn_full_fp8, wmtp_verify_attn_fp8 */
 
 /*
  * Split plan of the attention calls.  n_q = 1 for the draft calls;
@@ -194,6 +194,28 @@ wmtp_status wmtp_draft_attn_window_paged_fp8(
     int max_seq_len, int n_sink, int n_recent, float k_scale, float v_scale, float softmax_scale,
     float* o, float* lse, void* workspace, size_t workspace_bytes, int num_splits, unsigned flags,
     void* stream);
+
+/*
+ * The causal verify over fp8 caches: as wmtp_verify_attn (n_q queries, the
+ * attention over the dequantized keys and values of the caches described above
+ * for wmtp_draft_attn_full_fp8; k_scale folds into the logit scale, v_scale into
+ * the output).  (Verdict page, forward implications: the window composes with
+ * fp8 KV quantization; the verify reads the target KV, which fp8 halves.)  Up to
+ * 256 query rows per kv head (n_q * Hq / Hkv) as for bf16: more than 32 go
+ * through the kernel that shares each tile among its waves in LDS, which copies
+ * the fp8 bytes there and widens each operand to bf16 right before its product.
+ *   k_cache, v_cache   uint8 fp8 caches (16-byte aligned)
+ *   k_scale, v_scale   finite, > 0 (else WMTP_ERR_INVALID_ARG)
+ *   other arguments as wmtp_verify_attn; workspace and plan as
+ *   WMTP_CALL_PAGED_FP8 with this n_q
+ */
+wmtp_status wmtp_verify_attn_fp8(const uint16_t* q, const uint8_t* k_cache,
+                                 const uint8_t* v_cache, const int32_t* block_table,
+                                 const int32_t* seq_lens, int B, int n_q, int Hq, int Hkv, int D,
+                                 int num_pages, int max_pages, int max_seq_len, float k_scale,
+                                 float v_scale, float softmax_scale, float* o, float* lse,
+                                 void* workspace, size_t workspace_bytes, int num_splits,
+                                 unsigned flags, void* stream);
 
 /*
  * Verify of a tree of proposals: as wmtp_verify_attn, but the n_q appended

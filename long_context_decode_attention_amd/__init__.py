@@ -30,7 +30,8 @@ EXPORTS = (
     "wmtp_draft_attn_full", "wmtp_draft_attn_window", "wmtp_draft_attn_window_paged",
     "wmtp_draft_context_window", "wmtp_verify_attn_tree", "wmtp_paged_append_fp8",
     "wmtp_draft_attn_full_fp8", "wmtp_draft_attn_window_paged_fp8", "wmtp_ring_append",
-    "wmtp_paged_append", "wmtp_verify_attn", "wmtp_split_combine", "wmtp_draft_step_window",
+    "wmtp_paged_append", "wmtp_verify_attn", "wmtp_verify_attn_fp8", "wmtp_split_combine",
+    "wmtp_draft_step_window",
     "wmtp_draft_context_step_window", "wmtp_draft_step_window_static",
 )
 
@@ -73,6 +74,7 @@ _SIGS = {
     "wmtp_draft_step_window_static": ([_P] * 7 + [_I] * 8 + [_F, _P, _P, _I, _P], _I),
     "wmtp_paged_append": ([_P] * 6 + [_I] * 6 + [_P], _I),
     "wmtp_verify_attn": ([_P] * 5 + [_I] * 8 + [_F, _P, _P, _P, _SZ, _I, _U, _P], _I),
+    "wmtp_verify_attn_fp8": ([_P] * 5 + [_I] * 8 + [_F, _F, _F, _P, _P, _P, _SZ, _I, _U, _P], _I),
     "wmtp_split_combine": ([_P, _P, _I, _P] + [_I] * 6 + [_P, _P, _P], _I),
 }
 
@@ -422,6 +424,38 @@ def verify_attn(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, softmax
         B, n_q, Hq, Hkv, D, num_pages, max_pages, int(max_seq_len), float(softmax_scale),
         _ptr(o), _ptr(lse), _ptr(workspace), workspace.numel(), int(num_splits),
         FLAG_PARTIALS_ONLY if partials_only else 0, _stream(stream)), prepare)
+    if prepare:
+        return c
+    return workspace if partials_only else (o, lse)
+
+
+def verify_attn_fp8(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, k_scale=1.0,
+                    v_scale=1.0, softmax_scale=1.0, o=None, lse=None, workspace=None,
+                    num_splits=0, partials_only=False, stream=None, prepare=False):
+    """Causal full-context verify over fp8 caches (``wmtp_verify_attn_fp8``); q is
+    [B, n_q, Hq, D], the caches uint8 (e4m3 codes) in the tiled page layout."""
+    torch = _torch()
+    B, n_q, Hq, D = q.shape
+    num_pages, Hkv = k_cache.shape[0], k_cache.shape[1]
+    max_pages = block_table.shape[1]
+    _need(q, torch.bfloat16, None, "q")
+    _need(k_cache, torch.uint8, k_cache_shape(num_pages, Hkv, D), "k_cache")
+    _need(v_cache, torch.uint8, v_cache_shape(num_pages, Hkv, D), "v_cache")
+    _need(block_table, torch.int32, (B, max_pages), "block_table")
+    _need(seq_lens, torch.int32, (B,), "seq_lens")
+    max_keys = min(int(max_seq_len), max_pages * PAGE)
+    need = workspace_bytes(B, Hq, Hkv, D, n_q, max_keys, num_splits, partials_only, fp8=True)
+    if workspace is None:
+        workspace = new_workspace(need, q.device)
+    _need(workspace, torch.uint8, None, "workspace")
+    if not partials_only:
+        o, lse = _outputs(o, lse, (B, n_q, Hq, D), (B, n_q, Hq), q.device)
+    c = _invoke("wmtp_verify_attn_fp8", (
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
+        B, n_q, Hq, Hkv, D, num_pages, max_pages, int(max_seq_len), float(k_scale),
+        float(v_scale), float(softmax_scale), _ptr(o), _ptr(lse), _ptr(workspace),
+        workspace.numel(), int(num_splits), FLAG_PARTIALS_ONLY if partials_only else 0,
+        _stream(stream)), prepare)
     if prepare:
         return c
     return workspace if partials_only else (o, lse)

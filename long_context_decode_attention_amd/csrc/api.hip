@@ -73,7 +73,6 @@ wmtp_status run_attention(AttnArgs a, bool ring, int max_keys, int plan_keys, fl
                       &p, a.kv8 != 0))
     return ((long)a.n_q * (a.Hq / a.Hkv) > 256) ? WMTP_ERR_UNSUPPORTED : WMTP_ERR_INVALID_ARG;
   if (a.win && p.shared) return WMTP_ERR_UNSUPPORTED;   // truncated index: split kernel only
-  if (a.kv8 && p.shared) return WMTP_ERR_UNSUPPORTED;   // fp8 caches: split kernel only
   if (p.ws_bytes > 0) {
     if (!workspace || !aligned16(workspace)) return WMTP_ERR_WORKSPACE;
     if (workspace_bytes < p.ws_bytes) return WMTP_ERR_WORKSPACE;
@@ -220,8 +219,10 @@ static wmtp_status paged_attention(const uint16_t* q, const uint16_t* k_cache,
     if (!std::isfinite(k_scale) || !(k_scale > 0.f) || !std::isfinite(v_scale) ||
         !(v_scale > 0.f))
       return WMTP_ERR_INVALID_ARG;
-    // fp8 caches: the split kernel only (up to 32 query rows per kv head)
-    if ((long)n_q * (Hq / Hkv) > 32) return WMTP_ERR_UNSUPPORTED;
+    // fp8 caches: a draft (one query) reads them through the split kernel only,
+    // up to 32 query rows per kv head; a verify also through the shared kernel
+    if (n_q == 1 && Hq / Hkv > 32) return WMTP_ERR_UNSUPPORTED;
+    if (tree_mask) return WMTP_ERR_UNSUPPORTED;   // no fp8 tree verify
     a.kv8 = 1;
     a.scale_log2 = softmax_scale * k_scale * kLog2e;   // logits of the K codes
     a.v_scale = v_scale;
@@ -344,6 +345,20 @@ wmtp_status wmtp_draft_attn_window_paged_fp8(
                          Hq, Hkv, D, num_pages, max_pages, max_seq_len, softmax_scale, o, lse,
                          workspace, workspace_bytes, num_splits, flags, stream, true, n_sink,
                          n_recent, nullptr, true, k_scale, v_scale);
+}
+
+wmtp_status wmtp_verify_attn_fp8(const uint16_t* q, const uint8_t* k_cache,
+                                 const uint8_t* v_cache, const int32_t* block_table,
+                                 const int32_t* seq_lens, int B, int n_q, int Hq, int Hkv, int D,
+                                 int num_pages, int max_pages, int max_seq_len, float k_scale,
+                                 float v_scale, float softmax_scale, float* o, float* lse,
+                                 void* workspace, size_t workspace_bytes, int num_splits,
+                                 unsigned flags, void* stream) {
+  return paged_attention(q, reinterpret_cast<const uint16_t*>(k_cache),
+                         reinterpret_cast<const uint16_t*>(v_cache), block_table, seq_lens, B, n_q,
+                         Hq, Hkv, D, num_pages, max_pages, max_seq_len, softmax_scale, o, lse,
+                         workspace, workspace_bytes, num_splits, flags, stream, false, 0, 0,
+                         nullptr, true, k_scale, v_scale);
 }
 
 wmtp_status wmtp_verify_attn_tree(const uint16_t* q, const uint16_t* k_cache,

@@ -21,7 +21,16 @@
 // The per-tile math is the one of attn.hip (MFMA 32x32x16, online softmax with
 // P as bf16 hi + lo parts); a wave's rows never meet another wave's, so each
 // wave writes its own rows' (o, lse).
+//
+// fp8 caches (KV8): a tile keeps the bf16 tile's element order at one byte per
+// element, so its K half and its V half are each copied into LDS as they lie in
+// memory (1 KB direct loads of contiguous bytes, half as many as for bf16); an
+// operand is then 8 bytes per lane, read at the element offset the bf16 layout
+// gives and turned into the bf16 MFMA operand right before its product (every
+// e4m3 value is a bf16 value: exact).
 #include "attn_device.h"
+
+#include <type_traits>
 
 namespace wmtp {
 
@@ -74,10 +83,40 @@ __device__ __forceinline__ void lds_load_async(const void* base, uint32_t voff, 
 // above it, which bounds how many operand registers are live at once.
 __device__ __forceinline__ void operand_fence() { asm volatile("" ::: "memory"); }
 
+// An MFMA operand as it sits in LDS: 16 bytes of bf16, or 8 bytes of fp8 codes.
+template <bool KV8>
+using LdsOp = std::conditional_t<KV8, u32x2, bf16x8>;
+
+template <bool KV8>
+__device__ __forceinline__ LdsOp<KV8> lds_op(const unsigned char* p) {
+  return *reinterpret_cast<const LdsOp<KV8>*>(p);
+}
+
+// LDS byte offsets, inside a stage, of K operand ks and of V^T operand (db, kk),
+// without the lane's own offset (k_lane / v_lane).  bf16: each operand is a
+// 1 KB block in MFMA lane order.  fp8: the stage holds the tile's bytes as in
+// memory, so the offsets are the tile's element offsets.
+template <int D, bool KV8>
+__device__ __forceinline__ int k_lds(int ks) { return KV8 ? ks * 512 : ks * 1024; }
+template <int D, bool KV8>
+__device__ __forceinline__ int v_lds(int db, int kk) {
+  return KV8 ? kk * (16 * D) + db * 512 : (2 * db + kk) * 1024;
+}
+template <bool KV8>
+__device__ __forceinline__ int k_lane(int lane) {
+  const int m = lane & 31, h = lane >> 5;
+  return KV8 ? s_row_key(m) * 16 + 8 * h : lane * 16;
+}
+template <bool KV8>
+__device__ __forceinline__ int v_lane(int lane) {
+  const int m = lane & 31, h = lane >> 5;
+  return KV8 ? m * 16 + 8 * h : lane * 16;
+}
+
 // S^T of one tile for this wave's RBW row blocks: K operands read from the LDS
 // stage at `base` (offset by lane * 16) in two halves.  The MFMAs are only
 // issued here; their results are used one iteration later.
-template <int D, int RBW>
+template <int D, int RBW, bool KV8>
 __device__ __forceinline__ void s_tile(f32x16 (&sacc)[RBW], const bf16x8 (&qop)[RBW][D / 16],
                                        const unsigned char* base) {
   constexpr int KS = D / 16;
@@ -86,14 +125,15 @@ __device__ __forceinline__ void s_tile(f32x16 (&sacc)[RBW], const bf16x8 (&qop)[
   for (int rb = 0; rb < RBW; ++rb) sacc[rb] = f32x16{};
 #pragma unroll
   for (int k0 = 0; k0 < KS; k0 += KH) {
-    bf16x8 kop[KH];
+    LdsOp<KV8> kop[KH];
 #pragma unroll
-    for (int ks = 0; ks < KH; ++ks)
-      kop[ks] = *reinterpret_cast<const bf16x8*>(base + (k0 + ks) * 1024);
+    for (int ks = 0; ks < KH; ++ks) kop[ks] = lds_op<KV8>(base + k_lds<D, KV8>(k0 + ks));
 #pragma unroll
-    for (int ks = 0; ks < KH; ++ks)
+    for (int ks = 0; ks < KH; ++ks) {
+      const bf16x8 k = as_operand(kop[ks]);
 #pragma unroll
-      for (int rb = 0; rb < RBW; ++rb) sacc[rb] = mfma32x32x16(kop[ks], qop[rb][k0 + ks], sacc[rb]);
+      for (int rb = 0; rb < RBW; ++rb) sacc[rb] = mfma32x32x16(k, qop[rb][k0 + ks], sacc[rb]);
+    }
     operand_fence();
   }
 }
@@ -102,7 +142,7 @@ __device__ __forceinline__ void s_tile(f32x16 (&sacc)[RBW], const bf16x8 (&qop)[
 // stage at `base`, in two halves.  mask_v (wave-uniform): some key of the tile
 // is past the sequence length, and its values, which may hold any bits (even
 // NaN), are zeroed so that 0-weight * value stays 0 in the PV product.
-template <int D, int RBW>
+template <int D, int RBW, bool KV8>
 __device__ __forceinline__ void pv_tile(SoftmaxState<D, RBW>& st, const float (&x)[RBW][16],
                                         float c, const unsigned char* base, uint32_t keep,
                                         bool mask_v) {
@@ -119,7 +159,7 @@ __device__ __forceinline__ void pv_tile(SoftmaxState<D, RBW>& st, const float (&
     for (int db = 0; db < DH; ++db)
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
-        vop[db][kk] = *reinterpret_cast<const bf16x8*>(base + (2 * (d0 + db) + kk) * 1024);
+        vop[db][kk] = as_operand(lds_op<KV8>(base + v_lds<D, KV8>(d0 + db, kk)));
     if (mask_v) {
 #pragma unroll
       for (int db = 0; db < DH; ++db)
@@ -165,7 +205,7 @@ __device__ __forceinline__ void anchor(T& v) { asm volatile("" : "+v"(v)); }
 // the refill for later tiles, right after the S^T MFMA of step i, where its
 // issue time overlaps that MFMA.  PV(t) takes the hi bf16 parts of the weights
 // only (the precision argument is at the fast loop in the kernel).
-template <int D, int RBW, int NLOAD, typename Dma>
+template <int D, int RBW, bool KV8, int NLOAD, typename Dma>
 __device__ __forceinline__ void fast_tile(SoftmaxState<D, RBW>& st, f32x16 (&s_acc)[RBW],
                                           const bf16x8 (&qop)[RBW][D / 16],
                                           float (&x)[RBW][16], float c,
@@ -185,10 +225,10 @@ __device__ __forceinline__ void fast_tile(SoftmaxState<D, RBW>& st, f32x16 (&s_a
     pdrop[rb] = 0.f;
   }
   uint32_t hw[RBW][8];                         // packed P^T words: key pair w of row block
-  bf16x8 kop[KS];
-  bf16x8 vop[KS];                              // V operand (db, kk) at index 2 * db + kk
+  LdsOp<KV8> kop[KS];
+  LdsOp<KV8> vop[KS];                          // V operand (db, kk) at index 2 * db + kk
 #pragma unroll
-  for (int ks = 0; ks < kAhead; ++ks) kop[ks] = *reinterpret_cast<const bf16x8*>(kbase + ks * 1024);
+  for (int ks = 0; ks < kAhead; ++ks) kop[ks] = lds_op<KV8>(kbase + k_lds<D, KV8>(ks));
 #pragma unroll
   for (int rb = 0; rb < RBW; ++rb) s_acc[rb] = f32x16{};
 #pragma unroll
@@ -211,11 +251,13 @@ __device__ __forceinline__ void fast_tile(SoftmaxState<D, RBW>& st, f32x16 (&s_a
         }
       }
     }
-    if (ks + kAhead < KS)
-      kop[ks + kAhead] = *reinterpret_cast<const bf16x8*>(kbase + (ks + kAhead) * 1024);
-    vop[ks] = *reinterpret_cast<const bf16x8*>(vbase + ks * 1024);
+    if (ks + kAhead < KS) kop[ks + kAhead] = lds_op<KV8>(kbase + k_lds<D, KV8>(ks + kAhead));
+    vop[ks] = lds_op<KV8>(vbase + v_lds<D, KV8>(ks >> 1, ks & 1));
+    {
+      const bf16x8 k = as_operand(kop[ks]);
 #pragma unroll
-    for (int rb = 0; rb < RBW; ++rb) s_acc[rb] = mfma32x32x16(kop[ks], qop[rb][ks], s_acc[rb]);
+      for (int rb = 0; rb < RBW; ++rb) s_acc[rb] = mfma32x32x16(k, qop[rb][ks], s_acc[rb]);
+    }
     if (ks < NLOAD) dma(ks);
 #pragma unroll
     for (int rb = 0; rb < RBW; ++rb) {
@@ -256,20 +298,27 @@ __device__ __forceinline__ void fast_tile(SoftmaxState<D, RBW>& st, f32x16 (&s_a
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-    for (int rb = 0; rb < RBW; ++rb)
+    for (int db = 0; db < DB; ++db) {
+      const bf16x8 v = as_operand(vop[2 * db + kk]);
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-        st.acc[rb][db] = mfma32x32x16(vop[2 * db + kk], p_hi[rb][kk], st.acc[rb][db]);
+      for (int rb = 0; rb < RBW; ++rb) st.acc[rb][db] = mfma32x32x16(v, p_hi[rb][kk], st.acc[rb][db]);
+    }
 }
 
 // TREE: the appended positions form a tree (a.tree_mask), else a causal chain.
-template <int D, int RBW, int NW, bool TREE>
+// KV8: the caches hold fp8 e4m3 codes (K's scale folded into scale_log2, V's
+// applied to the output).
+template <int D, int RBW, int NW, bool TREE, bool KV8>
 __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  constexpr int HALF = KS * 1024;        // bytes of a K (or V) half of a tile: KS 1 KB operands
-  constexpr int NH = KS / NW;            // wave loads per half tile
-  static_assert(KS % NW == 0, "operands split evenly over the waves");
+  // bytes of a K (or V) half of a tile in LDS: KS operands of 1 KB (bf16) or 512 B (fp8)
+  constexpr int HALF = KS * (KV8 ? 512 : 1024);
+  constexpr int NCH = HALF / 1024;               // 1 KB wave loads per half tile
+  constexpr int NH = (NCH + NW - 1) / NW;        // loads per half of each wave that loads
+  // every wave issues NH loads per half, or (fewer chunks than waves) none: the
+  // vmcnt waits below count NH per half
+  static_assert(NCH % NW == 0 || NCH < NW, "chunks split evenly over the loading waves");
 
   // K ring then V ring, kSlots half tiles each (160 KB at D = 256).
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kSlots * HALF];
@@ -278,6 +327,8 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int m = lane & 31;
   const int h = lane >> 5;
+  const int klane = k_lane<KV8>(lane);   // the lane's byte offset in a K / V stage operand
+  const int vlane = v_lane<KV8>(lane);
 
   int item, rg;
   if (a.nrg == 1) {
@@ -383,29 +434,41 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
   };
   auto k_slot = [&](int u) { return smem + (u % kSlots) * HALF; };
   auto v_slot = [&](int u) { return smem + (kSlots + u % kSlots) * HALF; };
+  // Bytes of tile `tile` in a cache, and the byte offset, inside it, of this
+  // lane's 16 bytes of the wave's 1 KB load number c of the K (kv = 0) or V half
+  // (bf16: operand c in MFMA lane order; fp8: the half's bytes c KB on, as stored).
+  auto tile_bytes = [&](const uint16_t* cache, size_t tile) {
+    return reinterpret_cast<const unsigned char*>(cache) + tile * (size_t)(32 * D) * (KV8 ? 1 : 2);
+  };
+  auto chunk_off = [&](int kv, int c) -> uint32_t {
+    if constexpr (KV8) return (uint32_t)(c * 1024 + lane * 16);
+    return kv == 0 ? 2u * k_operand_offset(c, m, h) : 2u * v_operand_offset<D>(c >> 1, c & 1, m, h);
+  };
   auto issue_k = [&](int u) {
     bool ok;
-    const uint16_t* kt = a.kc + page_of(u, ok) * (size_t)(32 * D);
+    const unsigned char* kt = tile_bytes(a.kc, page_of(u, ok));
     ok_tile = (ok_tile & ~(1u << (u & 31))) | ((ok ? 1u : 0u) << (u & 31));
     unsigned char* base = k_slot(u);
 #pragma unroll
     for (int i = 0; i < NH; ++i) {
-      const int op = wave + NW * i;
+      const int c = wave + NW * i;
+      if (NCH < NW && c >= NCH) break;   // wave-uniform: a wave loads NH chunks or none
       // cache policy 2 = non-temporal (the tile is read from HBM once)
-      __builtin_amdgcn_global_load_lds((void*)(kt + k_operand_offset(op, m, h)),
-                                       (__attribute__((address_space(3))) void*)(base + op * 1024),
+      __builtin_amdgcn_global_load_lds((void*)(kt + chunk_off(0, c)),
+                                       (__attribute__((address_space(3))) void*)(base + c * 1024),
                                        16, 0, 2);
     }
   };
   auto issue_v = [&](int u) {
     bool ok;
-    const uint16_t* vt = a.vc + page_of(u, ok) * (size_t)(32 * D);
+    const unsigned char* vt = tile_bytes(a.vc, page_of(u, ok));
     unsigned char* base = v_slot(u);
 #pragma unroll
     for (int i = 0; i < NH; ++i) {
-      const int op = wave + NW * i;   // V operand (op / 2, op % 2)
-      __builtin_amdgcn_global_load_lds((void*)(vt + v_operand_offset<D>(op >> 1, op & 1, m, h)),
-                                       (__attribute__((address_space(3))) void*)(base + op * 1024),
+      const int c = wave + NW * i;
+      if (NCH < NW && c >= NCH) break;
+      __builtin_amdgcn_global_load_lds((void*)(vt + chunk_off(1, c)),
+                                       (__attribute__((address_space(3))) void*)(base + c * 1024),
                                        16, 0, 2);
     }
   };
@@ -425,7 +488,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
       wait_vmcnt<0>();
     }
     lds_barrier();
-    if (any_row) s_tile<D, RBW>(s_acc, qop, k_slot(0) + lane * 16);
+    if (any_row) s_tile<D, RBW, KV8>(s_acc, qop, k_slot(0) + klane);
   }
 
   // Publish K(t+1) and V(t); then refill the freed slots (issue_for).
@@ -448,7 +511,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
     issue_for(t);
   };
   auto next_scores = [&](int t) {
-    if (any_row && t + 1 < ntile) s_tile<D, RBW>(s_acc, qop, k_slot(t + 1) + lane * 16);
+    if (any_row && t + 1 < ntile) s_tile<D, RBW, KV8>(s_acc, qop, k_slot(t + 1) + klane);
   };
 
   // Masked scores of tile t (from s_acc, which then is free) and the facts its
@@ -520,8 +583,8 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
           break;
         }
         bool ok_k, ok_v;
-        const uint16_t* kt = a.kc + page_of(t + kSlots, ok_k) * (size_t)(32 * D);
-        const uint16_t* vt = a.vc + page_of(t + kSlots - 1, ok_v) * (size_t)(32 * D);
+        const unsigned char* kt = tile_bytes(a.kc, page_of(t + kSlots, ok_k));
+        const unsigned char* vt = tile_bytes(a.vc, page_of(t + kSlots - 1, ok_v));
         {
           const int u = t + kSlots;
           ok_tile = (ok_tile & ~(1u << (u & 31))) | ((ok_k ? 1u : 0u) << (u & 31));
@@ -529,16 +592,13 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
         unsigned char* kdst = k_slot(t + kSlots);
         unsigned char* vdst = v_slot(t + kSlots - 1);
         auto dma = [&](int i) {
-          if (i < NH) {
-            const int op = wave + NW * i;
-            lds_load_async(kt, 2u * k_operand_offset(op, m, h), kdst + op * 1024);
-          } else {
-            const int op = wave + NW * (i - NH);
-            lds_load_async(vt, 2u * v_operand_offset<D>(op >> 1, op & 1, m, h), vdst + op * 1024);
-          }
+          const int kv = i < NH ? 0 : 1;
+          const int c = wave + NW * (i - kv * NH);
+          if (NCH < NW && c >= NCH) return;   // wave-uniform
+          lds_load_async(kv == 0 ? kt : vt, chunk_off(kv, c), (kv == 0 ? kdst : vdst) + c * 1024);
         };
-        fast_tile<D, RBW, 2 * NH>(st, s_acc, qop, x, a.scale_log2, k_slot(t + 1) + lane * 16,
-                                  v_slot(t) + lane * 16, dma);
+        fast_tile<D, RBW, KV8, 2 * NH>(st, s_acc, qop, x, a.scale_log2, k_slot(t + 1) + klane,
+                                       v_slot(t) + vlane, dma);
 #pragma unroll
         for (int rb = 0; rb < RBW; ++rb)
 #pragma unroll
@@ -557,7 +617,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
     next_scores(t);
     if (ok_t) {
       raise_and_rescale<D, RBW>(st, mx);
-      pv_tile<D, RBW>(st, x, a.scale_log2, v_slot(t) + lane * 16, keep, mask_v);
+      pv_tile<D, RBW, KV8>(st, x, a.scale_log2, v_slot(t) + vlane, keep, mask_v);
     }
     ++t;
   }
@@ -569,7 +629,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
     const float Ltot = sum_over_row(st.l[rb]);
     const float Lpv = Ltot - sum_over_row(st.l_drop[rb]);
     if (row >= a.R) continue;
-    const float inv = Lpv > 0.f ? 1.f / Lpv : 0.f;
+    const float inv = (Lpv > 0.f ? 1.f / Lpv : 0.f) * (KV8 ? a.v_scale : 1.f);
     float* op;
     float* lp;
     if (a.direct) {
@@ -593,9 +653,14 @@ template <int D, int RBW, int NW = kWaves>
 hipError_t launch_shared_one(const AttnArgs& a, int grid, hipStream_t stream) {
   AttnArgs arg = a;
   void* args[] = {&arg};
-  const void* k = a.tree_mask
-                      ? reinterpret_cast<const void*>(&attn_shared_kernel<D, RBW, NW, true>)
-                      : reinterpret_cast<const void*>(&attn_shared_kernel<D, RBW, NW, false>);
+  const void* k;
+  if (a.kv8) {   // fp8 caches: causal verify only
+    if (a.tree_mask) return hipErrorInvalidValue;
+    k = reinterpret_cast<const void*>(&attn_shared_kernel<D, RBW, NW, false, true>);
+  } else {
+    k = a.tree_mask ? reinterpret_cast<const void*>(&attn_shared_kernel<D, RBW, NW, true, false>)
+                    : reinterpret_cast<const void*>(&attn_shared_kernel<D, RBW, NW, false, false>);
+  }
   return hipLaunchKernel(k, dim3(grid), dim3(64 * NW), args, 0, stream);
 }
 

@@ -141,6 +141,21 @@ def test_verify_and_window_argument_checks():
                                    256, 16, 16, -1.0, 1.0, None)
     assert st == INVALID
 
+    def v8(**kw):
+        a = dict(n_q=8, Hq=32, Hkv=2, D=256, ks=1.0, vs=1.0, k=FAKE, ws=None, wsb=0)
+        a.update(kw)
+        return lib.wmtp_verify_attn_fp8(P(FAKE), P(a["k"]), P(FAKE), P(FAKE), P(FAKE), 1, a["n_q"],
+                                        a["Hq"], a["Hkv"], a["D"], 16, 16, 1024, a["ks"], a["vs"],
+                                        1.0, P(FAKE), None, P(a["ws"]), a["wsb"], 0, 0, None)
+    assert v8(ks=-1.0) == INVALID
+    assert v8(vs=float("inf")) == INVALID
+    assert v8(k=None) == INVALID
+    assert v8(k=FAKE + 8) == INVALID                  # misaligned cache
+    assert v8(D=96) == UNSUPPORTED
+    assert v8(n_q=17) == UNSUPPORTED                  # 272 query rows per kv head
+    assert v8() == WORKSPACE                          # 128 rows: the shared kernel, partials
+    assert v8(n_q=2, Hq=16) == WORKSPACE              # 16 rows: the split kernel, partials
+
 
 def test_paged_window_argument_checks():
     lib = _lib()

@@ -81,8 +81,9 @@ def test_ctx1m_draft_chain_and_verify_full_size():
 
 def test_ctx1m_next_rows_full_size():
     """The widened rows at 1M: the truncated paged index, the fp8 draft KV, the
-    draft context pass over a ring with slack (also fused with its append) and the
-    tree verify, each in its automatic split plan, checked on kv head 1's rows."""
+    draft context pass over a ring with slack (also fused with its append), the
+    tree verify and the verify over fp8 target KV, each in its automatic split
+    plan, checked on kv head 1's rows (the verifies on kv head 0's)."""
     import long_context_decode_attention_amd as lib
     from long_context_decode_attention_amd import scenario as scn
     from oracle import fp8 as F
@@ -161,3 +162,19 @@ def test_ctx1m_next_rows_full_size():
         ro, rl = OA.draft_over(qg, Kg, Vg, rows.astype(np.int64), 1.0)
         compare(o[0, i, :G], l[0, i, :G], ro, rl, f"tree verify 1M query {i}")
         _say(f"tree verify query {i} matches")
+    # the causal verify over the same target KV as fp8 codes, on the same pages
+    k8, v8 = lib.new_paged_cache_fp8(vs.kv.k.shape[0], Hkv, D)
+    for lo in range(0, Lt, 1 << 16):
+        hi = min(Lt, lo + (1 << 16))
+        lib.paged_append_fp8(k8, v8, vs.kv.block_table, dev_i32([lo]), dev_bf16(vs.K[0][lo:hi][None]),
+                             dev_bf16(vs.V[0][lo:hi][None]))
+    o8, l8 = lib.verify_attn_fp8(dev_bf16(vs.q), k8, v8, vs.kv.block_table, dev_i32([Lt]), Lt)
+    torch().cuda.synchronize()
+    _say("fp8 verify done; oracle on kv head 0 over the dequantized KV")
+    qg, Kg, Vg = _group(vs.q[0], vs.K[0], vs.V[0], 0, G)
+    Kq = F.dequantize_e4m3(F.bf16_to_e4m3(Kg[:Lt]))
+    Vq = F.dequantize_e4m3(F.bf16_to_e4m3(Vg[:Lt]))
+    for i in (0, n_q - 1):
+        ro, rl = OA.draft_full(qg[i], Kq, Vq, S + i + 1, 1.0)
+        compare(o8[0, i, :G], l8[0, i, :G], ro, rl, f"fp8 verify 1M query {i}")
+        _say(f"fp8 verify query {i} matches")

@@ -715,11 +715,12 @@ def test_error_codes():
 
 def _fp8_case(cfg_name, seed, S, k_scale, v_scale, perm=True):
     """A paged fp8 draft cache holding positions 0 .. S-1 of the seeded draft K/V,
-    written by the fp8 append in a few calls; returns what the tests need."""
+    written by the fp8 append in a few calls; returns what the tests need.
+    cfg_name is a workload name or a dict with Hq, Hkv and D."""
     from oracle import fp8 as F
     from long_context_decode_attention_amd import scenario as scn
     lib = _lib()
-    cfg = CFG[cfg_name]
+    cfg = cfg_name if isinstance(cfg_name, dict) else CFG[cfg_name]
     Hkv, D = cfg["Hkv"], cfg["D"]
     K = W.kv_positions(seed, "draft_k", 0, 0, S, Hkv, D)
     V = W.kv_positions(seed, "draft_v", 0, 0, S, Hkv, D)
@@ -795,6 +796,36 @@ def test_fp8_draft_full_and_window(cfg_name, S, k_scale, v_scale, num_splits):
         oc, lc = lib.split_combine(po, pl, 1, cfg["Hkv"], G, 1, splits_per_group=splits)
         torch().cuda.synchronize()
         assert torch().equal(oc.view(o.shape), o) and torch().equal(lc.view(l.shape), l)
+
+
+D64 = dict(Hq=16, Hkv=2, D=64)   # head dim 64: fewer 1 KB tile chunks than waves in the fp8 verify
+
+
+@pytest.mark.parametrize("cfg_name,S,n_q,k_scale,v_scale,num_splits", [
+    ("ctx1m_g32x2_d256", 20000, 8, 1.0, 1.0, 1),       # 128 rows, one split of 625 tiles
+    ("ctx1m_g32x2_d256", 9000, 8, 0.5, 2.0, 0),
+    ("nope8l_1m_g64x2_d128", 12000, 8, 1.0, 1.0, 2),   # 256 rows: eight waves
+    ("ctx128k_g32x4_d128", 15000, 8, 0.25, 0.5, 2),    # 64 rows: two row blocks per wave
+    ("ctx8k_g16x2_d128", 3000, 4, 1.0, 1.0, 0),        # 32 rows: the split kernel
+    (D64, 7000, 8, 1.0, 1.0, 1),                       # 64 rows at D = 64
+    ("ctx1m_g32x2_d256", 100, 8, 1.0, 1.0, 0),         # short: a masked tail over NaN codes
+    ("ctx1m_g32x2_d256", 0, 8, 1.0, 1.0, 0),           # the proposed positions only
+])
+def test_fp8_verify(cfg_name, S, n_q, k_scale, v_scale, num_splits):
+    """The causal verify over fp8 target caches against the oracle's verify over the
+    dequantized keys and values (slots past the sequence hold NaN codes)."""
+    lib = _lib()
+    L = S + n_q
+    c = _fp8_case(cfg_name, 93 + S % 11, L, k_scale, v_scale)
+    cfg = c["cfg"]
+    q = W.queries(94 + S % 5, "q_verify", (1, n_q, cfg["Hq"]), cfg["D"])
+    o, l = lib.verify_attn_fp8(dev_bf16(q), c["k8"], c["v8"], c["bt"], dev_i32([L]), L, k_scale,
+                               v_scale, 1.0, num_splits=num_splits)
+    torch().cuda.synchronize()
+    ro, rl = OA.verify(q[0], c["Kq"], c["Vq"], L, 1.0)
+    err, lerr = compare(o[0], l[0], ro, rl, f"fp8 verify S={S} n_q={n_q}")
+    print(f"fp8 verify D={cfg['D']} rows={n_q * cfg['Hq'] // cfg['Hkv']} S={S}: "
+          f"max|o err| {err:.2e}, max|lse err| {lerr:.2e}")
 
 
 def test_draft_context_pass_batch_of_two():
