@@ -73,14 +73,16 @@ __device__ __forceinline__ float sum_over_row(float v) { return v + __shfl_xor(v
 
 // Eight fp8 e4m3 values (bytes 0..7 of r, element j = byte j) as the bf16 MFMA
 // operand of the same element order.  Every e4m3 value is a bf16 value, so the
-// conversion (hardware fp8 -> fp32, then the high halves) is exact.
+// conversion is exact: gfx950 widens two fp8 bytes to two packed bf16 in one
+// instruction (scale 1, so nothing is rounded).
 __device__ __forceinline__ bf16x8 fp8x8_to_bf16(u32x2 r) {
-  const auto f0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)r.x, false);
-  const auto f1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)r.x, true);
-  const auto f2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)r.y, false);
-  const auto f3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)r.y, true);
-  return __builtin_bit_cast(bf16x8, u32x4{pack_bf16x2(f0[0], f0[1]), pack_bf16x2(f1[0], f1[1]),
-                                          pack_bf16x2(f2[0], f2[1]), pack_bf16x2(f3[0], f3[1])});
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 h0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.x, 1.0f, false);
+  const bf16x2 h1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.x, 1.0f, true);
+  const bf16x2 h2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.y, 1.0f, false);
+  const bf16x2 h3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.y, 1.0f, true);
+  return __builtin_bit_cast(bf16x8, u32x4{__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1),
+                                          __builtin_bit_cast(uint32_t, h2), __builtin_bit_cast(uint32_t, h3)});
 }
 __device__ __forceinline__ bf16x8 as_operand(bf16x8 v) { return v; }
 __device__ __forceinline__ bf16x8 as_operand(u32x2 r) { return fp8x8_to_bf16(r); }
