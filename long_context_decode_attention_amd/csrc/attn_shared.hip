@@ -453,10 +453,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
     for (int i = 0; i < NH; ++i) {
       const int c = wave + NW * i;
       if (NCH < NW && c >= NCH) break;   // wave-uniform: a wave loads NH chunks or none
-      // cache policy 2 = non-temporal (the tile is read from HBM once)
-      __builtin_amdgcn_global_load_lds((void*)(kt + chunk_off(0, c)),
-                                       (__attribute__((address_space(3))) void*)(base + c * 1024),
-                                       16, 0, 2);
+      lds_load_async(kt, chunk_off(0, c), base + c * 1024);
     }
   };
   auto issue_v = [&](int u) {
@@ -467,9 +464,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
     for (int i = 0; i < NH; ++i) {
       const int c = wave + NW * i;
       if (NCH < NW && c >= NCH) break;
-      __builtin_amdgcn_global_load_lds((void*)(vt + chunk_off(1, c)),
-                                       (__attribute__((address_space(3))) void*)(base + c * 1024),
-                                       16, 0, 2);
+      lds_load_async(vt, chunk_off(1, c), base + c * 1024);
     }
   };
 
