@@ -67,9 +67,18 @@ __device__ __forceinline__ uint32_t keys_below(int count, int h) {
   return b0 | (b1 << 8);
 }
 
-// Max / sum over the two lanes of a row (n and n + 32).
-__device__ __forceinline__ float max_over_row(float v) { return fmaxf(v, __shfl_xor(v, 32)); }
-__device__ __forceinline__ float sum_over_row(float v) { return v + __shfl_xor(v, 32); }
+// Max / sum over the two lanes of a row (n and n + 32).  v_permlane32_swap of v
+// with itself leaves lanes n and n + 32 holding (v[n], v[n]) in the first result
+// and (v[n + 32], v[n + 32]) in the second, so one swap and one VALU operation
+// combine the pair in every lane, with no LDS round trip.
+__device__ __forceinline__ float max_over_row(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_over_row(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // Eight fp8 e4m3 values (bytes 0..7 of r, element j = byte j) as the bf16 MFMA
 // operand of the same element order.  Every e4m3 value is a bf16 value, so the

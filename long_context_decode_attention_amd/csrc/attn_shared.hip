@@ -62,21 +62,37 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_barrier" ::: "memory");
 }
 
-// One 1 KB global-to-LDS load (global_load_lds_dwordx4, non-temporal): lane i's
-// 16 bytes at base + voff (base wave-uniform, voff the lane's byte offset) land
-// at dst + 16 * i.  Written as inline asm because the
+// N 1 KB global-to-LDS loads (global_load_lds_dwordx4, non-temporal) under one
+// M0: load j takes lane i's 16 bytes at base + voff + 1024 j (base wave-uniform,
+// voff the lane's byte offset) to dst + 1024 j + 16 i.  The instruction's
+// immediate offset moves the global address and the LDS address alike, so one
+// M0 value serves the run; the compiler is told M0 is overwritten, and sets it
+// again itself where it needs it.  Written as inline asm because the
 // compiler treats the builtin as an LDS write that may alias every LDS read in
-// flight and waits for all of them first; the slots refilled here are never
-// read while their loads are outstanding (a barrier separates the last read of
-// a slot from its refill, and the explicit vmcnt waits plus a barrier its
-// refill from the next read), so no such wait is needed.  The load is counted
-// in vmcnt like any other, which the explicit waits below account for.
-__device__ __forceinline__ void lds_load_async(const void* base, uint32_t voff, unsigned char* dst) {
+// flight and, with one anywhere in the kernel, drains all LDS reads at every
+// LDS wait; the slots refilled here are never read while their loads are
+// outstanding (a barrier separates the last read of a slot from its refill,
+// and the explicit vmcnt waits plus a barrier its refill from the next read),
+// so no such wait is needed.  The loads are counted in vmcnt like any other,
+// which the explicit waits below account for.
+template <int N>
+__device__ __forceinline__ void lds_load_run(const void* base, uint32_t voff, unsigned char* dst) {
+  static_assert(N == 1 || N == 2 || N == 4, "runs of 1, 2 or 4 loads");
   const unsigned m0 = (unsigned)(size_t)((__attribute__((address_space(3))) unsigned char*)dst);
-  unsigned saved;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
-               "global_load_lds_dwordx4 %1, %2 nt\n\ts_mov_b32 m0, %0"
-               : "=&s"(saved) : "v"(voff), "s"(base), "s"(m0) : "memory");
+  if constexpr (N == 1) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+                 :: "v"(voff), "s"(base), "s"(m0) : "memory", "m0");
+  } else if constexpr (N == 2) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt\n\t"
+                 "global_load_lds_dwordx4 %0, %1 offset:1024 nt"
+                 :: "v"(voff), "s"(base), "s"(m0) : "memory", "m0");
+  } else {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt\n\t"
+                 "global_load_lds_dwordx4 %0, %1 offset:1024 nt\n\t"
+                 "global_load_lds_dwordx4 %0, %1 offset:2048 nt\n\t"
+                 "global_load_lds_dwordx4 %0, %1 offset:3072 nt"
+                 :: "v"(voff), "s"(base), "s"(m0) : "memory", "m0");
+  }
 }
 
 // Compiler-level fence for memory operations: LDS reads after it are not hoisted
@@ -94,13 +110,14 @@ __device__ __forceinline__ LdsOp<KV8> lds_op(const unsigned char* p) {
 
 // LDS byte offsets, inside a stage, of K operand ks and of V^T operand (db, kk),
 // without the lane's own offset (k_lane / v_lane).  bf16: each operand is a
-// 1 KB block in MFMA lane order.  fp8: the stage holds the tile's bytes as in
-// memory, so the offsets are the tile's element offsets.
+// 1 KB block in MFMA lane order, the blocks in the order the tile holds them
+// in memory (K by ks, V^T by kk and then db).  fp8: the stage holds the tile's
+// bytes as in memory, so the offsets are the tile's element offsets.
 template <int D, bool KV8>
 __device__ __forceinline__ int k_lds(int ks) { return KV8 ? ks * 512 : ks * 1024; }
 template <int D, bool KV8>
 __device__ __forceinline__ int v_lds(int db, int kk) {
-  return KV8 ? kk * (16 * D) + db * 512 : (2 * db + kk) * 1024;
+  return KV8 ? kk * (16 * D) + db * 512 : (kk * (D / 32) + db) * 1024;
 }
 template <bool KV8>
 __device__ __forceinline__ int k_lane(int lane) {
@@ -201,11 +218,11 @@ __device__ __forceinline__ void anchor(T& v) { asm volatile("" : "+v"(v)); }
 // VALU executes while the matrix core runs the MFMA; anchors at every step keep
 // that order.  K operand reads run four steps ahead of their MFMAs and the V
 // operand reads are spread over the same steps, so PV(t) finds them in
-// registers.  dma(i), i < NLOAD, issues the wave's i-th global-to-LDS load of
-// the refill for later tiles, right after the S^T MFMA of step i, where its
-// issue time overlaps that MFMA.  PV(t) takes the hi bf16 parts of the weights
-// only (the precision argument is at the fast loop in the kernel).
-template <int D, int RBW, bool KV8, int NLOAD, typename Dma>
+// registers.  dma(0) and dma(1) issue the wave's global-to-LDS loads of the K
+// and the V half of the refill for later tiles, right after the S^T MFMAs of
+// steps 0 and KS / 2.  PV(t) takes the hi bf16 parts of the weights only (the
+// precision argument is at the fast loop in the kernel).
+template <int D, int RBW, bool KV8, typename Dma>
 __device__ __forceinline__ void fast_tile(SoftmaxState<D, RBW>& st, f32x16 (&s_acc)[RBW],
                                           const bf16x8 (&qop)[RBW][D / 16],
                                           float (&x)[RBW][16], float c,
@@ -258,7 +275,8 @@ __device__ __forceinline__ void fast_tile(SoftmaxState<D, RBW>& st, f32x16 (&s_a
 #pragma unroll
       for (int rb = 0; rb < RBW; ++rb) s_acc[rb] = mfma32x32x16(k, qop[rb][ks], s_acc[rb]);
     }
-    if (ks < NLOAD) dma(ks);
+    if (ks == 0) dma(0);
+    if (ks == KS / 2) dma(1);
 #pragma unroll
     for (int rb = 0; rb < RBW; ++rb) {
 #pragma unroll
@@ -278,11 +296,6 @@ __device__ __forceinline__ void fast_tile(SoftmaxState<D, RBW>& st, f32x16 (&s_a
   }
 #pragma unroll
   for (int ks = KS - kAhead; ks < KS; ++ks) anchor(vop[ks]);
-  // The refill loads go here, where this wave has no LDS read in flight: a
-  // global-to-LDS load waits for the wave's outstanding LDS reads before it
-  // issues, which costs little only at this point.
-#pragma unroll
-  for (int i = KS; i < NLOAD; ++i) dma(i);
   bf16x8 p_hi[RBW][2];
 #pragma unroll
   for (int rb = 0; rb < RBW; ++rb) {
@@ -440,32 +453,24 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
   auto tile_bytes = [&](const uint16_t* cache, size_t tile) {
     return reinterpret_cast<const unsigned char*>(cache) + tile * (size_t)(32 * D) * (KV8 ? 1 : 2);
   };
-  auto chunk_off = [&](int kv, int c) -> uint32_t {
-    if constexpr (KV8) return (uint32_t)(c * 1024 + lane * 16);
-    return kv == 0 ? 2u * k_operand_offset(c, m, h) : 2u * v_operand_offset<D>(c >> 1, c & 1, m, h);
-  };
+  // Chunk c of a half sits at c KB in the tile's half and in the stage alike;
+  // the lane's 16 bytes sit at c KB + k_goff / v_goff in the tile (bf16: MFMA
+  // lane order; fp8: as stored) and at c KB + 16 * lane in the stage.  Wave w
+  // loads chunks NH*w .. NH*w + NH - 1 (or, with fewer chunks than waves, chunk w).
+  const uint32_t k_goff = KV8 ? (uint32_t)(lane * 16) : 2u * k_operand_offset(0, m, h);
+  const uint32_t v_goff = KV8 ? (uint32_t)(lane * 16) : 2u * v_operand_offset<D>(0, 0, m, h);
+  const bool loads = !(NCH < NW && wave >= NCH);   // wave-uniform
+  const int c0 = wave * NH;                         // the wave's first chunk
   auto issue_k = [&](int u) {
     bool ok;
     const unsigned char* kt = tile_bytes(a.kc, page_of(u, ok));
     ok_tile = (ok_tile & ~(1u << (u & 31))) | ((ok ? 1u : 0u) << (u & 31));
-    unsigned char* base = k_slot(u);
-#pragma unroll
-    for (int i = 0; i < NH; ++i) {
-      const int c = wave + NW * i;
-      if (NCH < NW && c >= NCH) break;   // wave-uniform: a wave loads NH chunks or none
-      lds_load_async(kt, chunk_off(0, c), base + c * 1024);
-    }
+    if (loads) lds_load_run<NH>(kt + c0 * 1024, k_goff, k_slot(u) + c0 * 1024);
   };
   auto issue_v = [&](int u) {
     bool ok;
     const unsigned char* vt = tile_bytes(a.vc, page_of(u, ok));
-    unsigned char* base = v_slot(u);
-#pragma unroll
-    for (int i = 0; i < NH; ++i) {
-      const int c = wave + NW * i;
-      if (NCH < NW && c >= NCH) break;
-      lds_load_async(vt, chunk_off(1, c), base + c * 1024);
-    }
+    if (loads) lds_load_run<NH>(vt + c0 * 1024, v_goff, v_slot(u) + c0 * 1024);
   };
 
   // Prologue: K(0..kSlots-1) and V(0..kSlots-2) in the order the steps would have issued them,
@@ -557,7 +562,12 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
   int t = 0;
   while (t < ntile) {
     bool synced = false;   // tile t is published, its refill not yet issued
-    if (any_row) {
+    if (any_row && t + kSlots < ntile) {
+      // Kept across the fast tiles: t % kSlots, and the tile index of the next V
+      // refill, which is the tile the previous K refill looked up.
+      int sj = t % kSlots;
+      bool ok_v;
+      size_t v_tix = page_of(t + kSlots - 1, ok_v);
       for (; t + kSlots < ntile; ++t) {
         publish(t);
         const int kb = kb0 + t;
@@ -577,23 +587,28 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
           synced = true;
           break;
         }
-        bool ok_k, ok_v;
-        const unsigned char* kt = tile_bytes(a.kc, page_of(t + kSlots, ok_k));
-        const unsigned char* vt = tile_bytes(a.vc, page_of(t + kSlots - 1, ok_v));
+        bool ok_k;
+        const size_t k_tix = page_of(t + kSlots, ok_k);
+        const unsigned char* kt = tile_bytes(a.kc, k_tix);
+        const unsigned char* vt = tile_bytes(a.vc, v_tix);
+        v_tix = k_tix;
         {
           const int u = t + kSlots;
           ok_tile = (ok_tile & ~(1u << (u & 31))) | ((ok_k ? 1u : 0u) << (u & 31));
         }
-        unsigned char* kdst = k_slot(t + kSlots);
-        unsigned char* vdst = v_slot(t + kSlots - 1);
+        // slots: K(t+kSlots) refills K(t)'s, V(t+kSlots-1) V(t-1)'s; reads K(t+1), V(t)
+        const int sj1 = sj == kSlots - 1 ? 0 : sj + 1;
+        const int sjm = sj == 0 ? kSlots - 1 : sj - 1;
+        unsigned char* kdst = smem + sj * HALF;
+        unsigned char* vdst = smem + (kSlots + sjm) * HALF;
         auto dma = [&](int i) {
-          const int kv = i < NH ? 0 : 1;
-          const int c = wave + NW * (i - kv * NH);
-          if (NCH < NW && c >= NCH) return;   // wave-uniform
-          lds_load_async(kv == 0 ? kt : vt, chunk_off(kv, c), (kv == 0 ? kdst : vdst) + c * 1024);
+          if (!loads) return;
+          if (i == 0) lds_load_run<NH>(kt + c0 * 1024, k_goff, kdst + c0 * 1024);
+          else lds_load_run<NH>(vt + c0 * 1024, v_goff, vdst + c0 * 1024);
         };
-        fast_tile<D, RBW, KV8, 2 * NH>(st, s_acc, qop, x, a.scale_log2, k_slot(t + 1) + klane,
-                                       v_slot(t) + vlane, dma);
+        fast_tile<D, RBW, KV8>(st, s_acc, qop, x, a.scale_log2, smem + sj1 * HALF + klane,
+                                       smem + (kSlots + sj) * HALF + vlane, dma);
+        sj = sj1;
 #pragma unroll
         for (int rb = 0; rb < RBW; ++rb)
 #pragma unroll
