@@ -189,9 +189,11 @@ __device__ __forceinline__ bool first_max_or_rescale(SoftmaxState<D, NB>& st,
 }
 
 // General-loop maximum update: raise where needed and rescale the row's
-// accumulators and sum by exp2(m_old - m_new).
-template <int D, int NB>
-__device__ __forceinline__ void raise_and_rescale(SoftmaxState<D, NB>& st, const float (&mx)[NB]) {
+// accumulators and sum by exp2(m_old - m_new); also(rb, alpha) rescales whatever
+// else the caller keeps in the same units.
+template <int D, int NB, typename Also>
+__device__ __forceinline__ void raise_and_rescale(SoftmaxState<D, NB>& st, const float (&mx)[NB],
+                                                  Also&& also) {
   constexpr int DB = D / 32;
 #pragma unroll
   for (int rb = 0; rb < NB; ++rb) {
@@ -208,8 +210,13 @@ __device__ __forceinline__ void raise_and_rescale(SoftmaxState<D, NB>& st, const
         st.acc[rb][db] *= alpha;
         pin_acc(st.acc[rb][db]);
       }
+      also(rb, alpha);
     }
   }
+}
+template <int D, int NB>
+__device__ __forceinline__ void raise_and_rescale(SoftmaxState<D, NB>& st, const float (&mx)[NB]) {
+  raise_and_rescale(st, mx, [](int, float) {});
 }
 
 // Weights of one row block as the P^T operands of the two PV steps.

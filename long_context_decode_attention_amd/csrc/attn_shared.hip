@@ -221,9 +221,16 @@ __device__ __forceinline__ void anchor(T& v) { asm volatile("" : "+v"(v)); }
 // registers.  dma(0) and dma(1) issue the wave's global-to-LDS loads of the K
 // and the V half of the refill for later tiles, right after the S^T MFMAs of
 // steps 0 and KS / 2.  PV(t) takes the hi bf16 parts of the weights only (the
-// precision argument is at the fast loop in the kernel).
-template <int D, int RBW, bool KV8, typename Dma>
+// precision argument is at the fast loop in the kernel).  What that leaves out
+// goes to the output's normaliser one of two ways.  HS: l_drop sums the fast
+// tiles' exact weights, and two more products with a V^T of ones sum their hi
+// parts into hs (every register of lane (n, h) holds row n's sum), two issue
+// slots instead of ~48 VALU instructions.  Otherwise l_drop sums the dropped
+// lo parts directly on the VALU (for waves that must fit half the register
+// file).
+template <int D, int RBW, bool KV8, bool HS, typename Dma>
 __device__ __forceinline__ void fast_tile(SoftmaxState<D, RBW>& st, f32x16 (&s_acc)[RBW],
+                                          f32x16 (&hs)[RBW],
                                           const bf16x8 (&qop)[RBW][D / 16],
                                           float (&x)[RBW][16], float c,
                                           const unsigned char* kbase, const unsigned char* vbase,
@@ -286,10 +293,12 @@ __device__ __forceinline__ void fast_tile(SoftmaxState<D, RBW>& st, f32x16 (&s_a
         psum[rb] += p[rb][i];
         if (i & 1) {
           const uint32_t hp = pack_bf16x2(p[rb][i - 1], p[rb][i]);
-          const float d0 = p[rb][i - 1] - __builtin_bit_cast(float, hp << 16);
-          const float d1 = p[rb][i] - __builtin_bit_cast(float, hp & 0xFFFF0000u);
           hw[rb][i >> 1] = hp;
-          pdrop[rb] += d0 + d1;
+          if constexpr (!HS) {
+            const float d0 = p[rb][i - 1] - __builtin_bit_cast(float, hp << 16);
+            const float d1 = p[rb][i] - __builtin_bit_cast(float, hp & 0xFFFF0000u);
+            pdrop[rb] += d0 + d1;
+          }
         }
       }
     }
@@ -300,14 +309,14 @@ __device__ __forceinline__ void fast_tile(SoftmaxState<D, RBW>& st, f32x16 (&s_a
 #pragma unroll
   for (int rb = 0; rb < RBW; ++rb) {
     st.l[rb] += psum[rb];
-    st.l_drop[rb] += pdrop[rb];
+    st.l_drop[rb] += HS ? psum[rb] : pdrop[rb];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
       p_hi[rb][kk] = __builtin_bit_cast(bf16x8, u32x4{hw[rb][4 * kk], hw[rb][4 * kk + 1],
                                                       hw[rb][4 * kk + 2], hw[rb][4 * kk + 3]});
   }
-  // PV(t) with the hi parts of the weights; l_drop holds what they leave out,
-  // so that the output is normalised by exactly the weights PV saw.
+  // PV(t) with the hi parts of the weights; l_drop (and hs) hold what they
+  // leave out, so that the output is normalised by exactly the weights PV saw.
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
@@ -316,6 +325,13 @@ __device__ __forceinline__ void fast_tile(SoftmaxState<D, RBW>& st, f32x16 (&s_a
 #pragma unroll
       for (int rb = 0; rb < RBW; ++rb) st.acc[rb][db] = mfma32x32x16(v, p_hi[rb][kk], st.acc[rb][db]);
     }
+  if constexpr (HS) {
+    const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int rb = 0; rb < RBW; ++rb) hs[rb] = mfma32x32x16(ones, p_hi[rb][kk], hs[rb]);
+  }
 }
 
 // TREE: the appended positions form a tree (a.tree_mask), else a causal chain.
@@ -332,6 +348,12 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
   // every wave issues NH loads per half, or (fewer chunks than waves) none: the
   // vmcnt waits below count NH per half
   static_assert(NCH % NW == 0 || NCH < NW, "chunks split evenly over the loading waves");
+
+  // The fast tiles' dropped weight parts are summed on the matrix cores (see
+  // fast_tile) unless the wave's registers are short for it: two waves per SIMD
+  // (half the register file each), or two row blocks at D = 128 (which would
+  // spill).
+  constexpr bool HS = NW <= 4 && !(D == 128 && RBW == 2);
 
   // K ring then V ring, kSlots half tiles each (160 KB at D = 256).
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kSlots * HALF];
@@ -409,6 +431,10 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) st.acc[rb][db] = f32x16{};
   }
+  // HS: hi parts of the fast tiles' weights, summed per row (any register)
+  f32x16 hs[RBW];
+#pragma unroll
+  for (int rb = 0; rb < RBW; ++rb) hs[rb] = f32x16{};
 
   // Page ids of this split (at most 256 pages): lane i of register r holds
   // logical page kb0/2 + 64*r + i, read once here so that no load other than
@@ -606,13 +632,15 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
           if (i == 0) lds_load_run<NH>(kt + c0 * 1024, k_goff, kdst + c0 * 1024);
           else lds_load_run<NH>(vt + c0 * 1024, v_goff, vdst + c0 * 1024);
         };
-        fast_tile<D, RBW, KV8>(st, s_acc, qop, x, a.scale_log2, smem + sj1 * HALF + klane,
+        fast_tile<D, RBW, KV8, HS>(st, s_acc, hs, qop, x, a.scale_log2, smem + sj1 * HALF + klane,
                                        smem + (kSlots + sj) * HALF + vlane, dma);
         sj = sj1;
 #pragma unroll
-        for (int rb = 0; rb < RBW; ++rb)
+        for (int rb = 0; rb < RBW; ++rb) {
 #pragma unroll
           for (int db = 0; db < DB; ++db) pin_acc(st.acc[rb][db]);
+          if (HS) pin_acc(hs[rb]);
+        }
       }
     }
     if (t >= ntile) break;
@@ -626,7 +654,12 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
     if (ok_t) scores_of(t);
     next_scores(t);
     if (ok_t) {
-      raise_and_rescale<D, RBW>(st, mx);
+      raise_and_rescale<D, RBW>(st, mx, [&](int rb, float alpha) {
+        if constexpr (HS) {
+          hs[rb] *= alpha;
+          pin_acc(hs[rb]);
+        }
+      });
       pv_tile<D, RBW, KV8>(st, x, a.scale_log2, v_slot(t) + vlane, keep, mask_v);
     }
     ++t;
@@ -637,7 +670,9 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
   for (int rb = 0; rb < RBW; ++rb) {
     const int row = row0 + rb * 32 + m;
     const float Ltot = sum_over_row(st.l[rb]);
-    const float Lpv = Ltot - sum_over_row(st.l_drop[rb]);
+    // the weights PV saw: all of them, less the fast tiles' dropped lo parts
+    const float Lpv = HS ? Ltot - (sum_over_row(st.l_drop[rb]) - hs[rb][0])
+                         : Ltot - sum_over_row(st.l_drop[rb]);
     if (row >= a.R) continue;
     const float inv = (Lpv > 0.f ? 1.f / Lpv : 0.f) * (KV8 ? a.v_scale : 1.f);
     float* op;
