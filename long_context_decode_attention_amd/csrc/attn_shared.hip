@@ -257,9 +257,14 @@ __device__ __forceinline__ void fast_tile(SoftmaxState<D, RBW>& st, f32x16 (&s_a
   for (int rb = 0; rb < RBW; ++rb) s_acc[rb] = f32x16{};
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    // step boundary: the previous step's results and this step's inputs
-    anchor(kop[ks]);
-    if (ks >= kAhead) anchor(vop[ks - kAhead]);
+    // step boundary: the previous step's results and this step's inputs (the K
+    // operand and the V operand read with it in one statement, so that one LDS
+    // wait covers both)
+    if (ks >= kAhead) {
+      asm volatile("" : "+v"(kop[ks]), "+v"(vop[ks - kAhead]));
+    } else {
+      anchor(kop[ks]);
+    }
 #pragma unroll
     for (int rb = 0; rb < RBW; ++rb) {
       anchor(psum[rb]);
@@ -448,6 +453,13 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
     my_page[r] = pg <= last_page ? a.block_table[(size_t)b * a.max_pages + pg] : -1;
   }
   wait_vmcnt<0>();
+  // Every page of the split inside the cache (the same for every wave): only
+  // then do tiles take the fast path, which then tracks no page validity.
+  bool pages_in = true;
+#pragma unroll
+  for (int r = 0; r < kPageRegs; ++r)
+    pages_in = pages_in && (page0 + 64 * r + lane > last_page || (unsigned)my_page[r] < (unsigned)a.num_pages);
+  const bool pages_ok = __all(pages_in);
 
   // Half tiles stream through two rings of LDS slots, K and V, filled by
   // direct global-to-LDS loads: the K half of tile u goes to K slot u % kSlots,
@@ -457,6 +469,8 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
   // V(t+kSlots-1) the slot V(t-1) left.  A page id outside the cache still issues its loads (from page
   // 0) so that every half costs the same number of loads; the tile is skipped.
   uint32_t ok_tile = 0;                 // bit u % 32: tile u has a valid page
+  // tile index of tile u, whose page the split's preloaded ids hold (ok: the page
+  // is inside the cache; else page 0 stands in)
   auto page_of = [&](int u, bool& ok) -> size_t {
     const int kb = kb0 + u;
     const int idx = (kb >> 1) - page0;   // 0 .. 64*kPageRegs - 1, wave-uniform
@@ -565,7 +579,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
       for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(x[rb][i]));
     }
   };
-  auto tile_ok = [&](int t) { return any_row && ((ok_tile >> (t & 31)) & 1u); };
+  auto tile_ok = [&](int t) { return any_row && (pages_ok || ((ok_tile >> (t & 31)) & 1u)); };
 
   // Tiles run through a fast path or a general one.  The fast path takes a tile
   // that is full (every key present and visible to every row), whose rows all
@@ -588,16 +602,16 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
   int t = 0;
   while (t < ntile) {
     bool synced = false;   // tile t is published, its refill not yet issued
-    if (any_row && t + kSlots < ntile) {
+    if (any_row && pages_ok && t + kSlots < ntile) {
       // Kept across the fast tiles: t % kSlots, and the tile index of the next V
-      // refill, which is the tile the previous K refill looked up.
+      // refill, which is the tile the previous K refill took.
       int sj = t % kSlots;
       bool ok_v;
       size_t v_tix = page_of(t + kSlots - 1, ok_v);
       for (; t + kSlots < ntile; ++t) {
         publish(t);
         const int kb = kb0 + t;
-        bool slow = !tile_ok(t) || (kb + 1) * 32 > vis_end;
+        bool slow = (kb + 1) * 32 > vis_end;
 #pragma unroll
         for (int rb = 0; rb < RBW; ++rb) {
 #pragma unroll
@@ -613,15 +627,18 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
           synced = true;
           break;
         }
-        bool ok_k;
-        const size_t k_tix = page_of(t + kSlots, ok_k);
+        // K(t+kSlots): an odd 32-key tile shares its page with the tile before
+        // it, V(t+kSlots-1), one tile on in the cache
+        size_t k_tix;
+        if ((kb + kSlots) & 1) {
+          k_tix = v_tix + 1;
+        } else {
+          bool ok_k;
+          k_tix = page_of(t + kSlots, ok_k);
+        }
         const unsigned char* kt = tile_bytes(a.kc, k_tix);
         const unsigned char* vt = tile_bytes(a.vc, v_tix);
         v_tix = k_tix;
-        {
-          const int u = t + kSlots;
-          ok_tile = (ok_tile & ~(1u << (u & 31))) | ((ok_k ? 1u : 0u) << (u & 31));
-        }
         // slots: K(t+kSlots) refills K(t)'s, V(t+kSlots-1) V(t-1)'s; reads K(t+1), V(t)
         const int sj1 = sj == kSlots - 1 ? 0 : sj + 1;
         const int sjm = sj == 0 ? kSlots - 1 : sj - 1;
