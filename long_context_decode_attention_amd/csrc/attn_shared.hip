@@ -612,16 +612,19 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
         publish(t);
         const int kb = kb0 + t;
         bool slow = (kb + 1) * 32 > vis_end;
+        // the fast path's own copy of the scores (the general path takes them
+        // from s_acc again), so that no score register is carried round the loop
+        float xf[RBW][16];
 #pragma unroll
         for (int rb = 0; rb < RBW; ++rb) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) x[rb][i] = s_acc[rb][i];
-          mx[rb] = lane_max16(x[rb]) * a.scale_log2;
+          for (int i = 0; i < 16; ++i) xf[rb][i] = s_acc[rb][i];
+          const float mxf = lane_max16(xf[rb]) * a.scale_log2;
           // m = -inf (no maximum yet) needs a raise as well
-          slow |= needs_raise(mx[rb], st.m[rb]);
+          slow |= needs_raise(mxf, st.m[rb]);
           // heavy: a weight above kHeavyWeight of the row's running sum (the
           // row's keys are split over lanes n and n + 32)
-          slow |= fast_exp2(mx[rb] - st.m[rb]) > sum_over_row(st.l[rb]) * kHeavyWeight;
+          slow |= fast_exp2(mxf - st.m[rb]) > sum_over_row(st.l[rb]) * kHeavyWeight;
         }
         if (__any(slow)) {
           synced = true;
@@ -649,7 +652,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
           if (i == 0) lds_load_run<NH>(kt + c0 * 1024, k_goff, kdst + c0 * 1024);
           else lds_load_run<NH>(vt + c0 * 1024, v_goff, vdst + c0 * 1024);
         };
-        fast_tile<D, RBW, KV8, HS>(st, s_acc, hs, qop, x, a.scale_log2, smem + sj1 * HALF + klane,
+        fast_tile<D, RBW, KV8, HS>(st, s_acc, hs, qop, xf, a.scale_log2, smem + sj1 * HALF + klane,
                                        smem + (kSlots + sj) * HALF + vlane, dma);
         sj = sj1;
 #pragma unroll
