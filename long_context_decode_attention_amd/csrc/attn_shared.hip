@@ -66,32 +66,35 @@ __device__ __forceinline__ void lds_barrier() {
 // M0: load j takes lane i's 16 bytes at base + voff + 1024 j (base wave-uniform,
 // voff the lane's byte offset) to dst + 1024 j + 16 i.  The instruction's
 // immediate offset moves the global address and the LDS address alike, so one
-// M0 value serves the run; the compiler is told M0 is overwritten, and sets it
-// again itself where it needs it.  Written as inline asm because the
-// compiler treats the builtin as an LDS write that may alias every LDS read in
-// flight and, with one anywhere in the kernel, drains all LDS reads at every
-// LDS wait; the slots refilled here are never read while their loads are
-// outstanding (a barrier separates the last read of a slot from its refill,
-// and the explicit vmcnt waits plus a barrier its refill from the next read),
-// so no such wait is needed.  The loads are counted in vmcnt like any other,
-// which the explicit waits below account for.
+// M0 value serves the run (M0 is saved and restored around it).  Written as
+// inline asm because the compiler treats the builtin as an LDS write that may
+// alias every LDS read in flight and, with one anywhere in the kernel, drains
+// all LDS reads at every LDS wait; the slots refilled here are never read while
+// their loads are outstanding (a barrier separates the last read of a slot from
+// its refill, and the explicit vmcnt waits plus a barrier its refill from the
+// next read), so no such wait is needed.  The loads are counted in vmcnt like
+// any other, which the explicit waits below account for.
 template <int N>
 __device__ __forceinline__ void lds_load_run(const void* base, uint32_t voff, unsigned char* dst) {
   static_assert(N == 1 || N == 2 || N == 4, "runs of 1, 2 or 4 loads");
   const unsigned m0 = (unsigned)(size_t)((__attribute__((address_space(3))) unsigned char*)dst);
+  unsigned saved;
   if constexpr (N == 1) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
-                 :: "v"(voff), "s"(base), "s"(m0) : "memory", "m0");
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+                 "global_load_lds_dwordx4 %1, %2 nt\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "v"(voff), "s"(base), "s"(m0) : "memory");
   } else if constexpr (N == 2) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt\n\t"
-                 "global_load_lds_dwordx4 %0, %1 offset:1024 nt"
-                 :: "v"(voff), "s"(base), "s"(m0) : "memory", "m0");
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+                 "global_load_lds_dwordx4 %1, %2 nt\n\t"
+                 "global_load_lds_dwordx4 %1, %2 offset:1024 nt\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "v"(voff), "s"(base), "s"(m0) : "memory");
   } else {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt\n\t"
-                 "global_load_lds_dwordx4 %0, %1 offset:1024 nt\n\t"
-                 "global_load_lds_dwordx4 %0, %1 offset:2048 nt\n\t"
-                 "global_load_lds_dwordx4 %0, %1 offset:3072 nt"
-                 :: "v"(voff), "s"(base), "s"(m0) : "memory", "m0");
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+                 "global_load_lds_dwordx4 %1, %2 nt\n\t"
+                 "global_load_lds_dwordx4 %1, %2 offset:1024 nt\n\t"
+                 "global_load_lds_dwordx4 %1, %2 offset:2048 nt\n\t"
+                 "global_load_lds_dwordx4 %1, %2 offset:3072 nt\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "v"(voff), "s"(base), "s"(m0) : "memory");
   }
 }
 
