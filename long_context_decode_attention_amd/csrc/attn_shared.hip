@@ -225,15 +225,17 @@ __device__ __forceinline__ void anchor(T& v) { asm volatile("" : "+v"(v)); }
 // and the V half of the refill for later tiles, right after the S^T MFMAs of
 // steps 0 and KS / 2.  PV(t) takes the hi bf16 parts of the weights only (the
 // precision argument is at the fast loop in the kernel).  What that leaves out
-// goes to the output's normaliser one of two ways.  HS: l_drop sums the fast
-// tiles' exact weights, and two more products with a V^T of ones sum their hi
-// parts into hs (every register of lane (n, h) holds row n's sum), two issue
-// slots instead of ~48 VALU instructions.  Otherwise l_drop sums the dropped
-// lo parts directly on the VALU (for waves that must fit half the register
-// file).
-template <int D, int RBW, bool KV8, bool HS, typename Dma>
+// goes to the output's normaliser in one of three ways (DROP).  kDropMfma:
+// l_drop sums the fast tiles' exact weights, and two more products with a V^T
+// of ones sum their hi parts into hs (every register of lane (n, h) holds row
+// n's sum), two issue slots.  kDropDot: l_drop as there, and a bf16 dot
+// product with (1, 1) adds each pair of hi parts to hsd (this lane's share):
+// one VALU instruction per pair and no registers.  kDropLo: l_drop sums the
+// dropped lo parts on the VALU (six instructions per pair).
+constexpr int kDropLo = 0, kDropMfma = 1, kDropDot = 2;
+template <int D, int RBW, bool KV8, int DROP, typename Dma>
 __device__ __forceinline__ void fast_tile(SoftmaxState<D, RBW>& st, f32x16 (&s_acc)[RBW],
-                                          f32x16 (&hs)[RBW],
+                                          f32x16 (&hs)[RBW], float (&hsd)[RBW],
                                           const bf16x8 (&qop)[RBW][D / 16],
                                           float (&x)[RBW][16], float c,
                                           const unsigned char* kbase, const unsigned char* vbase,
@@ -302,10 +304,15 @@ __device__ __forceinline__ void fast_tile(SoftmaxState<D, RBW>& st, f32x16 (&s_a
         if (i & 1) {
           const uint32_t hp = pack_bf16x2(p[rb][i - 1], p[rb][i]);
           hw[rb][i >> 1] = hp;
-          if constexpr (!HS) {
+          if constexpr (DROP == kDropLo) {
             const float d0 = p[rb][i - 1] - __builtin_bit_cast(float, hp << 16);
             const float d1 = p[rb][i] - __builtin_bit_cast(float, hp & 0xFFFF0000u);
             pdrop[rb] += d0 + d1;
+          } else if constexpr (DROP == kDropDot) {
+            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+            const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+            hsd[rb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, hp), ones, hsd[rb],
+                                                       false);
           }
         }
       }
@@ -317,7 +324,7 @@ __device__ __forceinline__ void fast_tile(SoftmaxState<D, RBW>& st, f32x16 (&s_a
 #pragma unroll
   for (int rb = 0; rb < RBW; ++rb) {
     st.l[rb] += psum[rb];
-    st.l_drop[rb] += HS ? psum[rb] : pdrop[rb];
+    st.l_drop[rb] += DROP == kDropLo ? pdrop[rb] : psum[rb];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
       p_hi[rb][kk] = __builtin_bit_cast(bf16x8, u32x4{hw[rb][4 * kk], hw[rb][4 * kk + 1],
@@ -333,7 +340,7 @@ __device__ __forceinline__ void fast_tile(SoftmaxState<D, RBW>& st, f32x16 (&s_a
 #pragma unroll
       for (int rb = 0; rb < RBW; ++rb) st.acc[rb][db] = mfma32x32x16(v, p_hi[rb][kk], st.acc[rb][db]);
     }
-  if constexpr (HS) {
+  if constexpr (DROP == kDropMfma) {
     const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
@@ -357,11 +364,14 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
   // vmcnt waits below count NH per half
   static_assert(NCH % NW == 0 || NCH < NW, "chunks split evenly over the loading waves");
 
-  // The fast tiles' dropped weight parts are summed on the matrix cores (see
-  // fast_tile) unless the wave's registers are short for it: two waves per SIMD
-  // (half the register file each), or two row blocks at D = 128 (which would
-  // spill).
-  constexpr bool HS = NW <= 4 && !(D == 128 && RBW == 2);
+  // How the fast tiles' hi weight parts are summed (see fast_tile): on the
+  // matrix cores where a wave has the registers for the sums, else by bf16 dot
+  // products on the VALU.
+#ifndef WMTP_SHARED_DROP
+  constexpr int DROP = (NW <= 4 && !(D == 128 && RBW == 2)) ? kDropMfma : kDropDot;
+#else
+  constexpr int DROP = WMTP_SHARED_DROP;
+#endif
 
   // K ring then V ring, kSlots half tiles each (160 KB at D = 256).
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kSlots * HALF];
@@ -439,10 +449,15 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) st.acc[rb][db] = f32x16{};
   }
-  // HS: hi parts of the fast tiles' weights, summed per row (any register)
+  // hi parts of the fast tiles' weights: summed per row (kDropMfma: any
+  // register) or this lane's share (kDropDot)
   f32x16 hs[RBW];
+  float hsd[RBW];
 #pragma unroll
-  for (int rb = 0; rb < RBW; ++rb) hs[rb] = f32x16{};
+  for (int rb = 0; rb < RBW; ++rb) {
+    hs[rb] = f32x16{};
+    hsd[rb] = 0.f;
+  }
 
   // Page ids of this split (at most 256 pages): lane i of register r holds
   // logical page kb0/2 + 64*r + i, read once here so that no load other than
@@ -655,14 +670,14 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
           if (i == 0) lds_load_run<NH>(kt + c0 * 1024, k_goff, kdst + c0 * 1024);
           else lds_load_run<NH>(vt + c0 * 1024, v_goff, vdst + c0 * 1024);
         };
-        fast_tile<D, RBW, KV8, HS>(st, s_acc, hs, qop, xf, a.scale_log2, smem + sj1 * HALF + klane,
+        fast_tile<D, RBW, KV8, DROP>(st, s_acc, hs, hsd, qop, xf, a.scale_log2, smem + sj1 * HALF + klane,
                                        smem + (kSlots + sj) * HALF + vlane, dma);
         sj = sj1;
 #pragma unroll
         for (int rb = 0; rb < RBW; ++rb) {
 #pragma unroll
           for (int db = 0; db < DB; ++db) pin_acc(st.acc[rb][db]);
-          if (HS) pin_acc(hs[rb]);
+          if (DROP == kDropMfma) pin_acc(hs[rb]);
         }
       }
     }
@@ -678,10 +693,11 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
     next_scores(t);
     if (ok_t) {
       raise_and_rescale<D, RBW>(st, mx, [&](int rb, float alpha) {
-        if constexpr (HS) {
+        if constexpr (DROP == kDropMfma) {
           hs[rb] *= alpha;
           pin_acc(hs[rb]);
         }
+        if constexpr (DROP == kDropDot) hsd[rb] *= alpha;
       });
       pv_tile<D, RBW, KV8>(st, x, a.scale_log2, v_slot(t) + vlane, keep, mask_v);
     }
@@ -694,8 +710,14 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
     const int row = row0 + rb * 32 + m;
     const float Ltot = sum_over_row(st.l[rb]);
     // the weights PV saw: all of them, less the fast tiles' dropped lo parts
-    const float Lpv = HS ? Ltot - (sum_over_row(st.l_drop[rb]) - hs[rb][0])
-                         : Ltot - sum_over_row(st.l_drop[rb]);
+    float Lpv;
+    if constexpr (DROP == kDropMfma) {
+      Lpv = Ltot - (sum_over_row(st.l_drop[rb]) - hs[rb][0]);
+    } else if constexpr (DROP == kDropDot) {
+      Lpv = Ltot - (sum_over_row(st.l_drop[rb]) - sum_over_row(hsd[rb]));
+    } else {
+      Lpv = Ltot - sum_over_row(st.l_drop[rb]);
+    }
     if (row >= a.R) continue;
     const float inv = (Lpv > 0.f ? 1.f / Lpv : 0.f) * (KV8 ? a.v_scale : 1.f);
     float* op;
