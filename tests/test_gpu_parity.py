@@ -443,18 +443,26 @@ def test_verify_short(S):
     _verify_case(CFG["ctx1m_g32x2_d256"], 30 + S, [S], 8)
 
 
+G64D64 = dict(Hq=64, Hkv=2, D=64)   # head dim 64, 256 rows: two row blocks per wave
+
+
 @pytest.mark.parametrize("cfg_name,S,n_q,num_splits,peak", [
     ("ctx1m_g32x2_d256", 20000, 8, 2, 1.0),
     ("ctx1m_g32x2_d256", 16000, 8, 1, 4.0),
     ("nope8l_1m_g64x2_d128", 12000, 8, 1, 1.0),
     ("ctx128k_g32x4_d128", 15000, 8, 2, 2.0),
+    (G64D64, 12000, 8, 1, 1.0),
+    (G64D64, 9000, 8, 2, 3.0),
 ])
 def test_verify_long_splits(cfg_name, S, n_q, num_splits, peak):
     """Splits of hundreds of 32-key tiles, so that most tiles take the verify's
     fast path, whose PV sees the weights rounded to bf16 (the normaliser then
-    uses the same rounded weights); plain and peaked queries (q x peak)."""
+    uses the same rounded weights); plain and peaked queries (q x peak).  The
+    shapes cover every way the fast tiles sum their hi weight parts: products
+    with a V^T of ones (head dim 256; head dim 64 with two row blocks per wave)
+    and bf16 dot products (head dim 128 with eight waves)."""
     lib = _lib()
-    cfg = CFG[cfg_name]
+    cfg = CFG[cfg_name] if isinstance(cfg_name, str) else cfg_name
     vs = VerifyScenario(cfg, 60 + S % 97, [S], n_q)
     vs.append_proposed()
     q = W.bf16_round(peak * W.bf16_to_f32(vs.q))
