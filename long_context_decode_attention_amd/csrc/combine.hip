@@ -175,11 +175,15 @@ hipError_t launch_sl(const CombineArgs& c, hipStream_t stream) {
 
 hipError_t launch_combine(const CombineArgs& c, hipStream_t stream) {
   if (c.R >= 64) {
-    // CL: a power of two dividing D / 4, the widest that gives about 512 workgroups.
+    // CL: a power of two dividing D / 4, the widest that gives about 512 workgroups
+    // and enough split lanes (256 / CL) that each lane loads its splits in one
+    // batch of kMergeUnroll (one memory round trip instead of several).
     const long pairs = (long)c.B * c.Hkv * c.R;
+    const int splits = c.indptr ? 64 : c.splits_per_group;
     int CL = 4;
     while (CL < 64 && (c.D / 4) % (2 * CL) == 0) CL *= 2;
     while (CL > 4 && pairs * (c.D / (4 * CL)) < 512) CL /= 2;
+    while (CL > 4 && (256 / CL) * kMergeUnroll < splits) CL /= 2;
     CombineArgs arg = c;
     int cl_arg = CL;
     void* args[] = {&arg, &cl_arg};
