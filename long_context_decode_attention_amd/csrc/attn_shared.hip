@@ -1,22 +1,24 @@
 // Split-KV attention for many query rows per kv head (the verify of n_q
 // proposed positions: n_q * G rows), with every K/V tile shared by all rows.
 //
-// One workgroup (NW = 4 waves, one per SIMD, each with the whole register file)
-// owns one key split of one (sequence, kv head) pair and up to 32 * RBW * NW
-// query rows; wave w owns rows [32*RBW*NW*rg + 32*RBW*w, +32*RBW), so every K/V
-// operand read from LDS feeds RBW row blocks.
+// One workgroup (NW = 4 waves, one per SIMD, each with the whole register file;
+// or NW = 8, two per SIMD, at head dim 128 with more than 128 rows) owns one key
+// split of one (sequence, kv head) pair and up to 32 * RBW * NW query rows; wave
+// w owns rows [32*RBW*NW*rg + 32*RBW*w, +32*RBW), so every K/V operand read from
+// LDS feeds RBW row blocks.
 //
-// The 32-key tiles of the split stream through a ring of 4 LDS stages, filled by
-// direct global-to-LDS loads (global_load_lds_dwordx4, non-temporal): each of the
-// tile's D/16 K operands and D/16 V^T operands is one 1 KB wave load that lands
-// in LDS in exactly the lane order the MFMA reads it back.
+// The K and V halves of the split's 32-key tiles stream through two rings of
+// kSlots LDS slots, filled by direct global-to-LDS loads (global_load_lds_dwordx4,
+// non-temporal): each of a half's D/16 operands is one 1 KB block in the lane
+// order the MFMA reads it back, the blocks in the order the tile holds them in
+// memory, so that a wave loads its share of a half as one run of loads.
 //
 // The loop is software-pipelined across tiles.  Iteration t issues the S^T
 // products of tile t+1 first; they run on the matrix cores while the VALU does
-// the softmax of tile t, whose PV products follow.  Tiles t and t+1 are resident
-// in LDS while tiles t+2 and t+3 are in flight; one barrier per iteration both
-// publishes tile t+1 and frees the stage of tile t-1, which the loads of tile
-// t+3 overwrite.
+// the softmax of tile t, whose PV products follow.  K(t+1) and V(t) are resident
+// while the next kSlots - 1 halves of each ring are in flight; one barrier per
+// iteration both publishes K(t+1), V(t) and frees the slots of K(t) and V(t-1),
+// which the refill (K(t+kSlots), V(t+kSlots-1)) overwrites.
 //
 // The per-tile math is the one of attn.hip (MFMA 32x32x16, online softmax with
 // P as bf16 hi + lo parts); a wave's rows never meet another wave's, so each
