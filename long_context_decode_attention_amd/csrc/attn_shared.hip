@@ -42,7 +42,7 @@ namespace {
 constexpr int kSlots = 5;       // LDS slots per ring (K, V): one resident, four in flight
 constexpr int kPageRegs = 4;   // page ids preloaded per split: 64 per register
 // A tile in which some weight exceeds this fraction of its row's running sum is
-// heavy and goes to the general path (see the kernel).
+// heavy: PV takes the hi and lo parts of its weights (see the kernel).
 constexpr float kHeavyWeight = 1.0f / 32.0f;
 
 // An MFMA operand as it sits in LDS: 16 bytes of bf16, or 8 bytes of fp8 codes.
@@ -160,20 +160,48 @@ __device__ __forceinline__ void pv_tile(SoftmaxState<D, RBW>& st, const float (&
 // registers.  dma(0) and dma(1) issue the wave's global-to-LDS loads of the K
 // and the V half of the refill for later tiles, right after the S^T MFMAs of
 // steps 0 and KS / 2.  PV(t) takes the hi bf16 parts of the weights only (the
-// precision argument is at the fast loop in the kernel).  What that leaves out
+// precision argument is at the fast loop in the kernel), unless keep_lo (a
+// heavy tile) adds the lo parts' products after them.  What hi alone leaves out
 // goes to the output's normaliser in one of three ways (DROP).  kDropMfma:
 // l_drop sums the fast tiles' exact weights, and two more products with a V^T
 // of ones sum their hi parts into hs (every register of lane (n, h) holds row
 // n's sum), two issue slots.  kDropDot: l_drop as there, and a bf16 dot
 // product with (1, 1) adds each pair of hi parts to hsd (this lane's share):
 // one VALU instruction per pair and no registers.  kDropLo: l_drop sums the
-// dropped lo parts on the VALU (six instructions per pair).
+// dropped lo parts on the VALU (six instructions per pair).  The tile ends with
+// the check of tile t+1 (copy_and_check), VALU work beside the PV products.
 constexpr int kDropLo = 0, kDropMfma = 1, kDropDot = 2;
+
+// Copies a tile's scores out of s_acc into x and checks this lane's rows:
+// raise, a score above the running maximum by more than the lazy margin (or
+// no maximum yet), which bars the tile from the fast path; heavy, a weight
+// above kHeavyWeight of the row's running sum (the row's keys are split over
+// lanes n and n + 32), which makes the fast tile keep the weights' lo parts.
+template <int D, int RBW>
+__device__ __forceinline__ void copy_and_check(const SoftmaxState<D, RBW>& st,
+                                               const f32x16 (&s_acc)[RBW], float (&x)[RBW][16],
+                                               float c, bool& raise, bool& heavy) {
+  raise = false;
+  heavy = false;
+#pragma unroll
+  for (int rb = 0; rb < RBW; ++rb) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      x[rb][i] = s_acc[rb][i];
+      asm volatile("" : "+v"(x[rb][i]));   // a vector register copy, carried as such
+    }
+    const float mxf = lane_max16(x[rb]) * c;
+    raise |= needs_raise(mxf, st.m[rb]);
+    heavy |= fast_exp2(mxf - st.m[rb]) > sum_over_row(st.l[rb]) * kHeavyWeight;
+  }
+}
+
 template <int D, int RBW, bool KV8, int DROP, typename Dma>
 __device__ __forceinline__ void fast_tile(SoftmaxState<D, RBW>& st, f32x16 (&s_acc)[RBW],
                                           f32x16 (&hs)[RBW], float (&hsd)[RBW],
                                           const bf16x8 (&qop)[RBW][D / 16],
-                                          float (&x)[RBW][16], float c,
+                                          float (&x)[RBW][16], bool keep_lo, bool& raise_next,
+                                          bool& heavy_next, float c,
                                           const unsigned char* kbase, const unsigned char* vbase,
                                           Dma&& dma) {
   constexpr int KS = D / 16;
@@ -282,6 +310,55 @@ __device__ __forceinline__ void fast_tile(SoftmaxState<D, RBW>& st, f32x16 (&s_a
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int rb = 0; rb < RBW; ++rb) hs[rb] = mfma32x32x16(ones, p_hi[rb][kk], hs[rb]);
+  }
+  // tile t+1's check, on its finished scores and tile t's running sums: VALU
+  // work beside the PV products instead of ahead of the next tile's
+  copy_and_check<D, RBW>(st, s_acc, x, c, raise_next, heavy_next);
+  if (keep_lo) {
+    // a heavy tile (wave-uniform): the lo parts of its weights as well, so that
+    // PV sees hi + lo as on the general path, and the normaliser term of the
+    // dropped parts counts them as seen (ones products or dot products of the
+    // lo parts, or l_drop less this tile's dropped parts)
+    bf16x8 p_lo[RBW][2];
+#pragma unroll
+    for (int rb = 0; rb < RBW; ++rb)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        u32x4 lw;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int w = 4 * kk + j;
+          const uint32_t hp = hw[rb][w];
+          lw[j] = pack_bf16x2(p[rb][2 * w] - __builtin_bit_cast(float, hp << 16),
+                              p[rb][2 * w + 1] - __builtin_bit_cast(float, hp & 0xFFFF0000u));
+          if constexpr (DROP == kDropDot) {
+            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+            const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+            hsd[rb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, lw[j]), ones,
+                                                       hsd[rb], false);
+          }
+        }
+        p_lo[rb][kk] = __builtin_bit_cast(bf16x8, lw);
+      }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const bf16x8 v = as_operand(vop[2 * db + kk]);
+#pragma unroll
+        for (int rb = 0; rb < RBW; ++rb) st.acc[rb][db] = mfma32x32x16(v, p_lo[rb][kk], st.acc[rb][db]);
+      }
+    if constexpr (DROP == kDropMfma) {
+      const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int rb = 0; rb < RBW; ++rb) hs[rb] = mfma32x32x16(ones, p_lo[rb][kk], hs[rb]);
+    }
+    if constexpr (DROP == kDropLo) {
+#pragma unroll
+      for (int rb = 0; rb < RBW; ++rb) st.l_drop[rb] -= pdrop[rb];
+    }
   }
 }
 
@@ -551,8 +628,10 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
   // perturbed by at most 2^-9 relative: |error| <= 2^-9 * sum_i w_i |v_i - o|
   // over the fast tiles' keys.  A heavy tile, where some weight exceeds
   // kHeavyWeight of its row's running sum (a needle, a few dominant keys, the
-  // start of a split), takes the general path, so no key that is a large share
-  // of the mass is rounded.  lse uses the exact sum.
+  // start of a split), stays on the fast path but feeds PV the hi and lo parts,
+  // as the general path does, so no key that is a large share of the mass is
+  // rounded (with scores ~N(0, 1), ~15 of a wave's 256 tiles in a split, most
+  // of them near its start).  lse uses the exact sum.
   int t = 0;
   while (t < ntile) {
     bool synced = false;   // tile t is published, its refill not yet issued
@@ -562,24 +641,16 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
       int sj = t % kSlots;
       bool ok_v;
       size_t v_tix = page_of(t + kSlots - 1, ok_v);
+      // the fast path's own copy of tile t's scores (the general path takes
+      // them from s_acc again) and its check; each fast tile leaves both for the
+      // tile after it
+      float xf[RBW][16];
+      bool raise_t, heavy_t;
+      copy_and_check<D, RBW>(st, s_acc, xf, a.scale_log2, raise_t, heavy_t);
       for (; t + kSlots < ntile; ++t) {
         publish(t);
         const int kb = kb0 + t;
-        bool slow = (kb + 1) * 32 > vis_end;
-        // the fast path's own copy of the scores (the general path takes them
-        // from s_acc again), so that no score register is carried round the loop
-        float xf[RBW][16];
-#pragma unroll
-        for (int rb = 0; rb < RBW; ++rb) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) xf[rb][i] = s_acc[rb][i];
-          const float mxf = lane_max16(xf[rb]) * a.scale_log2;
-          // m = -inf (no maximum yet) needs a raise as well
-          slow |= needs_raise(mxf, st.m[rb]);
-          // heavy: a weight above kHeavyWeight of the row's running sum (the
-          // row's keys are split over lanes n and n + 32)
-          slow |= fast_exp2(mxf - st.m[rb]) > sum_over_row(st.l[rb]) * kHeavyWeight;
-        }
+        const bool slow = raise_t || (kb + 1) * 32 > vis_end;
         if (__any(slow)) {
           synced = true;
           break;
@@ -606,8 +677,10 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_shared_kernel(AttnArgs a) {
           if (i == 0) lds_load_run<NH>(kt + c0 * 1024, k_goff, kdst + c0 * 1024);
           else lds_load_run<NH>(vt + c0 * 1024, v_goff, vdst + c0 * 1024);
         };
-        fast_tile<D, RBW, KV8, DROP>(st, s_acc, hs, hsd, qop, xf, a.scale_log2, smem + sj1 * HALF + klane,
-                                       smem + (kSlots + sj) * HALF + vlane, dma);
+        const bool keep_lo = __any(heavy_t);
+        fast_tile<D, RBW, KV8, DROP>(st, s_acc, hs, hsd, qop, xf, keep_lo, raise_t, heavy_t, a.scale_log2,
+                                     smem + sj1 * HALF + klane, smem + (kSlots + sj) * HALF + vlane,
+                                     dma);
         sj = sj1;
 #pragma unroll
         for (int rb = 0; rb < RBW; ++rb) {
