@@ -194,6 +194,12 @@ __device__ __forceinline__ void copy_and_check(const SoftmaxState<D, RBW>& st,
     raise |= needs_raise(mxf, st.m[rb]);
     heavy |= fast_exp2(mxf - st.m[rb]) > sum_over_row(st.l[rb]) * kHeavyWeight;
   }
+  // the flags are computed here, beside the caller's products, not sunk past
+  // the branch that follows (the compiler moves them to their first use)
+  int r = raise, hv = heavy;
+  asm volatile("" : "+v"(r), "+v"(hv));
+  raise = r != 0;
+  heavy = hv != 0;
 }
 
 template <int D, int RBW, bool KV8, int DROP, typename Dma>
