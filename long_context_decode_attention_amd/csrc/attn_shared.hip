@@ -335,13 +335,16 @@ __device__ __forceinline__ void fast_tile(SoftmaxState<D, RBW>& st, f32x16 (&s_a
         for (int j = 0; j < 4; ++j) {
           const int w = 4 * kk + j;
           const uint32_t hp = hw[rb][w];
-          lw[j] = pack_bf16x2(p[rb][2 * w] - __builtin_bit_cast(float, hp << 16),
-                              p[rb][2 * w + 1] - __builtin_bit_cast(float, hp & 0xFFFF0000u));
+          // a scalar, not the vector element: bit-casting lw[j] itself made the
+          // compiler read element 0 for every j
+          const uint32_t lp = pack_bf16x2(p[rb][2 * w] - __builtin_bit_cast(float, hp << 16),
+                                          p[rb][2 * w + 1] - __builtin_bit_cast(float, hp & 0xFFFF0000u));
+          lw[j] = lp;
           if constexpr (DROP == kDropDot) {
             typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
             const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-            hsd[rb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, lw[j]), ones,
-                                                       hsd[rb], false);
+            hsd[rb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, lp), ones, hsd[rb],
+                                                       false);
           }
         }
         p_lo[rb][kk] = __builtin_bit_cast(bf16x8, lw);

@@ -518,6 +518,56 @@ def test_verify_long_split_wide_values(cfg_name, S, num_splits):
 
 
 @pytest.mark.parametrize("cfg_name,S,num_splits", [
+    ("ctx1m_g32x2_d256", 24000, 1),          # four waves, hi parts summed by products
+    ("nope8l_1m_g64x2_d128", 16000, 1),      # eight waves, hi parts summed by dot products
+])
+def test_verify_every_tile_heavy(cfg_name, S, num_splits):
+    """Every 32-key tile holds one key whose weight is ~5 % of its row's running
+    sum (its score grows by 0.05 per tile, staying inside the lazy margin of the
+    split's first maximum), so every fast tile is heavy and keeps its weights' lo
+    parts.  The result must then carry the hi + lo precision: well below the error
+    that bf16-rounded weights alone give on the same input, computed here."""
+    cfg = CFG[cfg_name]
+    n_q, Hq, Hkv, D = 8, cfg["Hq"], cfg["Hkv"], cfg["D"]
+    L = S + n_q
+    rng = np.random.default_rng(93)
+    # every query row ~ u = 1/16 per component (plus noise): a key c * 1 scores
+    # ~ c * D / 16
+    qf = 0.0625 + 0.01 * rng.standard_normal((1, n_q, Hq, D))
+    q = W.bf16_round(qf.astype(np.float32))
+    Kf = 0.25 * rng.standard_normal((L, Hkv, D))
+    for n in range(S // 32):
+        beta = 4.0 + 0.05 * n                 # the spike's score, in nats
+        Kf[32 * n + (7 * n) % 32] = beta / (0.0625 * D)
+    K = W.bf16_round(Kf.astype(np.float32))
+    V = W.bf16_round(rng.standard_normal((L, Hkv, D)).astype(np.float32))
+    o, l, ro, rl = _verify_custom(cfg_name, 93, S, n_q, K, V, q, num_splits)
+    got = o.double().cpu().numpy().reshape(ro.shape)
+    err = float(np.max(np.abs(got - ro)))
+    lerr = float(np.max(np.abs(l.double().cpu().numpy().reshape(rl.shape) - rl)))
+    # the same rows with every weight rounded to bf16 (what PV sees without the
+    # lo parts), normalised by the rounded weights
+    Qd = W.bf16_to_f32(q).astype(np.float64)[0]
+    Kd = W.bf16_to_f32(K).astype(np.float64)
+    Vd = W.bf16_to_f32(V).astype(np.float64)
+    G = Hq // Hkv
+    hi_err = 0.0
+    for g in range(Hkv):
+        for qi in (0, n_q - 1):
+            lim = S + qi + 1                  # causal: keys up to the query's position
+            s = Qd[qi, g * G] @ Kd[:lim, g].T
+            w = np.exp(s - s.max())
+            wh = W.bf16_to_f32(W.bf16_round(w.astype(np.float32))).astype(np.float64)
+            ex = w @ Vd[:lim, g] / w.sum()
+            hi = wh @ Vd[:lim, g] / wh.sum()
+            hi_err = max(hi_err, float(np.max(np.abs(hi - ex))))
+    print(f"verify every tile heavy {cfg_name}: max|o err| {err:.2e} (bf16 weights alone: "
+          f"{hi_err:.2e}), max|lse err| {lerr:.2e}")
+    assert err <= 0.1 * hi_err
+    assert lerr <= 1e-4
+
+
+@pytest.mark.parametrize("cfg_name,S,num_splits", [
     ("ctx1m_g32x2_d256", 20000, 1),
     ("nope8l_1m_g64x2_d128", 12000, 2),
 ])
