@@ -86,8 +86,11 @@ __device__ __forceinline__ void load_k(KTile<D, RING, KV8>& t, const AttnArgs& a
     for (int ks = 0; ks < D / 16; ++ks) t.k[ks] = ld_u32x2_stream(kt + k_operand_offset(ks, m, h));
   } else {
     const uint16_t* kt = a.kc + tile * (size_t)(32 * D);
+    // a ring is read again at the next draft step: ordinary loads, so that its
+    // lines may stay in L2; a paged pass streams bytes it reads once
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) t.k[ks] = ld_bf16x8_stream(kt + k_operand_offset(ks, m, h));
+    for (int ks = 0; ks < D / 16; ++ks)
+      t.k[ks] = RING ? ld_bf16x8(kt + k_operand_offset(ks, m, h)) : ld_bf16x8_stream(kt + k_operand_offset(ks, m, h));
   }
   if constexpr (RING) {
     // slots 8h..8h+7 and 16+8h..16+8h+7 of the tile
@@ -103,7 +106,7 @@ __device__ __forceinline__ void load_k(KTile<D, RING, KV8>& t, const AttnArgs& a
   }
 }
 
-template <int D, bool KV8>
+template <int D, bool KV8, bool RING>
 __device__ __forceinline__ void load_v(VTile<D, KV8>& t, const AttnArgs& a, size_t tile, int m,
                                        int h) {
   if constexpr (KV8) {
@@ -117,7 +120,9 @@ __device__ __forceinline__ void load_v(VTile<D, KV8>& t, const AttnArgs& a, size
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) t.v[db][kk] = ld_bf16x8_stream(vt + v_operand_offset<D>(db, kk, m, h));
+      for (int kk = 0; kk < 2; ++kk)
+        t.v[db][kk] = RING ? ld_bf16x8(vt + v_operand_offset<D>(db, kk, m, h))
+                           : ld_bf16x8_stream(vt + v_operand_offset<D>(db, kk, m, h));
   }
 }
 
@@ -374,7 +379,7 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
       }
     } else {
       load_k<D, RING, KV8>(kt, a, tile, b, kbl, m, h);
-      load_v<D, KV8>(vt, a, tile, m, h);
+      load_v<D, KV8, RING>(vt, a, tile, m, h);
       asm volatile("" ::: "memory");
       if (RING) T0 = ring_count();
       stage_q();
@@ -526,7 +531,7 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
         }
       // the raw V bytes are converted: refill them now, so that the next tile's V
       // loads run under this tile's PV products
-      if constexpr (decltype(has_next)::value) load_v<D, KV8>(vt, a, tile_n, m, h);
+      if constexpr (decltype(has_next)::value) load_v<D, KV8, RING>(vt, a, tile_n, m, h);
       pv<D, NB>(st, vv, p_hi, p_lo);
     } else {
       if (mask_v) {
@@ -539,7 +544,7 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
       }
       pv<D, NB>(st, vt.v, p_hi, p_lo);
     }
-    if constexpr (!KV8 && decltype(has_next)::value) load_v<D, KV8>(vt, a, tile_n, m, h);
+    if constexpr (!KV8 && decltype(has_next)::value) load_v<D, KV8, RING>(vt, a, tile_n, m, h);
   };
   const std::true_type more;
   const std::false_type last;
