@@ -86,8 +86,10 @@ __device__ __forceinline__ void load_k(KTile<D, RING, KV8>& t, const AttnArgs& a
     for (int ks = 0; ks < D / 16; ++ks) t.k[ks] = ld_u32x2_stream(kt + k_operand_offset(ks, m, h));
   } else {
     const uint16_t* kt = a.kc + tile * (size_t)(32 * D);
-    // a ring is read again at the next draft step: ordinary loads, so that its
-    // lines may stay in L2; a paged pass streams bytes it reads once
+    // a ring is read again at the next draft step: ordinary loads (the window
+    // still misses L2 at every step, by the fetch counters, but the step is
+    // faster without the streaming hint, which keeps the window out of the
+    // memory-side cache); a paged pass streams bytes it reads once
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks)
       t.k[ks] = RING ? ld_bf16x8(kt + k_operand_offset(ks, m, h)) : ld_bf16x8_stream(kt + k_operand_offset(ks, m, h));
