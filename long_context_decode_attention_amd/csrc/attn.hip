@@ -77,22 +77,24 @@ __device__ __forceinline__ size_t tile_of_page(const AttnArgs& a, int ppage, int
 
 // The fp8 tiles keep the bf16 tiles' element order at one byte per element, so
 // the operand offsets are the same numbers in bytes.
-template <int D, bool RING, bool KV8>
+// KEEP: the tiles are read again at the next draft step (a ring, or a window
+// through the truncated paged index): ordinary loads.  The window still misses
+// L2 at every step, by the fetch counters, but the step is faster without the
+// streaming hint, which keeps the window out of the memory-side cache.  A full
+// pass streams bytes it reads once.
+template <int D, bool RING, bool KV8, bool KEEP>
 __device__ __forceinline__ void load_k(KTile<D, RING, KV8>& t, const AttnArgs& a, size_t tile,
                                        int b, int kb, int m, int h) {
   if constexpr (KV8) {
     const uint8_t* kt = reinterpret_cast<const uint8_t*>(a.kc) + tile * (size_t)(32 * D);
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) t.k[ks] = ld_u32x2_stream(kt + k_operand_offset(ks, m, h));
+    for (int ks = 0; ks < D / 16; ++ks)
+      t.k[ks] = KEEP ? ld_u32x2(kt + k_operand_offset(ks, m, h)) : ld_u32x2_stream(kt + k_operand_offset(ks, m, h));
   } else {
     const uint16_t* kt = a.kc + tile * (size_t)(32 * D);
-    // a ring is read again at the next draft step: ordinary loads (the window
-    // still misses L2 at every step, by the fetch counters, but the step is
-    // faster without the streaming hint, which keeps the window out of the
-    // memory-side cache); a paged pass streams bytes it reads once
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks)
-      t.k[ks] = RING ? ld_bf16x8(kt + k_operand_offset(ks, m, h)) : ld_bf16x8_stream(kt + k_operand_offset(ks, m, h));
+      t.k[ks] = KEEP ? ld_bf16x8(kt + k_operand_offset(ks, m, h)) : ld_bf16x8_stream(kt + k_operand_offset(ks, m, h));
   }
   if constexpr (RING) {
     // slots 8h..8h+7 and 16+8h..16+8h+7 of the tile
@@ -108,7 +110,7 @@ __device__ __forceinline__ void load_k(KTile<D, RING, KV8>& t, const AttnArgs& a
   }
 }
 
-template <int D, bool KV8, bool RING>
+template <int D, bool KV8, bool KEEP>
 __device__ __forceinline__ void load_v(VTile<D, KV8>& t, const AttnArgs& a, size_t tile, int m,
                                        int h) {
   if constexpr (KV8) {
@@ -116,14 +118,16 @@ __device__ __forceinline__ void load_v(VTile<D, KV8>& t, const AttnArgs& a, size
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) t.v[db][kk] = ld_u32x2_stream(vt + v_operand_offset<D>(db, kk, m, h));
+      for (int kk = 0; kk < 2; ++kk)
+        t.v[db][kk] = KEEP ? ld_u32x2(vt + v_operand_offset<D>(db, kk, m, h))
+                           : ld_u32x2_stream(vt + v_operand_offset<D>(db, kk, m, h));
   } else {
     const uint16_t* vt = a.vc + tile * (size_t)(32 * D);
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
-        t.v[db][kk] = RING ? ld_bf16x8(vt + v_operand_offset<D>(db, kk, m, h))
+        t.v[db][kk] = KEEP ? ld_bf16x8(vt + v_operand_offset<D>(db, kk, m, h))
                            : ld_bf16x8_stream(vt + v_operand_offset<D>(db, kk, m, h));
   }
 }
@@ -216,7 +220,9 @@ __device__ __forceinline__ uint32_t present_keys(const KTile<D, RING, KV8>& t, c
   }
 }
 
-template <int D, int NB, bool RING, bool KV8, bool STEP = false>
+// WIN: the call reads a window through the truncated paged index (a.win), whose
+// tiles the next draft step reads again (ordinary loads).
+template <int D, int NB, bool RING, bool KV8, bool STEP = false, bool WIN = false>
 __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
   static_assert(!STEP || (RING && !KV8 && NB == 1), "the fused step reads a bf16 ring");
   constexpr int NW = 4;         // waves
@@ -380,8 +386,8 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
         new_positions<D>(kt, a, T0, h);
       }
     } else {
-      load_k<D, RING, KV8>(kt, a, tile, b, kbl, m, h);
-      load_v<D, KV8, RING>(vt, a, tile, m, h);
+      load_k<D, RING, KV8, RING || WIN>(kt, a, tile, b, kbl, m, h);
+      load_v<D, KV8, RING || WIN>(vt, a, tile, m, h);
       asm volatile("" ::: "memory");
       if (RING) T0 = ring_count();
       stage_q();
@@ -502,7 +508,7 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
         __builtin_amdgcn_sched_group_barrier(0x008, QD, 0);
       }
     }
-    if constexpr (decltype(has_next)::value) load_k<D, RING, KV8>(kt, a, tile_n, b, kbn, m, h);
+    if constexpr (decltype(has_next)::value) load_k<D, RING, KV8, RING || WIN>(kt, a, tile_n, b, kbn, m, h);
 #pragma unroll
     for (int rb = 0; rb < NB; ++rb) {
       uint32_t vis;
@@ -533,7 +539,7 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
         }
       // the raw V bytes are converted: refill them now, so that the next tile's V
       // loads run under this tile's PV products
-      if constexpr (decltype(has_next)::value) load_v<D, KV8, RING>(vt, a, tile_n, m, h);
+      if constexpr (decltype(has_next)::value) load_v<D, KV8, RING || WIN>(vt, a, tile_n, m, h);
       pv<D, NB>(st, vv, p_hi, p_lo);
     } else {
       if (mask_v) {
@@ -546,7 +552,7 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
       }
       pv<D, NB>(st, vt.v, p_hi, p_lo);
     }
-    if constexpr (!KV8 && decltype(has_next)::value) load_v<D, KV8, RING>(vt, a, tile_n, m, h);
+    if constexpr (!KV8 && decltype(has_next)::value) load_v<D, KV8, RING || WIN>(vt, a, tile_n, m, h);
   };
   const std::true_type more;
   const std::false_type last;
@@ -740,11 +746,11 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
   }
 }
 
-template <int D, int NB, bool RING, bool KV8>
+template <int D, int NB, bool RING, bool KV8, bool WIN = false>
 hipError_t launch_one(const AttnArgs& a, int grid, hipStream_t stream) {
   AttnArgs arg = a;
   void* args[] = {&arg};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_split_kernel<D, NB, RING, KV8>),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_split_kernel<D, NB, RING, KV8, false, WIN>),
                          dim3(grid), dim3(256), args, 0, stream);
 }
 
@@ -752,6 +758,9 @@ template <int D>
 hipError_t launch_d(const AttnArgs& a, const AttnPlan& p, bool ring, hipStream_t stream) {
   if (p.nrb != 1) return hipErrorInvalidValue;
   if (ring) return launch_one<D, 1, true, false>(a, p.grid, stream);
+  if (a.win)
+    return a.kv8 ? launch_one<D, 1, false, true, true>(a, p.grid, stream)
+                 : launch_one<D, 1, false, false, true>(a, p.grid, stream);
   return a.kv8 ? launch_one<D, 1, false, true>(a, p.grid, stream)
                : launch_one<D, 1, false, false>(a, p.grid, stream);
 }

@@ -30,7 +30,11 @@ __device__ __forceinline__ bf16x8 ld_bf16x8_stream(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// 8-byte non-temporal load (8 fp8 values of a streamed K/V tile).
+// 8-byte load (8 fp8 values of a K/V tile read again later), and its
+// non-temporal form for streamed tiles.
+__device__ __forceinline__ u32x2 ld_u32x2(const uint8_t* p) {
+  return *reinterpret_cast<const u32x2*>(p);
+}
 __device__ __forceinline__ u32x2 ld_u32x2_stream(const uint8_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
 }
