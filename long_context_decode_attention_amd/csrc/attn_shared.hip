@@ -149,9 +149,10 @@ __device__ __forceinline__ void pv_tile(SoftmaxState<D, RBW>& st, const float (&
   }
 }
 
-// One tile of the fast loop, as one branch-free block: S(t+1) into s_acc from the
-// LDS stage at kbase, the weights of tile t from its scores x, and PV(t) from the
-// stage at vbase.  Every key of tile t is present and visible to every row, and
+// One tile of the fast loop, as one block (branch-free up to a heavy tile's lo
+// products at its end): S(t+1) into s_acc from the LDS stage at kbase, the
+// weights of tile t from its scores x, and PV(t) from the stage at vbase.  Every
+// key of tile t is present and visible to every row, and
 // no rescale is due.  Step ks issues the S^T MFMA(s) of head-dim step ks and
 // then the softmax work of 256/D of tile t's scores per row block, which the
 // VALU executes while the matrix core runs the MFMA; anchors at every step keep
