@@ -480,7 +480,7 @@ def _verify_custom(cfg_name, seed, S, n_q, K, V, q, num_splits):
     """Verify over caller-built K/V bits (positions 0 .. S + n_q - 1) against the oracle."""
     lib = _lib()
     from long_context_decode_attention_amd import scenario as scn
-    cfg = CFG[cfg_name]
+    cfg = CFG[cfg_name] if isinstance(cfg_name, str) else cfg_name
     L = S + n_q
     kv = scn.alloc_paged_kv([L], cfg["Hkv"], cfg["D"], W.page_permutation(seed, "target_k", (L + 63) // 64))
     scn.poison(kv.k)
@@ -520,6 +520,7 @@ def test_verify_long_split_wide_values(cfg_name, S, num_splits):
 @pytest.mark.parametrize("cfg_name,S,num_splits", [
     ("ctx1m_g32x2_d256", 24000, 1),          # four waves, hi parts summed by products
     ("nope8l_1m_g64x2_d128", 16000, 1),      # eight waves, hi parts summed by dot products
+    (G64D64, 12000, 1),                      # two row blocks per wave
 ])
 def test_verify_every_tile_heavy(cfg_name, S, num_splits):
     """Every 32-key tile holds one key whose weight is ~5 % of its row's running
@@ -527,7 +528,7 @@ def test_verify_every_tile_heavy(cfg_name, S, num_splits):
     split's first maximum), so every fast tile is heavy and keeps its weights' lo
     parts.  The result must then carry the hi + lo precision: well below the error
     that bf16-rounded weights alone give on the same input, computed here."""
-    cfg = CFG[cfg_name]
+    cfg = CFG[cfg_name] if isinstance(cfg_name, str) else cfg_name
     n_q, Hq, Hkv, D = 8, cfg["Hq"], cfg["Hkv"], cfg["D"]
     L = S + n_q
     rng = np.random.default_rng(93)
